@@ -1,0 +1,281 @@
+"""Plain CPU oracle of the OLMoE mixture-of-experts feed-forward layer, in float64.
+
+TEST INFRASTRUCTURE. Only tests/, __graft_entry__.smoke() and the CPU-baseline
+leg of bench.py may import or run this module; the GPU library never does, and
+this module imports nothing from it. Inputs arrive as bf16 bit patterns
+(uint16) or float32 arrays and are widened to float64 exactly; no intermediate
+value is rounded except where a step of the layer says so (the bf16 input of
+each layer of the residual stack).
+
+Sources (page title, then section / equation):
+  [G]  "OLMoE Guide: 64-Expert Fine-Grained Open MoE Architecture":
+       "Router Mechanics & Loss Formulations", items 1 (top-8 softmax routing),
+       2 (auxiliary load balancing loss), 3 (router z-loss); and the PyTorch
+       module under "Hands-On Implementation".
+  [P]  "OLMoE: Open Mixture-of-Experts Language Models": "Pretraining
+       architecture" (router = linear layer then softmax, 8 of 64 experts,
+       dropless token choice), 4.1.6 and 4.1.7 (loss weights 0.01 and 0.001).
+  [X]  "Mixture-of-experts LLMs from scratch with OLMoE": section 2 "The router
+       and the experts" (softmax over all experts then top-k, grouped dispatch,
+       every-expert brute force) and section 3 "OLMoE in PyTorch" (no
+       renormalisation, float32 residual stream, RMSNorm).
+
+Readings taken where the pages are silent or disagree:
+  * routing weights are the 64-way softmax probabilities of the chosen experts,
+    NOT renormalised over the 8 ([X] sections 2-3 and [P] over [G]'s formula);
+  * the 8 experts are the 8 largest logits; equal logits go to the lower expert
+    id, and route_ids lists them by descending logit;
+  * the load-balancing term is alpha*E*sum_e f_e*P_e with alpha applied once
+    (as [G]'s code does), the z-loss is beta*mean_t(lse_t^2); both are returned
+    separately and their sum is [G]'s total auxiliary loss;
+  * for T = 0 both losses are 0 and nothing else is produced;
+  * RMSNorm of the stack uses weight 1 and eps 1e-5 and its output is rounded
+    to bf16 (round to nearest even), the type the layer takes.
+
+Pins: every function here is checked in tests/test_oracle_pins.py against closed
+forms, brute force, library routines or values the pages print.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+ALPHA = 0.01   # [P] 4.1.6; [G] item 2
+BETA = 0.001   # [P] 4.1.7; [G] item 3
+RMS_EPS = 1e-5  # [X] section 3 (library default for the missing config key)
+
+
+# ----------------------------------------------------------------- type helpers
+
+
+def to_f64(a) -> np.ndarray:
+    """bf16 bit patterns (uint16) or any float array -> float64, exactly."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def round_to_bf16(a) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value (ties to even), directly
+    from float64 (no double rounding through float32). Returns float64."""
+    a = np.asarray(a, dtype=np.float64)
+    out = np.zeros_like(a)
+    nz = (a != 0) & np.isfinite(a)
+    _, e = np.frexp(a[nz])                      # a = m * 2**e, 0.5 <= |m| < 1
+    quantum = np.ldexp(1.0, np.maximum(e, -125) - 8)   # bf16 spacing in that binade
+    out[nz] = np.rint(a[nz] / quantum) * quantum       # rint: ties to even
+    out[~np.isfinite(a)] = a[~np.isfinite(a)]
+    big = np.abs(out) > 3.3895313892515355e38
+    out[big] = np.copysign(np.inf, out[big])
+    return out
+
+
+def bf16_bits(a64) -> np.ndarray:
+    """Bit patterns of float64 values that are already exact bf16 values."""
+    return (np.asarray(a64, np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+# ---------------------------------------------------------------------- router
+
+
+def router_logits(x, w_router) -> np.ndarray:
+    """h(x) = W_g x for every token: [T,D] x [E,D] -> [T,E] ([G] item 1; [X] section 2)."""
+    return to_f64(x) @ to_f64(w_router).T
+
+
+def softmax_all(logits):
+    """Softmax over all experts with its log-normaliser ([X] section 2: softmax first).
+
+    Returns (lse [T], probs [T,E]); lse_t = log sum_e exp(h_te) ([G] item 3)."""
+    m = logits.max(axis=-1, keepdims=True)
+    s = np.exp(logits - m).sum(axis=-1, keepdims=True)
+    lse = m + np.log(s)
+    return lse[:, 0], np.exp(logits - lse)
+
+
+def top_k(logits, k):
+    """The k largest logits per token by a full sort on (-logit, expert id).
+
+    Returns ids [T,k] (descending logit, ties -> lower id) and the gap between
+    the k-th and (k+1)-th sorted logits (inf when k = E)."""
+    T, E = logits.shape
+    expert = np.broadcast_to(np.arange(E), (T, E))
+    order = np.lexsort((expert, -logits), axis=-1)          # primary key: -logit
+    ids = order[:, :k].astype(np.int64)
+    srt = np.take_along_axis(logits, order, axis=-1)
+    gap = srt[:, k - 1] - srt[:, k] if k < E else np.full(T, np.inf)
+    return ids, gap
+
+
+# -------------------------------------------------------------------- dispatch
+
+
+def dispatch(ids, n_experts):
+    """Group the (token, slot) pairs by expert, keeping tokens in ascending order.
+
+    counts[e]  = number of tokens that chose e
+    offsets    = exclusive prefix sum of counts (length E+1)
+    perm[p]    = token of the p-th row of the expert-contiguous order
+    inv[t, j]  = row p holding (t, ids[t, j])
+    ([X] section 2, grouped dispatch: sort pairs by expert, then count.)"""
+    ids = np.asarray(ids)
+    T, K = ids.shape
+    counts = np.zeros(n_experts, dtype=np.int64)
+    perm = np.zeros(T * K, dtype=np.int64)
+    inv = np.zeros((T, K), dtype=np.int64)
+    pos = 0
+    for e in range(n_experts):
+        toks, slots = np.nonzero(ids == e)      # row-major: tokens ascending
+        n = toks.size
+        counts[e] = n
+        perm[pos:pos + n] = toks
+        inv[toks, slots] = pos + np.arange(n)
+        pos += n
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    return counts, offsets, perm, inv
+
+
+# ---------------------------------------------------------------------- experts
+
+
+def silu(g):
+    """SiLU / Swish with beta = 1: g * sigmoid(g) ([G] item 1; [X] section 2 uses F.silu)."""
+    return g / (1.0 + np.exp(-g))
+
+
+def swiglu_expert(X, w_gate_e, w_up_e, w_down_e) -> np.ndarray:
+    """(SiLU(X W_gate^T) * (X W_up^T)) W_down^T; weights stored [out, in]
+    ([G] item 1 and its SwiGLUExpert; [X] section 2, Experts.run)."""
+    wg, wu, wd = to_f64(w_gate_e), to_f64(w_up_e), to_f64(w_down_e)
+    X = to_f64(X)
+    return (silu(X @ wg.T) * (X @ wu.T)) @ wd.T
+
+
+def losses(probs, counts, lse, k, alpha=ALPHA, beta=BETA):
+    """Switch load-balancing loss and router z-loss ([G] items 2-3).
+
+    f_e = counts_e / (T k), P_e = mean_t p_te, aux = alpha * E * sum_e f_e P_e,
+    z = beta * mean_t lse_t^2."""
+    T, E = probs.shape
+    if T == 0:
+        return 0.0, 0.0
+    f = counts / float(T * k)
+    P = probs.mean(axis=0)
+    return float(alpha * E * np.sum(f * P)), float(beta * np.mean(lse ** 2))
+
+
+def moe_layer_ref(x, w_router, w_gate, w_up, w_down, k=8, forced_ids=None,
+                  keep_y=False):
+    """One MoE layer, grouped by expert ([X] section 2 dispatch; [P] "Pretraining
+    architecture"; [G] item 1 for the weighted sum).
+
+    x [T,D] bf16 bits or float; w_router [E,D]; w_gate, w_up [E,F,D];
+    w_down [E,D,F]. forced_ids [T,k] replaces the router's choice (used where
+    two routings are both correct within rounding).
+    Returns a dict: out [T,D], ids, probs (route_probs [T,k]), p_all [T,E],
+    logits, lse, gap, counts, offsets, perm, inv, aux, z (and y [Tk,D] if keep_y)."""
+    x64 = to_f64(x)
+    T, D = x64.shape
+    E = np.asarray(w_router).shape[0]
+    logits = router_logits(x64, w_router) if T else np.zeros((0, E))
+    if T:
+        lse, p_all = softmax_all(logits)
+    else:
+        lse, p_all = np.zeros(0), np.zeros((0, E))
+    if forced_ids is None:
+        ids, gap = top_k(logits, k) if T else (np.zeros((0, k), np.int64), np.zeros(0))
+    else:
+        ids = np.asarray(forced_ids, dtype=np.int64).reshape(T, k)
+        gap = np.full(T, np.nan)
+    probs = np.take_along_axis(p_all, ids, axis=-1)          # not renormalised
+    counts, offsets, perm, inv = dispatch(ids, E)
+    y = np.zeros((T * k, D))
+    for e in range(E):
+        a, b = offsets[e], offsets[e + 1]
+        if b > a:
+            y[a:b] = swiglu_expert(x64[perm[a:b]], w_gate[e], w_up[e], w_down[e])
+    out = np.zeros((T, D))
+    for j in range(k):                                         # weighted sum over the k slots
+        out += probs[:, j:j + 1] * y[inv[:, j]]
+    aux, z = losses(p_all, counts, lse, k)
+    r = dict(out=out, ids=ids, probs=probs, p_all=p_all, logits=logits, lse=lse, gap=gap,
+             counts=counts, offsets=offsets, perm=perm, inv=inv, aux=aux, z=z)
+    if keep_y:
+        r["y"] = y
+    return r
+
+
+# ----------------------------------------------------------------- brute force
+
+
+def moe_layer_dense_ref(x, w_router, w_gate, w_up, w_down, k=8):
+    """The same layer the wasteful way: every expert on every token, outputs of
+    unchosen experts multiplied by zero ([X] section 2, dense_run). Selection by
+    pairwise comparison: expert e is chosen iff fewer than k experts beat it,
+    where e' beats e if h_e' > h_e, or h_e' = h_e and e' < e. Tiny inputs only."""
+    x64 = to_f64(x)
+    T, D = x64.shape
+    wr = to_f64(w_router)
+    E = wr.shape[0]
+    logits = np.zeros((T, E))
+    for t in range(T):
+        for e in range(E):
+            logits[t, e] = sum(x64[t, d] * wr[e, d] for d in range(D)) if D <= 64 else x64[t] @ wr[e]
+    rank = np.zeros((T, E), dtype=np.int64)
+    for t in range(T):
+        for e in range(E):
+            rank[t, e] = sum(1 for e2 in range(E)
+                             if logits[t, e2] > logits[t, e] or (logits[t, e2] == logits[t, e] and e2 < e))
+    chosen = rank < k
+    ids = np.zeros((T, k), dtype=np.int64)
+    for t in range(T):
+        for e in range(E):
+            if chosen[t, e]:
+                ids[t, rank[t, e]] = e
+    z_t = np.array([np.log(np.sum(np.exp(logits[t]))) for t in range(T)])
+    p = np.exp(logits - z_t[:, None])
+    gate = np.where(chosen, p, 0.0)
+    out = np.zeros((T, D))
+    for e in range(E):
+        ye = swiglu_expert(x64, w_gate[e], w_up[e], w_down[e])
+        out += gate[:, e:e + 1] * ye
+    counts = chosen.sum(axis=0)
+    f = counts / (T * k)
+    P = p.sum(axis=0) / T
+    aux = ALPHA * E * sum(f[e] * P[e] for e in range(E))
+    z = BETA * sum(v * v for v in z_t) / T
+    return dict(out=out, ids=ids, counts=counts, aux=float(aux), z=float(z), probs_all=p)
+
+
+# ------------------------------------------------------------------------ stack
+
+
+def rmsnorm_bf16(h, eps=RMS_EPS) -> np.ndarray:
+    """RMSNorm with weight 1, computed in float64, then rounded to bf16 (the
+    layer's input type) ([X] section 3, RMSNorm). Returns float64 bf16 values."""
+    h = np.asarray(h, dtype=np.float64)
+    u = h / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps)
+    return round_to_bf16(u)
+
+
+def moe_stack_ref(h0, layers, k=8, teacher_inputs=None, eps=RMS_EPS):
+    """Residual stack h <- h + MoE_l(RMSNorm(h)), l = 0..L-1, h kept in float64
+    ([X] section 3, Block.forward with the attention sublayer left out).
+
+    layers: list of dicts with w_router / w_gate / w_up / w_down.
+    teacher_inputs: optional per-layer bf16 inputs to use instead of RMSNorm(h)
+    (runs each layer on given inputs, so every layer can be judged alone).
+    Returns (h_final, per-layer list of dicts: x_in (bf16 bits), out, ids,
+    counts, aux, z, gap)."""
+    h = np.asarray(h0, dtype=np.float64).copy()
+    per_layer = []
+    for l, w in enumerate(layers):
+        if teacher_inputs is not None:
+            xin = to_f64(teacher_inputs[l])
+        else:
+            xin = rmsnorm_bf16(h, eps)
+        r = moe_layer_ref(xin, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], k)
+        h = h + r["out"]
+        per_layer.append(dict(x_in=bf16_bits(xin), out=r["out"], ids=r["ids"], counts=r["counts"],
+                              aux=r["aux"], z=r["z"], gap=r["gap"]))
+    return h, per_layer

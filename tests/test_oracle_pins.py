@@ -1,0 +1,320 @@
+"""Pins of the float64 oracle to things other than itself: closed forms, brute
+force, library routines, and values the pages print (tests/golden/)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_mixture_experts_expert_amd import inputs
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def small_layer(T, D=32, F=16, E=8, seed=0, w_std=0.3):
+    return inputs.host_layer(T, seed=seed, dims=(D, F, E), w_std=w_std)
+
+
+# ----------------------------------------------------------------- bf16 helpers
+
+
+def test_bf16_widening_known_values():
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0000, 0x8000, 0x7F7F], np.uint16)
+    v = oracle.to_f64(bits)
+    assert v[0] == 1.0 and v[1] == -2.0 and v[2] == 1.0 + 2.0 ** -7
+    assert v[3] == 0.0 and v[4] == 0.0 and np.signbit(v[4])
+    assert v[5] == (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def test_round_to_bf16_ties_and_double_rounding():
+    r = oracle.round_to_bf16(np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8),
+                                       1 + 2 ** -8 + 2 ** -30, 0.0, 3.0]))
+    assert r[0] == 1.0                   # tie -> even
+    assert r[1] == 1 + 2 ** -6           # tie -> even (upwards)
+    assert r[2] == -1.0
+    assert r[3] == 1 + 2 ** -7           # above the tie: rounds up (float32 first would not)
+    assert r[4] == 0.0 and r[5] == 3.0
+
+
+def test_round_to_bf16_matches_torch_on_float32_values():
+    rng = np.random.default_rng(1)
+    a = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        rng.standard_normal(1000) * 1e-39]).astype(np.float32)
+    ours = oracle.round_to_bf16(a.astype(np.float64))
+    ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(ours, ref)
+    np.testing.assert_array_equal(oracle.bf16_bits(ours),
+                                  torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
+def test_generator_bf16_rounding_matches_torch():
+    a = np.random.default_rng(2).standard_normal(50000).astype(np.float32)
+    np.testing.assert_array_equal(inputs.f32_to_bf16_bits(a),
+                                  torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
+# ----------------------------------------------------------------------- router
+
+
+def test_router_logits_basis_vector_picks_a_column():
+    D, E = 32, 8
+    wr = np.random.default_rng(3).standard_normal((E, D)).astype(np.float32)
+    x = np.zeros((1, D))
+    x[0, 5] = 3.0
+    np.testing.assert_array_equal(oracle.router_logits(x, wr)[0], 3.0 * wr[:, 5].astype(np.float64))
+
+
+def test_router_logits_match_library_linear():
+    L = small_layer(7)
+    ref = torch.nn.functional.linear(torch.from_numpy(oracle.to_f64(L["x"])),
+                                     torch.from_numpy(L["w_router"].astype(np.float64))).numpy()
+    np.testing.assert_allclose(oracle.router_logits(L["x"], L["w_router"]), ref, rtol=1e-13, atol=1e-13)
+
+
+def test_softmax_matches_library():
+    lg = np.random.default_rng(4).standard_normal((50, 64)) * 5
+    lse, p = oracle.softmax_all(lg)
+    t = torch.from_numpy(lg)
+    np.testing.assert_allclose(p, torch.softmax(t, -1).numpy(), rtol=1e-13, atol=1e-300)
+    np.testing.assert_allclose(lse, torch.logsumexp(t, -1).numpy(), rtol=1e-14)
+    np.testing.assert_allclose(p.sum(-1), 1.0, rtol=1e-14)
+
+
+def test_topk_matches_library_on_distinct_logits():
+    lg = np.random.default_rng(5).standard_normal((200, 64))
+    ids, gap = oracle.top_k(lg, 8)
+    v, i = torch.topk(torch.from_numpy(lg), 8, dim=-1, sorted=True)
+    np.testing.assert_array_equal(ids, i.numpy())
+    srt = np.sort(lg, axis=-1)[:, ::-1]
+    np.testing.assert_allclose(gap, srt[:, 7] - srt[:, 8], rtol=0, atol=0)
+    assert (gap > 0).all()
+
+
+def test_topk_constructed_order_and_ties():
+    # logits equal to one router column with a known order
+    col = np.array([0.5, 3.0, -1.0, 3.0, 2.0, 0.25, 7.0, -2.0, 1.0, 1.0, 0.0, 2.5])
+    ids, gap = oracle.top_k(col[None, :], 8)
+    # 7.0(6), 3.0(1), 3.0(3), 2.5(11), 2.0(4), 1.0(8), 1.0(9), 0.5(0); next 0.25
+    assert ids[0].tolist() == [6, 1, 3, 11, 4, 8, 9, 0]
+    assert gap[0] == 0.5 - 0.25
+    ids, gap = oracle.top_k(np.zeros((3, 64)), 8)
+    assert (ids == np.arange(8)).all() and (gap == 0).all()
+
+
+def test_zero_router_uniform_probs_and_closed_form_losses():
+    T, E = 40, 64
+    L = inputs.host_layer(T, dims=(32, 16, E), w_std=0.1)
+    L["w_router"][:] = 0
+    r = oracle.moe_layer_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], 8)
+    np.testing.assert_allclose(r["p_all"], 1.0 / 64, rtol=1e-15)
+    assert (r["ids"] == np.arange(8)).all()
+    # Sum f = 1 and P uniform => aux = alpha exactly (the balanced minimum stated by the
+    # OLMoE guide, item 2); z = beta * (ln 64)^2.
+    assert r["aux"] == pytest.approx(0.01, rel=1e-15)
+    assert r["z"] == pytest.approx(0.001 * math.log(64) ** 2, rel=1e-14)
+    assert r["z"] == pytest.approx(0.0172963085, rel=1e-9)
+
+
+def test_losses_closed_form_concentrated_router():
+    # logits = c on experts 0..7 and 0 elsewhere for every token
+    c, T, E = 1.7, 10, 64
+    lg = np.zeros((T, E))
+    lg[:, :8] = c
+    lse, p = oracle.softmax_all(lg)
+    ids, _ = oracle.top_k(lg, 8)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    aux, z = oracle.losses(p, counts, lse, 8)
+    p_top = math.exp(c) / (8 * math.exp(c) + 56)
+    assert aux == pytest.approx(0.01 * 64 * p_top, rel=1e-14)
+    assert z == pytest.approx(0.001 * math.log(8 * math.exp(c) + 56) ** 2, rel=1e-14)
+    assert oracle.losses(np.zeros((0, E)), np.zeros(E), np.zeros(0), 8) == (0.0, 0.0)
+
+
+def test_router_variant_statistics_match_page(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "router_variants.json")))
+    s = inputs.logits_2n01(40000)
+    lse, p = oracle.softmax_all(s)
+    ids, _ = oracle.top_k(s, 8)
+    w = np.take_along_axis(p, ids, -1)
+    sums = w.sum(-1)
+    # the page's 0.744 is the mean over 1000 tokens; its own spread is std/sqrt(1000)
+    tol = 3 * sums.std() / math.sqrt(g["setup"]["tokens"]) + 5e-4
+    assert abs(sums.mean() - g["weights_sum_to"]["softmax, top-k"]) < tol
+    # renormalising the chosen probabilities = softmax over the chosen logits
+    ren = w / w.sum(-1, keepdims=True)
+    top_logits = np.take_along_axis(s, ids, -1)
+    ts = torch.softmax(torch.from_numpy(top_logits), -1).numpy()
+    assert np.abs(ren - ts).max() < 1e-14 <= g["renormalised_vs_topk_softmax_largest_difference_fp32"]
+    np.testing.assert_allclose(ren.sum(-1), g["weights_sum_to"]["softmax, top-k, renormalise"], atol=1e-12)
+    # same experts whether ranking logits, probabilities or sigmoids
+    ids_p, _ = oracle.top_k(p, 8)
+    ids_s, _ = oracle.top_k(1 / (1 + np.exp(-s)), 8)
+    assert (ids_p == ids).all() and (ids_s == ids).all() == g["all_routers_choose_same_experts"]
+
+
+# --------------------------------------------------------------------- dispatch
+
+
+def test_dispatch_matches_stable_argsort_and_bincount():
+    rng = np.random.default_rng(6)
+    T, E, K = 300, 64, 8
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(T)])
+    counts, offsets, perm, inv = oracle.dispatch(ids, E)
+    flat = ids.ravel()
+    order = np.argsort(flat, kind="stable")
+    np.testing.assert_array_equal(perm, order // K)
+    np.testing.assert_array_equal(counts, np.bincount(flat, minlength=E))
+    assert offsets[-1] == T * K and offsets[0] == 0
+    # inv is the inverse of the sorted order
+    inv_ref = np.empty(T * K, np.int64)
+    inv_ref[order] = np.arange(T * K)
+    np.testing.assert_array_equal(inv.ravel(), inv_ref)
+    # bijection, ascending tokens inside each segment, segment membership
+    assert sorted(inv.ravel().tolist()) == list(range(T * K))
+    for e in range(E):
+        seg = perm[offsets[e]:offsets[e + 1]]
+        assert (np.diff(seg) > 0).all()
+        assert set(seg.tolist()) == set(np.nonzero((ids == e).any(1))[0].tolist())
+
+
+def test_dispatch_empty_and_skewed():
+    counts, offsets, perm, inv = oracle.dispatch(np.zeros((0, 8), np.int64), 64)
+    assert counts.sum() == 0 and perm.size == 0 and (offsets == 0).all()
+    ids = np.tile(np.arange(8), (5, 1))
+    counts, offsets, perm, inv = oracle.dispatch(ids, 64)
+    assert counts[:8].tolist() == [5] * 8 and counts[8:].sum() == 0
+    assert perm.tolist() == list(range(5)) * 8
+
+
+# ---------------------------------------------------------------------- experts
+
+
+def test_silu_matches_library():
+    g = np.linspace(-50, 50, 2001)
+    np.testing.assert_allclose(oracle.silu(g), torch.nn.functional.silu(torch.from_numpy(g)).numpy(),
+                               rtol=1e-14, atol=1e-300)
+
+
+def test_swiglu_expert_hand_worked():
+    # D=2, F=1: g = 1, u = -1, h = -sigmoid(1), y = h * [2, 3]
+    x = np.array([[1.0, 2.0]])
+    wg = np.array([[0.5, 0.25]])
+    wu = np.array([[1.0, -1.0]])
+    wd = np.array([[2.0], [3.0]])
+    s1 = 0.7310585786300049
+    np.testing.assert_allclose(oracle.swiglu_expert(x, wg, wu, wd), [[-2 * s1, -3 * s1]], rtol=1e-15)
+    # gate and up are not interchangeable: swapping them changes the sign and value
+    assert not np.allclose(oracle.swiglu_expert(x, wu, wg, wd), oracle.swiglu_expert(x, wg, wu, wd))
+
+
+def test_identical_experts_reduce_to_dense_ffn():
+    T, D, F, E = 9, 24, 12, 16
+    L = inputs.host_layer(T, dims=(D, F, E), w_std=0.3)
+    for key in ("w_gate", "w_up", "w_down"):
+        L[key][:] = L[key][0]
+    r = oracle.moe_layer_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], 4)
+    x = torch.from_numpy(oracle.to_f64(L["x"]))
+    wg, wu, wd = (torch.from_numpy(oracle.to_f64(L[k][0])) for k in ("w_gate", "w_up", "w_down"))
+    ffn = torch.nn.functional.linear(torch.nn.functional.silu(torch.nn.functional.linear(x, wg))
+                                     * torch.nn.functional.linear(x, wu), wd).numpy()
+    np.testing.assert_allclose(r["out"], r["probs"].sum(-1, keepdims=True) * ffn, rtol=1e-12, atol=1e-13)
+
+
+def test_zero_down_projection_gives_zero():
+    L = small_layer(11)
+    L["w_down"][:] = 0
+    r = oracle.moe_layer_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], 4)
+    assert (r["out"] == 0).all()
+
+
+@pytest.mark.parametrize("T,D,F,E,K", [(1, 16, 8, 8, 2), (13, 32, 16, 8, 4), (32, 256, 128, 16, 4)])
+def test_grouped_layer_matches_dense_brute_force(T, D, F, E, K):
+    # the last shape is the reduced verification case of the OLMoE guide's module
+    # (d 256, expert width 128, 16 experts, top-4, 2 x 16 tokens)
+    L = inputs.host_layer(T, seed=T, dims=(D, F, E), w_std=0.2)
+    r = oracle.moe_layer_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], K)
+    b = oracle.moe_layer_dense_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], K)
+    assert r["out"].shape == (T, D)
+    np.testing.assert_array_equal(r["ids"], b["ids"])
+    np.testing.assert_array_equal(r["counts"], b["counts"])
+    np.testing.assert_allclose(r["out"], b["out"], rtol=1e-12, atol=1e-12)
+    assert r["aux"] == pytest.approx(b["aux"], rel=1e-13)
+    assert r["z"] == pytest.approx(b["z"], rel=1e-13)
+    # route probabilities sum to at most one (no renormalisation)
+    assert (r["probs"].sum(-1) <= 1 + 1e-15).all()
+    assert (np.diff(r["probs"], axis=-1) <= 0).all()
+
+
+def test_page_toy_grouped_vs_dense(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "dispatch_vs_dense.json")))
+    s = g["setup"]
+    rng = np.random.default_rng(7)
+    T, D, F, E, K = s["tokens"], s["width"], s["hidden"], s["experts"], s["k"]
+    x = rng.standard_normal((T, D))
+    wr = (rng.standard_normal((D, E)) * 0.1).T.copy()
+    wg = rng.standard_normal((E, F, D)) * s["weight_std"]
+    wu = rng.standard_normal((E, F, D)) * s["weight_std"]
+    wd = rng.standard_normal((E, D, F)) * s["weight_std"]
+    r = oracle.moe_layer_ref(x, wr, wg, wu, wd, K)
+    # dense: every expert on every token, unchosen experts weighted by zero (fast form)
+    gate = np.zeros((T, E))
+    np.put_along_axis(gate, r["ids"], r["probs"], -1)
+    dense = sum(gate[:, e:e + 1] * oracle.swiglu_expert(x, wg[e], wu[e], wd[e]) for e in range(E))
+    diff = np.abs(r["out"] - dense).max()
+    assert diff < 1e-13 < g["max_difference_fp32"]
+
+
+def test_forced_ids_and_empty():
+    L = small_layer(6)
+    r = oracle.moe_layer_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], 4)
+    f = oracle.moe_layer_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], 4,
+                             forced_ids=r["ids"])
+    np.testing.assert_array_equal(f["out"], r["out"])
+    e = oracle.moe_layer_ref(L["x"][:0], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], 4)
+    assert e["out"].shape == (0, 32) and e["aux"] == 0.0 and e["z"] == 0.0 and e["counts"].sum() == 0
+
+
+def test_expert_shapes_match_page_parameter_count(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "olmoe_params.json")))
+    c = g["config"]
+    d, f, e, k, L, V = (c["hidden_size"], c["intermediate_size"], c["num_experts"],
+                        c["num_experts_per_tok"], c["num_hidden_layers"], c["vocab_size"])
+    assert (d, f, e, k) == (inputs.D_MODEL, inputs.D_EXPERT, inputs.N_EXPERTS, inputs.TOP_K)
+    expert = 3 * d * f                       # gate [f,d] + up [f,d] + down [d,f]
+    per_layer_other = 4 * d * d + 2 * d + 2 * d + e * d   # attention, qk-norm, two norms, router
+    embed = 2 * V * d + d                    # untied embeddings + final norm
+    total = embed + L * (per_layer_other + e * expert)
+    active = embed + L * (per_layer_other + k * expert)
+    assert total == g["total_parameters"] and active == g["active_parameters"]
+    assert e * expert == 402_653_184
+
+
+# ------------------------------------------------------------------------ stack
+
+
+def test_rmsnorm_closed_form_and_library():
+    h = np.full((2, 2048), 3.0)
+    u = oracle.rmsnorm_bf16(h, 1e-5)
+    assert (u == oracle.round_to_bf16(np.array([3.0 / math.sqrt(9.0 + 1e-5)]))[0]).all()
+    hr = np.random.default_rng(8).standard_normal((5, 2048)) * 4
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(hr), (2048,), eps=1e-5).numpy()
+    np.testing.assert_array_equal(oracle.rmsnorm_bf16(hr), oracle.round_to_bf16(ref))
+
+
+def test_stack_with_zero_down_is_identity_and_one_layer_matches_layer():
+    T, D, F, E = 5, 32, 16, 8
+    h0 = np.random.default_rng(9).standard_normal((T, D)).astype(np.float32)
+    layers = [inputs.host_layer(T, seed=l, dims=(D, F, E), w_std=0.3) for l in range(3)]
+    for w in layers:
+        w["w_down"] = np.zeros_like(w["w_down"])
+    h, per = oracle.moe_stack_ref(h0, layers, k=4)
+    np.testing.assert_array_equal(h, h0.astype(np.float64))
+    layers = [inputs.host_layer(T, seed=l, dims=(D, F, E), w_std=0.3) for l in range(1)]
+    h, per = oracle.moe_stack_ref(h0, layers, k=4)
+    xin = oracle.rmsnorm_bf16(h0.astype(np.float64))
+    r = oracle.moe_layer_ref(xin, **{k: layers[0][k] for k in ("w_router", "w_gate", "w_up", "w_down")}, k=4)
+    np.testing.assert_array_equal(h, h0 + r["out"])
+    np.testing.assert_array_equal(per[0]["x_in"], oracle.bf16_bits(xin))
