@@ -1,0 +1,164 @@
+/*
+ * olmoe_moe.h - C ABI of the OLMoE mixture-of-experts feed-forward layer on
+ * MI355X (gfx950).
+ *
+ * The layer (sources: "OLMoE Guide: 64-Expert Fine-Grained Open MoE
+ * Architecture", Router Mechanics & Loss Formulations items 1-3;
+ * "Mixture-of-experts LLMs from scratch with OLMoE", sections 2 and 3;
+ * "OLMoE: Open Mixture-of-Experts Language Models", Pretraining architecture):
+ *
+ *   logits  l[t,e] = sum_k x[t,k] * W_router[e,k]             (2048 -> 64)
+ *   p[t,e]  = softmax over all 64 experts (fp32)
+ *   S_t     = the 8 largest logits; equal logits go to the lower expert id
+ *   out[t]  = sum_{e in S_t} p[t,e] * W_down[e] (SiLU(W_gate[e] x_t) * (W_up[e] x_t))
+ *
+ * The routing weights are the 64-way probabilities themselves: they are not
+ * renormalised over the chosen 8 and sum to less than one.  Routing is
+ * dropless token choice: every (token, expert) pair is computed.
+ *
+ * Conventions for every entry point:
+ *   - tensor pointers are DEVICE pointers (HBM), row-major, 16-byte aligned;
+ *   - bf16 tensors are passed as void* holding IEEE bfloat16 bit patterns;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream);
+ *     all device work is enqueued on it and returns before it completes, so
+ *     every buffer must stay alive until the stream has passed this call;
+ *   - the caller allocates and owns every buffer, workspace included; the
+ *     library allocates no device memory and keeps no pointer after return;
+ *   - arguments are checked on the host before anything is enqueued; on any
+ *     status other than OLMOE_OK nothing was enqueued (except OLMOE_EHIP,
+ *     where a launch itself failed) and olmoe_last_error() holds a message
+ *     (thread-local, valid until the next call on the same thread);
+ *   - results are bitwise reproducible for identical inputs on one device
+ *     and build (no floating-point atomics anywhere).
+ */
+#ifndef OLMOE_MOE_H
+#define OLMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define OLMOE_API __attribute__((visibility("default")))
+#else
+#define OLMOE_API
+#endif
+
+#define OLMOE_ABI_VERSION 1
+
+#define OLMOE_D 2048 /* hidden size */
+#define OLMOE_F 1024 /* expert width (SwiGLU intermediate size) */
+#define OLMOE_E 64   /* experts per layer */
+#define OLMOE_K 8    /* experts per token */
+#define OLMOE_MAX_TOKENS ((int64_t)1 << 24) /* T limit: 8*T row indices fit in int32 */
+
+typedef enum {
+  OLMOE_OK = 0,
+  OLMOE_EINVAL = 1,     /* bad argument: null, negative/too large T, misaligned, aliasing */
+  OLMOE_EWORKSPACE = 2, /* workspace missing or smaller than olmoe_moe_workspace_bytes(T) */
+  OLMOE_EHIP = 3,       /* a HIP call or kernel launch failed */
+  OLMOE_ENODEVICE = 4   /* no usable gfx950 device is current */
+} olmoe_status_t;
+
+/* ABI version of the loaded library (OLMOE_ABI_VERSION it was built with). */
+OLMOE_API int olmoe_abi_version(void);
+
+/* Text of the last non-OK status on this thread ("" if none). */
+OLMOE_API const char* olmoe_last_error(void);
+
+/* Bytes of device workspace olmoe_moe_forward needs for T tokens (pure host
+ * function, no device access).  Returns 0 for T < 0 or T > OLMOE_MAX_TOKENS.
+ * Grows as about 8*T*(1024+2048)*2 bytes (the SwiGLU activations and the
+ * per-slot expert outputs) plus routing tables. */
+OLMOE_API size_t olmoe_moe_workspace_bytes(int64_t T);
+
+/* Where the dispatch tables live inside the workspace, as byte offsets from
+ * its start (pure host function; for inspection and tests):
+ *   perm    int32 [8T]   token of each row in expert-contiguous order; rows of
+ *                        expert e occupy [offsets[e], offsets[e+1]), tokens
+ *                        ascending inside each expert (a stable sort of the
+ *                        (token, slot) pairs by expert id)
+ *   inv     int32 [T,8]  row holding (t, route_ids[t,j])
+ *   offsets int32 [65]   exclusive prefix sum of the per-expert counts
+ * Any out-pointer may be NULL. */
+OLMOE_API olmoe_status_t olmoe_moe_workspace_layout(int64_t T, size_t* perm_off, size_t* inv_off,
+                                          size_t* offsets_off);
+
+/* One OLMoE MoE layer forward for T tokens.
+ *
+ *   x             bf16 [T,2048]         input rows
+ *   W_router      fp32 [64,2048]        router weights (no bias)
+ *   W_gate        bf16 [64,1024,2048]   per expert [out,in], in contiguous
+ *   W_up          bf16 [64,1024,2048]
+ *   W_down        bf16 [64,2048,1024]
+ *   T             tokens, 0 <= T <= OLMOE_MAX_TOKENS
+ *   out           bf16 [T,2048]         must not overlap any input
+ *   route_ids     int32 [T,8] or NULL   chosen experts by descending logit,
+ *                                       equal logits -> lower id first
+ *   route_probs   fp32 [T,8] or NULL    their 64-way softmax probabilities
+ *                                       (not renormalised)
+ *   expert_counts int32 [64] or NULL    tokens routed to each expert (sum 8T)
+ *   aux_loss      fp32 [1] or NULL      Switch load-balancing loss
+ *                                       0.01 * 64 * sum_e f_e P_e with
+ *                                       f_e = counts_e / (8T), P_e = mean_t p[t,e]
+ *                                       ("OLMoE Guide", item 2)
+ *   z_loss        fp32 [1] or NULL      router z-loss 0.001 * mean_t lse_t^2,
+ *                                       lse_t = log sum_e exp(l[t,e]) (item 3)
+ *   workspace     device buffer of at least olmoe_moe_workspace_bytes(T) bytes,
+ *                 256-byte aligned; contents on entry are ignored
+ *
+ * Arithmetic: router logits, softmax and losses in fp32 (the router is
+ * evaluated exactly as an fp32 dot product of the bf16 inputs and fp32
+ * weights); expert GEMMs on MFMA with fp32 accumulation (gate/up in bf16;
+ * down in fp16, W_down converted exactly); the SwiGLU activation is formed in
+ * fp32 and stored as fp16, expert outputs are stored as fp16 (both rounded to
+ * nearest even, saturated at +-65504), and the weighted sum is accumulated in
+ * fp32 over the 8 slots in route order and rounded once to bf16.
+ *
+ * T == 0 is valid: expert_counts is zeroed and the losses are set to 0.
+ * Errors: OLMOE_EINVAL for a NULL required pointer, T out of range,
+ * a pointer not 16-byte aligned, or `out` overlapping x or a weight;
+ * OLMOE_EWORKSPACE for a NULL or short workspace; OLMOE_ENODEVICE when the
+ * current device is not gfx950; OLMOE_EHIP when a launch fails. */
+OLMOE_API olmoe_status_t olmoe_moe_forward(const void* x, const float* W_router, const void* W_gate,
+                                 const void* W_up, const void* W_down, int64_t T, void* out,
+                                 int32_t* route_ids, float* route_probs,
+                                 int32_t* expert_counts, float* aux_loss, float* z_loss,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* RMSNorm of the residual stream with unit weight, rounded to the layer's
+ * input type: x_out[t] = bf16(h[t] / sqrt(mean_k h[t,k]^2 + eps)), computed in
+ * fp32 ("Mixture-of-experts LLMs from scratch with OLMoE", section 3, RMSNorm;
+ * the residual stream is kept in fp32 there).
+ *   h      fp32 [T,2048]
+ *   x_out  bf16 [T,2048], must not overlap h
+ * Errors: OLMOE_EINVAL for NULL pointers, T out of range, eps not > 0 or
+ * misalignment; OLMOE_ENODEVICE / OLMOE_EHIP as above. */
+OLMOE_API olmoe_status_t olmoe_rmsnorm_bf16(const float* h, float eps, int64_t T, void* x_out,
+                                  void* stream);
+
+/* Residual update h[t,k] += float(y[t,k]) in fp32 (same section: the block
+ * adds the MoE output to the fp32 residual stream).
+ *   h  fp32 [T,2048] (updated in place);  y  bf16 [T,2048], must not overlap h. */
+OLMOE_API olmoe_status_t olmoe_residual_add(float* h, const void* y, int64_t T, void* stream);
+
+/* Per-stage timing of olmoe_moe_forward with HIP events recorded on the
+ * caller's stream between the stages (router, dispatch, permute, gate/up,
+ * down, combine).  olmoe_timing_enable(1) starts recording for later calls
+ * on this thread and clears the sums; olmoe_timing_read() waits for the
+ * recorded events, fills up to `max_stages` per-stage sums in milliseconds,
+ * writes the number of timed calls to *calls, and returns the number of
+ * stages (or -1 on error).  Names of the stages: olmoe_timing_stage_name(i).
+ * Recording adds one event per stage boundary; leave it disabled for
+ * end-to-end timing. */
+OLMOE_API olmoe_status_t olmoe_timing_enable(int enable);
+OLMOE_API int olmoe_timing_read(double* stage_ms, int max_stages, int* calls);
+OLMOE_API const char* olmoe_timing_stage_name(int stage);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OLMOE_MOE_H */

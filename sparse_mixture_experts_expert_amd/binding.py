@@ -1,0 +1,206 @@
+"""Thin ctypes binding of libolmoe_moe.so (include/olmoe_moe.h).
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+torch supplies device memory and the current stream.  If the library has not
+been built, every call raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libolmoe_moe.so")
+
+D, F, E, K = 2048, 1024, 64, 8
+OK, EINVAL, EWORKSPACE, EHIP, ENODEVICE = range(5)
+STATUS_NAMES = {0: "OLMOE_OK", 1: "OLMOE_EINVAL", 2: "OLMOE_EWORKSPACE", 3: "OLMOE_EHIP", 4: "OLMOE_ENODEVICE"}
+
+_lib = None
+
+
+class OlmoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (once); raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m sparse_mixture_experts_expert_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, sz, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    L.olmoe_abi_version.restype = i32
+    L.olmoe_abi_version.argtypes = []
+    L.olmoe_last_error.restype = ctypes.c_char_p
+    L.olmoe_last_error.argtypes = []
+    L.olmoe_moe_workspace_bytes.restype = sz
+    L.olmoe_moe_workspace_bytes.argtypes = [i64]
+    L.olmoe_moe_workspace_layout.restype = i32
+    L.olmoe_moe_workspace_layout.argtypes = [i64, ctypes.POINTER(sz), ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    L.olmoe_moe_forward.restype = i32
+    L.olmoe_moe_forward.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.olmoe_rmsnorm_bf16.restype = i32
+    L.olmoe_rmsnorm_bf16.argtypes = [vp, ctypes.c_float, i64, vp, vp]
+    L.olmoe_residual_add.restype = i32
+    L.olmoe_residual_add.argtypes = [vp, vp, i64, vp]
+    L.olmoe_timing_enable.restype = i32
+    L.olmoe_timing_enable.argtypes = [i32]
+    L.olmoe_timing_read.restype = i32
+    L.olmoe_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), i32, ctypes.POINTER(i32)]
+    L.olmoe_timing_stage_name.restype = ctypes.c_char_p
+    L.olmoe_timing_stage_name.argtypes = [i32]
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != OK:
+        raise OlmoeError(status, lib().olmoe_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr() or None)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need(t, name, dtype, shape):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on the GPU, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def abi_version() -> int:
+    return lib().olmoe_abi_version()
+
+
+def workspace_bytes(T: int) -> int:
+    return int(lib().olmoe_moe_workspace_bytes(int(T)))
+
+
+def workspace_layout(T: int):
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().olmoe_moe_workspace_layout(int(T), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return {"perm": a.value, "inv": b.value, "offsets": c.value}
+
+
+def make_workspace(T: int, device="cuda"):
+    import torch
+    return torch.empty(max(workspace_bytes(T), 256), dtype=torch.uint8, device=device)
+
+
+def moe_forward(x, w_router, w_gate, w_up, w_down, *, out=None, route_ids=None, route_probs=None,
+                expert_counts=None, aux_loss=None, z_loss=None, workspace=None, stream=None,
+                want_routing=True):
+    """One MoE layer (olmoe_moe_forward).  Tensors are torch CUDA tensors:
+    x bf16 [T,2048], w_router fp32 [64,2048], w_gate / w_up bf16 [64,1024,2048],
+    w_down bf16 [64,2048,1024].  Missing outputs are allocated (routing outputs
+    only when want_routing).  Returns a dict of the output tensors."""
+    import torch
+    T = x.shape[0]
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, D))
+    _need(w_router, "w_router", torch.float32, (E, D))
+    _need(w_gate, "w_gate", torch.bfloat16, (E, F, D))
+    _need(w_up, "w_up", torch.bfloat16, (E, F, D))
+    _need(w_down, "w_down", torch.bfloat16, (E, D, F))
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    if want_routing:
+        route_ids = route_ids if route_ids is not None else torch.empty((T, K), dtype=torch.int32, device=dev)
+        route_probs = route_probs if route_probs is not None else torch.empty((T, K), dtype=torch.float32, device=dev)
+        expert_counts = expert_counts if expert_counts is not None else torch.empty(E, dtype=torch.int32, device=dev)
+        aux_loss = aux_loss if aux_loss is not None else torch.empty(1, dtype=torch.float32, device=dev)
+        z_loss = z_loss if z_loss is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = make_workspace(T, dev)
+    _check(lib().olmoe_moe_forward(
+        _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), int(T), _ptr(out),
+        _ptr(route_ids), _ptr(route_probs), _ptr(expert_counts), _ptr(aux_loss), _ptr(z_loss),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return {"out": out, "route_ids": route_ids, "route_probs": route_probs,
+            "expert_counts": expert_counts, "aux_loss": aux_loss, "z_loss": z_loss,
+            "workspace": workspace}
+
+
+def dispatch_tables(workspace, T: int):
+    """Views of perm [8T], inv [T,8], offsets [65] inside a workspace after a call."""
+    import torch
+    lay = workspace_layout(T)
+    def view(off, n):
+        return workspace[off:off + 4 * n].view(torch.int32)
+    return {"perm": view(lay["perm"], 8 * T), "inv": view(lay["inv"], 8 * T).view(T, K),
+            "offsets": view(lay["offsets"], E + 1)}
+
+
+def rmsnorm_bf16(h, eps: float = 1e-5, x_out=None, stream=None):
+    import torch
+    T = h.shape[0]
+    _need(h, "h", torch.float32, (T, D))
+    if x_out is None:
+        x_out = torch.empty((T, D), dtype=torch.bfloat16, device=h.device)
+    _check(lib().olmoe_rmsnorm_bf16(_ptr(h), float(eps), int(T), _ptr(x_out), _stream(stream)))
+    return x_out
+
+
+def residual_add(h, y, stream=None):
+    import torch
+    T = h.shape[0]
+    _need(h, "h", torch.float32, (T, D))
+    _need(y, "y", torch.bfloat16, (T, D))
+    _check(lib().olmoe_residual_add(_ptr(h), _ptr(y), int(T), _stream(stream)))
+    return h
+
+
+def moe_stack_forward(h, layers, eps: float = 1e-5, keep_inputs: bool = False, workspace=None,
+                      stream=None):
+    """Residual stack h <- h + MoE_l(RMSNorm(h)) over `layers` (dicts of weight
+    tensors), in place on the fp32 residual `h` [T,2048].  Returns h and, per
+    layer, expert counts / aux / z (and the bf16 layer inputs if keep_inputs)."""
+    import torch
+    T = h.shape[0]
+    dev = h.device
+    workspace = workspace if workspace is not None else make_workspace(T, dev)
+    xbuf = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    ybuf = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    counts = torch.empty((len(layers), E), dtype=torch.int32, device=dev)
+    aux = torch.empty(len(layers), dtype=torch.float32, device=dev)
+    z = torch.empty(len(layers), dtype=torch.float32, device=dev)
+    ids = torch.empty((len(layers), T, K), dtype=torch.int32, device=dev)
+    inputs = []
+    for l, w in enumerate(layers):
+        rmsnorm_bf16(h, eps, xbuf, stream)
+        if keep_inputs:
+            inputs.append(xbuf.clone())
+        moe_forward(xbuf, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], out=ybuf,
+                    route_ids=ids[l], route_probs=None, expert_counts=counts[l], aux_loss=aux[l:l + 1],
+                    z_loss=z[l:l + 1], workspace=workspace, stream=stream, want_routing=False)
+        residual_add(h, ybuf, stream)
+    return {"h": h, "expert_counts": counts, "aux_loss": aux, "z_loss": z, "route_ids": ids,
+            "inputs": inputs}
+
+
+def timing_enable(flag: bool = True):
+    _check(lib().olmoe_timing_enable(1 if flag else 0))
+
+
+def timing_read():
+    """Per-stage summed milliseconds and the number of timed calls since timing_enable."""
+    buf = (ctypes.c_double * 16)()
+    calls = ctypes.c_int()
+    n = lib().olmoe_timing_read(buf, 16, ctypes.byref(calls))
+    if n < 0:
+        raise OlmoeError(EHIP, lib().olmoe_last_error().decode())
+    names = [lib().olmoe_timing_stage_name(i).decode() for i in range(n)]
+    return {names[i]: buf[i] for i in range(n)}, calls.value

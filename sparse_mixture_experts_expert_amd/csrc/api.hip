@@ -1,0 +1,316 @@
+// C ABI of the OLMoE MoE library: argument checks, workspace layout, and the
+// launch sequence router -> scan -> permute -> gate/up -> down -> combine on
+// the caller's stream.  Declarations and contracts: include/olmoe_moe.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/olmoe_moe.h"
+#include "kernels.hpp"
+
+namespace {
+
+using namespace olmoe;
+
+thread_local std::string g_err;
+
+olmoe_status_t fail(olmoe_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+olmoe_status_t ok() {
+  g_err.clear();
+  return OLMOE_OK;
+}
+
+struct Layout {
+  size_t ids, probs, lrank, blk_counts, blk_psum, blk_lse2, blk_base, offsets, tp_gu, tp_dn, perm,
+      inv, h, y, total;
+};
+
+Layout make_layout(int64_t T) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~size_t(255);
+    return o;
+  };
+  const size_t rows = 8 * static_cast<size_t>(T);
+  const size_t nblk = static_cast<size_t>((T + 15) / 16);
+  L.offsets = take(65 * 4);
+  L.tp_gu = take(65 * 4);
+  L.tp_dn = take(65 * 4);
+  L.ids = take(rows * 4);
+  L.probs = take(rows * 4);
+  L.lrank = take(rows);
+  L.blk_counts = take(nblk * 64 * 4);
+  L.blk_psum = take(nblk * 64 * 4);
+  L.blk_lse2 = take(nblk * 4);
+  L.blk_base = take(nblk * 64 * 4);
+  L.perm = take(rows * 4);
+  L.inv = take(rows * 4);
+  L.h = take(rows * OLMOE_F * 2);
+  L.y = take(rows * OLMOE_D * 2);
+  L.total = off;
+  return L;
+}
+
+bool misaligned(const void* p, size_t a = 16) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// gfx950 check, cached per device
+std::mutex g_dev_mu;
+std::vector<int> g_dev_ok;  // -1 unknown, 0 no, 1 yes
+
+olmoe_status_t check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) return fail(OLMOE_ENODEVICE, "no HIP device: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if ((int)g_dev_ok.size() <= dev) g_dev_ok.resize(dev + 1, -1);
+  if (g_dev_ok[dev] < 0) {
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) return fail(OLMOE_ENODEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    g_dev_ok[dev] = std::strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+    if (!g_dev_ok[dev]) return fail(OLMOE_ENODEVICE, "device %d is %s, the library is built for gfx950", dev, p.gcnArchName);
+  }
+  if (!g_dev_ok[dev]) return fail(OLMOE_ENODEVICE, "current device is not gfx950");
+  return OLMOE_OK;
+}
+
+// ---------------------------------------------------------------- stage timing
+
+constexpr int N_STAGES = 6;
+const char* kStageNames[N_STAGES] = {"router", "scan", "permute", "gateup", "down", "combine"};
+
+struct TimingState {
+  bool enabled = false;
+  std::vector<std::vector<hipEvent_t>> pending;  // one set of N_STAGES+1 events per call
+};
+thread_local TimingState g_timing;
+
+struct StageRecorder {
+  std::vector<hipEvent_t>* ev = nullptr;
+  hipStream_t s;
+  int next = 0;
+  explicit StageRecorder(hipStream_t st) : s(st) {
+    if (!g_timing.enabled || g_timing.pending.size() >= 65536) return;
+    g_timing.pending.emplace_back(N_STAGES + 1);
+    ev = &g_timing.pending.back();
+    for (auto& x : *ev) (void)hipEventCreate(&x);
+    (void)hipEventRecord((*ev)[0], s);
+    next = 1;
+  }
+  void mark() {
+    if (ev && next <= N_STAGES) (void)hipEventRecord((*ev)[next++], s);
+  }
+  void finish() {
+    while (ev && next <= N_STAGES) (void)hipEventRecord((*ev)[next++], s);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+int olmoe_abi_version(void) { return OLMOE_ABI_VERSION; }
+
+const char* olmoe_last_error(void) { return g_err.c_str(); }
+
+size_t olmoe_moe_workspace_bytes(int64_t T) {
+  if (T < 0 || T > OLMOE_MAX_TOKENS) return 0;
+  return make_layout(T).total;
+}
+
+olmoe_status_t olmoe_moe_workspace_layout(int64_t T, size_t* perm_off, size_t* inv_off,
+                                          size_t* offsets_off) {
+  if (T < 0 || T > OLMOE_MAX_TOKENS) return fail(OLMOE_EINVAL, "T=%lld out of range", (long long)T);
+  const Layout L = make_layout(T);
+  if (perm_off) *perm_off = L.perm;
+  if (inv_off) *inv_off = L.inv;
+  if (offsets_off) *offsets_off = L.offsets;
+  return ok();
+}
+
+olmoe_status_t olmoe_moe_forward(const void* x, const float* W_router, const void* W_gate,
+                                 const void* W_up, const void* W_down, int64_t T, void* out,
+                                 int32_t* route_ids, float* route_probs, int32_t* expert_counts,
+                                 float* aux_loss, float* z_loss, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  // ---- host-side checks; nothing is enqueued unless all pass
+  if (T < 0 || T > OLMOE_MAX_TOKENS)
+    return fail(OLMOE_EINVAL, "T=%lld out of range [0, %lld]", (long long)T, (long long)OLMOE_MAX_TOKENS);
+  if (!W_router || !W_gate || !W_up || !W_down)
+    return fail(OLMOE_EINVAL, "a weight pointer is NULL");
+  if (T > 0 && (!x || !out)) return fail(OLMOE_EINVAL, "x or out is NULL");
+  const void* ptrs[] = {x, W_router, W_gate, W_up, W_down, out, route_ids, route_probs, expert_counts};
+  const char* names[] = {"x", "W_router", "W_gate", "W_up", "W_down", "out", "route_ids", "route_probs", "expert_counts"};
+  for (int i = 0; i < 9; ++i)
+    if (ptrs[i] && misaligned(ptrs[i])) return fail(OLMOE_EINVAL, "%s is not 16-byte aligned", names[i]);
+  if ((aux_loss && misaligned(aux_loss, 4)) || (z_loss && misaligned(z_loss, 4)))
+    return fail(OLMOE_EINVAL, "aux_loss / z_loss not 4-byte aligned");
+  const size_t act = static_cast<size_t>(T) * OLMOE_D * 2;
+  const size_t wexp = static_cast<size_t>(OLMOE_E) * OLMOE_F * OLMOE_D * 2;
+  if (overlaps(out, act, x, act) || overlaps(out, act, W_router, (size_t)OLMOE_E * OLMOE_D * 4) ||
+      overlaps(out, act, W_gate, wexp) || overlaps(out, act, W_up, wexp) || overlaps(out, act, W_down, wexp))
+    return fail(OLMOE_EINVAL, "out overlaps an input");
+  const Layout L = make_layout(T);
+  if (!workspace) return fail(OLMOE_EWORKSPACE, "workspace is NULL");
+  if (misaligned(workspace, 256)) return fail(OLMOE_EINVAL, "workspace is not 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(OLMOE_EWORKSPACE, "workspace has %zu bytes, %zu needed for T=%lld", workspace_bytes, L.total,
+                (long long)T);
+  if (overlaps(out, act, workspace, L.total)) return fail(OLMOE_EINVAL, "out overlaps the workspace");
+  olmoe_status_t st = check_device();
+  if (st != OLMOE_OK) return st;
+
+  // ---- launches
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int Ti = static_cast<int>(T);
+  int32_t* ids = route_ids ? route_ids : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* probs = route_probs ? route_probs : reinterpret_cast<float*>(ws + L.probs);
+  const GemmPlan plan = plan_gemm(Ti);
+  StageRecorder rec(s);
+  hipError_t he = hipSuccess;
+
+  if (Ti > 0) {
+    RouterArgs ra{static_cast<const uint16_t*>(x), W_router, Ti, ids, probs,
+                  reinterpret_cast<uint8_t*>(ws + L.lrank), reinterpret_cast<int32_t*>(ws + L.blk_counts),
+                  reinterpret_cast<float*>(ws + L.blk_psum), reinterpret_cast<float*>(ws + L.blk_lse2)};
+    he = launch_router(ra, s);
+    if (he != hipSuccess) return fail(OLMOE_EHIP, "router launch: %s", hipGetErrorString(he));
+  }
+  rec.mark();
+  ScanArgs sa{Ti,
+              reinterpret_cast<const int32_t*>(ws + L.blk_counts),
+              reinterpret_cast<const float*>(ws + L.blk_psum),
+              reinterpret_cast<const float*>(ws + L.blk_lse2),
+              reinterpret_cast<int32_t*>(ws + L.blk_base),
+              reinterpret_cast<int32_t*>(ws + L.offsets),
+              reinterpret_cast<int32_t*>(ws + L.tp_gu), plan.bm_gu,
+              reinterpret_cast<int32_t*>(ws + L.tp_dn), plan.bm_dn,
+              expert_counts, aux_loss, z_loss};
+  he = launch_scan(sa, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "scan launch: %s", hipGetErrorString(he));
+  rec.mark();
+  if (Ti == 0) {
+    rec.finish();
+    return ok();
+  }
+  PermuteArgs pa{Ti, ids, reinterpret_cast<const uint8_t*>(ws + L.lrank),
+                 reinterpret_cast<const int32_t*>(ws + L.blk_base), reinterpret_cast<int32_t*>(ws + L.perm),
+                 reinterpret_cast<int32_t*>(ws + L.inv)};
+  he = launch_permute(pa, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "permute launch: %s", hipGetErrorString(he));
+  rec.mark();
+  GemmArgs ga{Ti,
+              static_cast<const uint16_t*>(x),
+              static_cast<const uint16_t*>(W_gate),
+              static_cast<const uint16_t*>(W_up),
+              static_cast<const uint16_t*>(W_down),
+              reinterpret_cast<const int32_t*>(ws + L.perm),
+              reinterpret_cast<const int32_t*>(ws + L.offsets),
+              reinterpret_cast<const int32_t*>(ws + L.tp_gu),
+              reinterpret_cast<const int32_t*>(ws + L.tp_dn),
+              reinterpret_cast<uint16_t*>(ws + L.h),
+              reinterpret_cast<uint16_t*>(ws + L.y)};
+  he = launch_gateup(ga, plan, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "gate/up launch: %s", hipGetErrorString(he));
+  rec.mark();
+  he = launch_down(ga, plan, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "down launch: %s", hipGetErrorString(he));
+  rec.mark();
+  CombineArgs ca{Ti, reinterpret_cast<const uint16_t*>(ws + L.y), reinterpret_cast<const int32_t*>(ws + L.inv),
+                 probs, static_cast<uint16_t*>(out)};
+  he = launch_combine(ca, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "combine launch: %s", hipGetErrorString(he));
+  rec.mark();
+  return ok();
+}
+
+olmoe_status_t olmoe_rmsnorm_bf16(const float* h, float eps, int64_t T, void* x_out, void* stream) {
+  if (T < 0 || T > OLMOE_MAX_TOKENS) return fail(OLMOE_EINVAL, "T=%lld out of range", (long long)T);
+  if (!(eps > 0.f)) return fail(OLMOE_EINVAL, "eps must be > 0");
+  if (T > 0 && (!h || !x_out)) return fail(OLMOE_EINVAL, "h or x_out is NULL");
+  if (misaligned(h) || misaligned(x_out)) return fail(OLMOE_EINVAL, "h / x_out not 16-byte aligned");
+  if (overlaps(h, (size_t)T * OLMOE_D * 4, x_out, (size_t)T * OLMOE_D * 2))
+    return fail(OLMOE_EINVAL, "x_out overlaps h");
+  if (T == 0) return ok();
+  olmoe_status_t st = check_device();
+  if (st != OLMOE_OK) return st;
+  hipError_t he = launch_rmsnorm(h, eps, static_cast<int>(T), static_cast<uint16_t*>(x_out),
+                                 static_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "rmsnorm launch: %s", hipGetErrorString(he));
+  return ok();
+}
+
+olmoe_status_t olmoe_residual_add(float* h, const void* y, int64_t T, void* stream) {
+  if (T < 0 || T > OLMOE_MAX_TOKENS) return fail(OLMOE_EINVAL, "T=%lld out of range", (long long)T);
+  if (T > 0 && (!h || !y)) return fail(OLMOE_EINVAL, "h or y is NULL");
+  if (misaligned(h) || misaligned(y)) return fail(OLMOE_EINVAL, "h / y not 16-byte aligned");
+  if (overlaps(h, (size_t)T * OLMOE_D * 4, y, (size_t)T * OLMOE_D * 2))
+    return fail(OLMOE_EINVAL, "y overlaps h");
+  if (T == 0) return ok();
+  olmoe_status_t st = check_device();
+  if (st != OLMOE_OK) return st;
+  hipError_t he = launch_residual_add(h, static_cast<const uint16_t*>(y), static_cast<int>(T),
+                                      static_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "residual_add launch: %s", hipGetErrorString(he));
+  return ok();
+}
+
+olmoe_status_t olmoe_timing_enable(int enable) {
+  for (auto& set : g_timing.pending)
+    for (auto& e : set) (void)hipEventDestroy(e);
+  g_timing.pending.clear();
+  g_timing.enabled = enable != 0;
+  return ok();
+}
+
+int olmoe_timing_read(double* stage_ms, int max_stages, int* calls) {
+  if (!stage_ms && max_stages > 0) {
+    fail(OLMOE_EINVAL, "stage_ms is NULL");
+    return -1;
+  }
+  for (int i = 0; i < max_stages && i < N_STAGES; ++i) stage_ms[i] = 0.0;
+  int n = 0;
+  for (auto& set : g_timing.pending) {
+    if (hipEventSynchronize(set[N_STAGES]) != hipSuccess) {
+      fail(OLMOE_EHIP, "hipEventSynchronize failed");
+      return -1;
+    }
+    for (int i = 0; i < N_STAGES; ++i) {
+      float ms = 0.f;
+      (void)hipEventElapsedTime(&ms, set[i], set[i + 1]);
+      if (i < max_stages) stage_ms[i] += ms;
+    }
+    ++n;
+  }
+  if (calls) *calls = n;
+  return N_STAGES;
+}
+
+const char* olmoe_timing_stage_name(int stage) {
+  return (stage >= 0 && stage < N_STAGES) ? kStageNames[stage] : "";
+}
+
+}  // extern "C"

@@ -152,36 +152,37 @@ def host_workload(name: str, seed: int = 0, tokens: int | None = None):
 # ------------------------------------------------------------------------- device
 
 
-def device_layer(T: int, seed: int = 0, workload: str = "custom", layer: int = 0,
-                 scaled_rows_frac: float = 0.0, skew: bool = False, device="cuda",
-                 x: bool = True):
-    """One layer's inputs drawn on the device with torch's generator (fast at full size).
-
-    Same recipe as host_layer; returns torch tensors (bf16 / fp32) on `device`.
-    With x=False only the weights are drawn (the stack derives its inputs from h).
-    """
+def _device_normal(shape, seed, workload, layer, tensor_id, std, device):
     import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(_sub_seed(seed, workload, layer, tensor_id))
+    t = torch.empty(shape, dtype=torch.float32, device=device)
+    t.normal_(0.0, 1.0, generator=g)
+    return t.mul_(std)
 
-    def normal(shape, tensor_id, std):
-        g = torch.Generator(device=device)
-        g.manual_seed(_sub_seed(seed, workload, layer, tensor_id))
-        t = torch.empty(shape, dtype=torch.float32, device=device)
-        t.normal_(0.0, 1.0, generator=g)
-        return t.mul_(std)
 
+def device_x(T: int, seed: int = 0, workload: str = "custom", layer: int = 0,
+             scaled_rows_frac: float = 0.0, skew: bool = False, device="cuda"):
+    """Token rows x bf16 [T,2048] drawn on the device (see the module docstring)."""
+    import torch
+    x = _device_normal((T, D_MODEL), seed, workload, layer, _X, 1.0, device).to(torch.bfloat16)
+    if scaled_rows_frac > 0 and T > 0:
+        rows = torch.from_numpy(_scaled_rows(seed, workload, T, scaled_rows_frac)).to(device)
+        x[rows] = x[rows] * 8
+    if skew:
+        x[:, D_MODEL - 1] = 1.0
+    return x.contiguous()
+
+
+def device_weights(seed: int = 0, workload: str = "custom", layer: int = 0, skew: bool = False,
+                   device="cuda"):
+    """One layer's router (fp32) and expert (bf16) weights drawn on the device."""
+    import torch
     out = {}
-    if x:
-        xt = normal((T, D_MODEL), _X, 1.0).to(torch.bfloat16)
-        if scaled_rows_frac > 0 and T > 0:
-            rows = torch.from_numpy(_scaled_rows(seed, workload, T, scaled_rows_frac)).to(device)
-            xt[rows] = xt[rows] * 8
-        out["x"] = xt
-    wr = normal((N_EXPERTS, D_MODEL), _WR, WEIGHT_STD)
+    wr = _device_normal((N_EXPERTS, D_MODEL), seed, workload, layer, _WR, WEIGHT_STD, device)
     if skew:
         rank = _expert_ranking(seed, workload, layer)
         wr[:, D_MODEL - 1] = torch.from_numpy(skew_bias(rank)).to(device)
-        if x:
-            out["x"][:, D_MODEL - 1] = 1.0
     out["w_router"] = wr.contiguous()
     # draw and round expert weights one expert at a time to bound the fp32 scratch
     for key, tid, shape in (("w_gate", _WG, (D_EXPERT, D_MODEL)),
@@ -198,6 +199,14 @@ def device_layer(T: int, seed: int = 0, workload: str = "custom", layer: int = 0
     return out
 
 
+def device_layer(T: int, seed: int = 0, workload: str = "custom", layer: int = 0,
+                 scaled_rows_frac: float = 0.0, skew: bool = False, device="cuda"):
+    """One layer's inputs drawn on the device with torch's generator (fast at full size)."""
+    out = device_weights(seed, workload, layer, skew, device)
+    out["x"] = device_x(T, seed, workload, layer, scaled_rows_frac, skew, device)
+    return out
+
+
 def device_workload(name: str, seed: int = 0, device="cuda", tokens: int | None = None):
     """Device inputs for a named workload; the stack returns h0 (fp32) and per-layer weights."""
     import torch
@@ -209,7 +218,7 @@ def device_workload(name: str, seed: int = 0, device="cuda", tokens: int | None 
     g = torch.Generator(device=device)
     g.manual_seed(_sub_seed(seed, name, 99, _X))
     h0 = torch.empty((T, D_MODEL), dtype=torch.float32, device=device).normal_(generator=g)
-    layers = [device_layer(T, seed, name, l, device=device, x=False) for l in range(w.layers)]
+    layers = [device_weights(seed, name, l, device=device) for l in range(w.layers)]
     return {"h0": h0, "layers": layers}
 
 

@@ -1,0 +1,111 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+sizes its workspace, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_mixture_experts_expert_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "olmoe_moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"OLMOE_API\s+[\w\s\*]+?\b(olmoe_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return binding.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version(L):
+    text = open(HEADER).read()
+    v = int(re.search(r"#define OLMOE_ABI_VERSION (\d+)", text).group(1))
+    assert binding.abi_version() == v
+
+
+def test_workspace_bytes_formula():
+    assert binding.workspace_bytes(-1) == 0
+    assert binding.workspace_bytes((1 << 24) + 1) == 0
+    w0 = binding.workspace_bytes(0)
+    assert 0 < w0 < 4096
+    for T in (1, 32, 256, 4096, 16384):
+        w = binding.workspace_bytes(T)
+        act = 8 * T * (1024 + 2048) * 2
+        assert act <= w <= act + 8 * T * 20 + (T // 16 + 1) * 64 * 12 + 64 * 1024
+        lay = binding.workspace_layout(T)
+        assert lay["offsets"] % 256 == 0 and lay["perm"] % 256 == 0 and lay["inv"] % 256 == 0
+        assert lay["perm"] + 4 * 8 * T <= lay["inv"] <= w
+
+
+def _fwd(L, x=1 << 20, wr=2 << 20, wg=3 << 20, wu=4 << 30, wd=5 << 30, T=4, out=6 << 34,
+         ws=8 << 36, wsb=None, ids=None):
+    wsb = binding.workspace_bytes(T if T >= 0 else 0) if wsb is None else wsb
+    vp = ctypes.c_void_p
+    st = L.olmoe_moe_forward(vp(x), vp(wr), vp(wg), vp(wu), vp(wd), T, vp(out), vp(ids), None, None,
+                             None, None, vp(ws), wsb, None)
+    return st, L.olmoe_last_error().decode()
+
+
+def test_forward_rejects_bad_arguments_before_any_device_call(L):
+    assert _fwd(L, T=-1)[0] == binding.EINVAL
+    assert _fwd(L, T=(1 << 24) + 1)[0] == binding.EINVAL
+    st, msg = _fwd(L, wr=0)
+    assert st == binding.EINVAL and "NULL" in msg
+    assert _fwd(L, x=0)[0] == binding.EINVAL
+    assert _fwd(L, out=0)[0] == binding.EINVAL
+    st, msg = _fwd(L, x=(1 << 20) + 8)
+    assert st == binding.EINVAL and "aligned" in msg
+    assert _fwd(L, ids=(1 << 40) + 4)[0] == binding.EINVAL
+    # out overlapping x / a weight
+    assert _fwd(L, out=(1 << 20) + 16)[0] == binding.EINVAL
+    assert _fwd(L, out=(3 << 20) + 4096)[0] == binding.EINVAL
+    # workspace
+    st, msg = _fwd(L, ws=0)
+    assert st == binding.EWORKSPACE
+    st, msg = _fwd(L, wsb=1000)
+    assert st == binding.EWORKSPACE and "needed" in msg
+    assert _fwd(L, ws=(8 << 36) + 16)[0] == binding.EINVAL
+    # out overlapping the workspace
+    assert _fwd(L, out=(8 << 36) + 256)[0] == binding.EINVAL
+
+
+def test_glue_entry_points_reject_bad_arguments(L):
+    vp = ctypes.c_void_p
+    assert L.olmoe_rmsnorm_bf16(vp(1 << 20), ctypes.c_float(0.0), 4, vp(1 << 30), None) == binding.EINVAL
+    assert L.olmoe_rmsnorm_bf16(None, ctypes.c_float(1e-5), 4, vp(1 << 30), None) == binding.EINVAL
+    assert L.olmoe_rmsnorm_bf16(vp(1 << 20), ctypes.c_float(1e-5), 4, vp((1 << 20) + 64), None) == binding.EINVAL
+    assert L.olmoe_rmsnorm_bf16(vp(1 << 20), ctypes.c_float(1e-5), -2, vp(1 << 30), None) == binding.EINVAL
+    assert L.olmoe_residual_add(vp(1 << 20), vp((1 << 20) + 4096), 4, None) == binding.EINVAL
+    assert L.olmoe_residual_add(vp((1 << 20) + 4), vp(1 << 30), 4, None) == binding.EINVAL
+    # T == 0 with valid arguments needs no device work
+    assert L.olmoe_rmsnorm_bf16(None, ctypes.c_float(1e-5), 0, None, None) == binding.OK
+    assert L.olmoe_residual_add(None, None, 0, None) == binding.OK
+
+
+def test_timing_stage_names(L):
+    assert L.olmoe_timing_enable(0) == binding.OK
+    names = [L.olmoe_timing_stage_name(i).decode() for i in range(6)]
+    assert names == ["router", "scan", "permute", "gateup", "down", "combine"]
+    assert L.olmoe_timing_stage_name(6) == b""
+    stats, calls = binding.timing_read()
+    assert calls == 0 and set(stats) == set(names)
+
+
+def test_binding_raises_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", "/nonexistent/libolmoe_moe.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()
