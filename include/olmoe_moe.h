@@ -146,8 +146,8 @@ OLMOE_API olmoe_status_t olmoe_rmsnorm_bf16(const float* h, float eps, int64_t T
 OLMOE_API olmoe_status_t olmoe_residual_add(float* h, const void* y, int64_t T, void* stream);
 
 /* Per-stage timing of olmoe_moe_forward with HIP events recorded on the
- * caller's stream between the stages (router, dispatch, permute, gate/up,
- * down, combine).  olmoe_timing_enable(1) starts recording for later calls
+ * caller's stream between its stages: router (logits, softmax, top-8),
+ * dispatch (scan and permutation), gateup, down, combine.  olmoe_timing_enable(1) starts recording for later calls
  * on this thread and clears the sums; olmoe_timing_read() waits for the
  * recorded events, fills up to `max_stages` per-stage sums in milliseconds,
  * writes the number of timed calls to *calls, and returns the number of

@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "../../include/olmoe_moe.h"
+#include "common.hpp"
 #include "kernels.hpp"
 
 namespace {
@@ -35,8 +36,8 @@ olmoe_status_t ok() {
 }
 
 struct Layout {
-  size_t ids, probs, lrank, blk_counts, blk_psum, blk_lse2, blk_base, offsets, tp_gu, tp_dn, perm,
-      inv, h, y, total;
+  size_t tiles_gu, tiles_dn, planes, partial, ids, probs, lrank, blk_counts, blk_psum, blk_lse2, blk_base, offsets,
+      tp_gu, tp_dn, perm, inv, h, y, total;
 };
 
 Layout make_layout(int64_t T) {
@@ -52,6 +53,13 @@ Layout make_layout(int64_t T) {
   L.offsets = take(65 * 4);
   L.tp_gu = take(65 * 4);
   L.tp_dn = take(65 * 4);
+  // +8: the GEMM grids are rounded up to a multiple of 8 workgroups, and a surplus
+  // workgroup reads one entry past the last possible tile before it returns
+  const size_t max_tiles = static_cast<size_t>(max_row_tiles(static_cast<int>(T), MIN_TILE_ROWS)) + 8;
+  L.tiles_gu = take(max_tiles * 8);
+  L.tiles_dn = take(max_tiles * 8);
+  L.planes = take(3 * 64 * 2048 * 2);
+  L.partial = take(static_cast<size_t>(T) * 4 * 64 * 8);
   L.ids = take(rows * 4);
   L.probs = take(rows * 4);
   L.lrank = take(rows);
@@ -98,8 +106,10 @@ olmoe_status_t check_device() {
 
 // ---------------------------------------------------------------- stage timing
 
-constexpr int N_STAGES = 6;
-const char* kStageNames[N_STAGES] = {"router", "scan", "permute", "gateup", "down", "combine"};
+// router: logits and top-8 selection; dispatch: scan and permutation; then the
+// three expert stages
+constexpr int N_STAGES = 5;
+const char* kStageNames[N_STAGES] = {"router", "dispatch", "gateup", "down", "combine"};
 
 struct TimingState {
   bool enabled = false;
@@ -192,36 +202,39 @@ olmoe_status_t olmoe_moe_forward(const void* x, const float* W_router, const voi
   StageRecorder rec(s);
   hipError_t he = hipSuccess;
 
-  if (Ti > 0) {
-    RouterArgs ra{static_cast<const uint16_t*>(x), W_router, Ti, ids, probs,
-                  reinterpret_cast<uint8_t*>(ws + L.lrank), reinterpret_cast<int32_t*>(ws + L.blk_counts),
-                  reinterpret_cast<float*>(ws + L.blk_psum), reinterpret_cast<float*>(ws + L.blk_lse2)};
-    he = launch_router(ra, s);
-    if (he != hipSuccess) return fail(OLMOE_EHIP, "router launch: %s", hipGetErrorString(he));
-  }
-  rec.mark();
+  RouterArgs ra{static_cast<const uint16_t*>(x), W_router, Ti, reinterpret_cast<float2*>(ws + L.partial),
+                reinterpret_cast<uint16_t*>(ws + L.planes)};
+  SelectArgs se{reinterpret_cast<const float2*>(ws + L.partial), Ti, ids, probs,
+                reinterpret_cast<uint8_t*>(ws + L.lrank), reinterpret_cast<int32_t*>(ws + L.blk_counts),
+                reinterpret_cast<float*>(ws + L.blk_psum), reinterpret_cast<float*>(ws + L.blk_lse2)};
   ScanArgs sa{Ti,
               reinterpret_cast<const int32_t*>(ws + L.blk_counts),
               reinterpret_cast<const float*>(ws + L.blk_psum),
               reinterpret_cast<const float*>(ws + L.blk_lse2),
               reinterpret_cast<int32_t*>(ws + L.blk_base),
               reinterpret_cast<int32_t*>(ws + L.offsets),
-              reinterpret_cast<int32_t*>(ws + L.tp_gu), plan.bm_gu,
-              reinterpret_cast<int32_t*>(ws + L.tp_dn), plan.bm_dn,
+              reinterpret_cast<int32_t*>(ws + L.tp_gu), reinterpret_cast<int2*>(ws + L.tiles_gu), plan.bm_gu,
+              reinterpret_cast<int32_t*>(ws + L.tp_dn), reinterpret_cast<int2*>(ws + L.tiles_dn), plan.bm_dn,
               expert_counts, aux_loss, z_loss};
-  he = launch_scan(sa, s);
-  if (he != hipSuccess) return fail(OLMOE_EHIP, "scan launch: %s", hipGetErrorString(he));
+  PermuteArgs pa{Ti, ids, reinterpret_cast<const uint8_t*>(ws + L.lrank),
+                 reinterpret_cast<const int32_t*>(ws + L.blk_base), reinterpret_cast<int32_t*>(ws + L.perm),
+                 reinterpret_cast<int32_t*>(ws + L.inv)};
+  he = launch_router_partial(ra, s);
+  if (he == hipSuccess) he = launch_router_select(se, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "router launch: %s", hipGetErrorString(he));
+  rec.mark();
+  if (Ti <= SMALL_TOKENS) {
+    he = launch_scan_permute(sa, pa, s);   // T == 0 included: zero counts and losses
+  } else {
+    he = launch_scan(sa, s);
+    if (he == hipSuccess) he = launch_permute(pa, s);
+  }
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "dispatch launch: %s", hipGetErrorString(he));
   rec.mark();
   if (Ti == 0) {
     rec.finish();
     return ok();
   }
-  PermuteArgs pa{Ti, ids, reinterpret_cast<const uint8_t*>(ws + L.lrank),
-                 reinterpret_cast<const int32_t*>(ws + L.blk_base), reinterpret_cast<int32_t*>(ws + L.perm),
-                 reinterpret_cast<int32_t*>(ws + L.inv)};
-  he = launch_permute(pa, s);
-  if (he != hipSuccess) return fail(OLMOE_EHIP, "permute launch: %s", hipGetErrorString(he));
-  rec.mark();
   GemmArgs ga{Ti,
               static_cast<const uint16_t*>(x),
               static_cast<const uint16_t*>(W_gate),
@@ -231,6 +244,8 @@ olmoe_status_t olmoe_moe_forward(const void* x, const float* W_router, const voi
               reinterpret_cast<const int32_t*>(ws + L.offsets),
               reinterpret_cast<const int32_t*>(ws + L.tp_gu),
               reinterpret_cast<const int32_t*>(ws + L.tp_dn),
+              reinterpret_cast<const int2*>(ws + L.tiles_gu),
+              reinterpret_cast<const int2*>(ws + L.tiles_dn),
               reinterpret_cast<uint16_t*>(ws + L.h),
               reinterpret_cast<uint16_t*>(ws + L.y)};
   he = launch_gateup(ga, plan, s);

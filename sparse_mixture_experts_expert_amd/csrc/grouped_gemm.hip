@@ -1,4 +1,4 @@
-// Grouped expert GEMMs of the OLMoE MoE layer on bf16 MFMA (gfx950).
+// Grouped expert GEMMs of the OLMoE MoE layer on MFMA (gfx950).
 //
 // Each expert is a SwiGLU network, (SiLU(x W_gate^T) * (x W_up^T)) W_down^T,
 // with gate/up [1024,2048] and down [2048,1024] ("OLMoE Guide: 64-Expert
@@ -8,142 +8,171 @@
 // the groups into one grouped matrix multiplication).
 //
 // Work unit: (row tile of one expert, column tile).  Row tiles of all experts
-// are numbered in expert order; the scan kernel leaves the per-expert prefix of
-// that numbering, and each workgroup finds its expert by a binary search over
-// the 65-entry prefix, so there is no host round trip and no per-expert launch.
-// The grid is sized from the upper bound on the tile count; workgroups past the
-// real count return at once.
+// are numbered in expert order; the scan leaves a list of (first row, expert,
+// rows) per tile, so a workgroup learns its work with a single load: no host
+// round trip, no per-expert launch, no dependent chain of loads at start.
+// The 1-D grid is sized from the upper bound on the tile count (workgroups
+// past the real count return at once) and remapped so that consecutive units
+// (the column tiles of one row tile: same token rows, adjacent weight rows)
+// run on the same XCD and share its L2.
 //
 // gate/up: A = x rows gathered through perm (never materialised), B = the gate
 // rows and the up rows of the same output columns, so one workgroup holds both
 // accumulators and applies SiLU(g)*u in fp32 before the single store of H.
-// down: A = H rows (already expert-contiguous), B = W_down[e]; Y stored per row.
+// down: A = H rows (already expert-contiguous), B = W_down[e].
+//
+// Operand staging: an S-stage ring of LDS tiles, BK k wide, filled by direct
+// global->LDS 16-byte loads (each lane supplies its own address, so the row
+// gather costs nothing extra).  A wavefront's load covers 1 KiB: 1024/(2 BK)
+// rows x 2 BK contiguous bytes, whole cache lines per row.  The 16-byte chunks
+// land with the low 3 bits of their index XOR-swizzled by row, so the MFMA
+// fragment reads (8 rows x 16 bytes per group of lanes) hit distinct banks.  One barrier per k-step,
+// after waiting only for the loads of the stage about to be used: S-1 stages
+// stay in flight while the MFMAs run.
 //
 // The intermediates H and Y are stored as fp16 (round to nearest even,
 // saturated at +-65504): same bytes as bf16 but 3 more significand bits, which
 // keeps their rounding well below the output's own bf16 rounding.  The down
 // GEMM therefore runs on f16 MFMA; W_down's bf16 values are converted to fp16
-// while being staged into LDS, exactly for every weight in fp16's normal range
-// (weights below 2^-14 in magnitude keep an absolute error under 2^-24).
-//
-// Both operands are staged through LDS in [row][64] bf16 tiles whose 16-byte
-// chunks are XOR-swizzled by row, so the MFMA fragment reads (8 rows x 16 bytes
-// per group of lanes) hit distinct banks; two LDS buffers let the next k-tile's
-// global loads run during the current tile's MFMAs.
+// after the LDS read, exactly for every weight in fp16's normal range (weights
+// below 2^-14 in magnitude keep an absolute error under 2^-24).
 #include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
 
+#define GPTR(p) ((const __attribute__((address_space(1))) void*)(p))
+#define LPTR(p) ((__attribute__((address_space(3))) void*)(p))
+
 namespace olmoe {
 
 namespace {
 
-constexpr int BK = 64;
-
+// element offset of 16-byte chunk `ch` of tile row `row` (rows of BK elements);
+// the low 3 bits of the chunk index are XORed with the row
+template <int BK>
 __device__ __forceinline__ int swz(int row, int ch) { return row * BK + ((ch ^ (row & 7)) << 3); }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
-template <int BM_, int BN_, int WM_, int WN_, bool GATEUP_>
+// wait until at most N of this thread's vector-memory operations are in flight,
+// then workgroup barrier; the memory clobber keeps LDS reads below it
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int BM_, int BN_, int WM_, int WN_, bool GATEUP_, int STAGES_, int BK_ = 64, int ROT_ = 1, bool NTW_ = false>
 struct Cfg {
+  static constexpr int ROT = ROT_;   // rotate each work unit's starting k-step
+  static constexpr bool NTW = NTW_;  // weight loads marked non-temporal (streamed once)
   static constexpr int BM = BM_;   // rows (tokens) per tile
   static constexpr int BN = BN_;   // output columns per tile
+  static constexpr int BK = BK_;   // k per stage
+  static constexpr int CPR = BK / 8;   // 16-byte chunks per tile row
   static constexpr int WM = WM_, WN = WN_;
   static constexpr bool GATEUP = GATEUP_;
+  static constexpr int STAGES = STAGES_;
   static constexpr int NT = WM * WN * 64;
+  static constexpr int NW = WM * WN;
   static constexpr int G = GATEUP ? 2 : 1;        // accumulator sets (gate, up)
   using V = typename std::conditional<GATEUP, bf16x8, f16x8>::type;   // MFMA operand type
   static constexpr int NB = G * BN;               // B rows per tile
+  static constexpr int ROWS = BM + NB;            // LDS rows per stage
   static constexpr int KD = GATEUP ? D : F;       // reduction length
   static constexpr int ND = GATEUP ? F : D;       // output row length
+  static constexpr int KT = KD / BK;
   static constexpr int FM = BM / WM / 32;         // 32x32 fragments per wavefront
   static constexpr int FN = BN / WN / 32;
-  static constexpr int ACH = BM * (BK / 8) / NT;  // 16-byte A chunks per thread per k-tile
-  static constexpr int BCH = NB * (BK / 8) / NT;
+  static constexpr int RPL = 64 / CPR;            // tile rows per wavefront load
+  static constexpr int IPS = ROWS * CPR / NT;     // LDS-DMA loads per thread per stage
+  static constexpr int JA = BM / (RPL * NW);      // loads j < JA fill A rows, the rest B rows
+  static_assert(BM % (RPL * NW) == 0, "each load fills A rows only or B rows only");
   static_assert(FM >= 1 && FN >= 1, "tile too small for the wave grid");
-  static_assert(ACH >= 1 && BCH >= 1 && ACH * NT == BM * 8 && BCH * NT == NB * 8, "chunking");
-  static_assert(ND % BN == 0, "column tiles");
+  static_assert(CPR >= 8 && CPR <= 64 && IPS * NT == ROWS * CPR && ROWS % (RPL * NW) == 0, "stage loading");
+  static_assert(STAGES >= 2 && IPS * (STAGES - 2) <= 63, "vmcnt range");
+  static_assert(ND % BN == 0 && KD % BK == 0, "tiles");
 };
+
+// wait for the stage about to be used; `remaining` = stages issued after it (0 .. STAGES-2)
+template <class C, int R>
+__device__ __forceinline__ void wait_stage(int remaining) {
+  if constexpr (R == 0) {
+    vm_barrier<0>();
+  } else {
+    if (remaining >= R) vm_barrier<R * C::IPS>();
+    else wait_stage<C, R - 1>(remaining);
+  }
+}
 
 template <class C>
 __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W0, const bf16_t* __restrict__ W1,
-    const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tile_prefix, bf16_t* __restrict__ Cout) {
-  __shared__ __align__(16) bf16_t smem[2][(C::BM + C::NB) * BK];
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ tile_count, const int2* __restrict__ tiles,
+    int n_blocks, bf16_t* __restrict__ Cout) {
+  constexpr int BK = C::BK;
+  __shared__ __align__(16) bf16_t smem[C::STAGES][C::ROWS * BK];
 
-  const int tile = blockIdx.y;
-  const int nt = blockIdx.x;
-  if (tile >= tile_prefix[E]) return;
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {   // last expert whose first tile is <= tile
-    const int mid = (lo + hi) >> 1;
-    if (tile_prefix[mid] <= tile) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  const int row0 = offsets[e] + (tile - tile_prefix[e]) * C::BM;
-  const int valid = min(C::BM, offsets[e + 1] - row0);
+  // XCD-aware remap over the real unit count (known only here, from the scan): those units are
+  // spread evenly over the 8 XCDs (dispatch is round-robin over them), consecutive units on one
+  // XCD; surplus workgroups of the worst-case grid exit at once.  A remap over the padded grid
+  // would leave the last XCDs idle whenever the real count is well under the bound.
+  const int nunits = *tile_count * n_blocks;
+  const int nper = (nunits + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  const int logical = (blockIdx.x & 7) * nper + slot;
+  if (slot >= nper || logical >= nunits) return;
+  const int tile = logical / n_blocks;
+  const int nt = logical - tile * n_blocks;
+  const int2 ti = tiles[tile];
+  const int e = ti.y & 255;
+  const int row0 = ti.x;
+  const int valid = ti.y >> 8;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
   const int wm = wv / C::WN, wn = wv % C::WN;
-  const int ch = tid & 7;
 
-  const bf16_t* asrc[C::ACH];
+  // LDS-DMA sources: load j of wavefront wv fills stage rows (j*NW + wv)*RPL .. +RPL;
+  // lane -> row + lane/CPR, slot lane%CPR, which holds chunk slot ^ (row & 7)
+  const bf16_t* gp[C::IPS];
+  const int dummy = C::GATEUP ? perm[row0] : row0;   // any valid row for the tile's unused rows
 #pragma unroll
-  for (int q = 0; q < C::ACH; ++q) {
-    const int r = (tid >> 3) + q * (C::NT / 8);
-    if (r < valid) {
-      const int src = C::GATEUP ? perm[row0 + r] : row0 + r;
-      asrc[q] = A + (size_t)src * C::KD + ch * 8;
+  for (int j = 0; j < C::IPS; ++j) {
+    const int r = (j * C::NW + wv) * C::RPL + lane / C::CPR;
+    const int ch = (lane % C::CPR) ^ (r & 7);
+    const bf16_t* p;
+    if (r < C::BM) {
+      const int src = r < valid ? (C::GATEUP ? perm[row0 + r] : row0 + r) : dummy;
+      p = A + (size_t)src * C::KD;
     } else {
-      asrc[q] = nullptr;
-    }
-  }
-  const bf16_t* bsrc[C::BCH];
-#pragma unroll
-  for (int q = 0; q < C::BCH; ++q) {
-    const int r = (tid >> 3) + q * (C::NT / 8);
-    if (C::GATEUP) {
-      const bf16_t* base = r < C::BN ? W0 : W1;
-      const int n = nt * C::BN + (r < C::BN ? r : r - C::BN);
-      bsrc[q] = base + ((size_t)e * F + n) * D + ch * 8;
-    } else {
-      bsrc[q] = W0 + ((size_t)e * D + nt * C::BN + r) * F + ch * 8;
-    }
-  }
-
-  u32x4 ra[C::ACH], rb[C::BCH];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int q = 0; q < C::ACH; ++q)
-      ra[q] = asrc[q] ? *reinterpret_cast<const u32x4*>(asrc[q] + k0) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int q = 0; q < C::BCH; ++q) rb[q] = *reinterpret_cast<const u32x4*>(bsrc[q] + k0);
-  };
-  auto sstore = [&](int buf) {
-    bf16_t* As = smem[buf];
-    bf16_t* Bs = smem[buf] + C::BM * BK;
-#pragma unroll
-    for (int q = 0; q < C::ACH; ++q) {
-      const int r = (tid >> 3) + q * (C::NT / 8);
-      *reinterpret_cast<u32x4*>(&As[swz(r, ch)]) = ra[q];
-    }
-#pragma unroll
-    for (int q = 0; q < C::BCH; ++q) {
-      const int r = (tid >> 3) + q * (C::NT / 8);
-      u32x4 v = rb[q];
-      if constexpr (!C::GATEUP) {   // bf16 -> fp16 (exact in fp16's normal range)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v[i] << 16),
-                                                      __uint_as_float(v[i] & 0xFFFF0000u));
-          v[i] = __builtin_bit_cast(uint32_t, h);
-        }
+      const int rb = r - C::BM;
+      if constexpr (C::GATEUP) {
+        const bf16_t* base = rb < C::BN ? W0 : W1;
+        const int n = nt * C::BN + (rb < C::BN ? rb : rb - C::BN);
+        p = base + ((size_t)e * F + n) * D;
+      } else {
+        p = W0 + ((size_t)e * D + nt * C::BN + rb) * F;
       }
-      *reinterpret_cast<u32x4*>(&Bs[swz(r, ch)]) = v;
+    }
+    gp[j] = p + ch * 8;
+  }
+  // work units start at different k-steps so that concurrently running ones spread their
+  // requests over the memory channels (every tile row starts on a 4 KiB boundary); the
+  // order is a function of the unit only, so results stay reproducible
+  const int k0 = C::ROT ? (logical * 5) % C::KT : 0;
+  auto issue = [&](int kt, int sl) {
+    int kr = kt + k0;
+    kr = kr >= C::KT ? kr - C::KT : kr;
+#pragma unroll
+    for (int j = 0; j < C::IPS; ++j) {
+      const auto src = GPTR(gp[j] + kr * BK);
+      const auto dst = LPTR(&smem[sl][(j * C::NW + wv) * C::RPL * BK]);
+      if (C::NTW && j >= C::JA)
+        __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 2);   // cache policy: non-temporal
+      else
+        __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
     }
   };
 
@@ -157,15 +186,15 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[g][i][j][v] = 0.f;
 
-  constexpr int KT = C::KD / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
-    const bf16_t* As = smem[buf];
-    const bf16_t* Bs = smem[buf] + C::BM * BK;
+#pragma unroll
+  for (int s = 0; s < C::STAGES - 1; ++s)
+    if (s < C::KT) issue(s, s);
+
+  for (int kt = 0; kt < C::KT; ++kt) {
+    wait_stage<C, C::STAGES - 2>(min(C::STAGES - 2, C::KT - 1 - kt));
+    if (kt + C::STAGES - 1 < C::KT) issue(kt + C::STAGES - 1, (kt + C::STAGES - 1) % C::STAGES);
+    const bf16_t* As = smem[kt % C::STAGES];
+    const bf16_t* Bs = As + C::BM * BK;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int kc = kk * 2 + (lane >> 5);
@@ -174,14 +203,23 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) {
         const int r = wm * (C::BM / C::WM) + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const V*>(&As[swz(r, kc)]);
+        af[i] = *reinterpret_cast<const V*>(&As[swz<BK>(r, kc)]);
       }
 #pragma unroll
       for (int g = 0; g < C::G; ++g)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
           const int r = g * C::BN + wn * (C::BN / C::WN) + j * 32 + (lane & 31);
-          bfr[g][j] = *reinterpret_cast<const V*>(&Bs[swz(r, kc)]);
+          u32x4 v = *reinterpret_cast<const u32x4*>(&Bs[swz<BK>(r, kc)]);
+          if constexpr (!C::GATEUP) {   // bf16 -> fp16 (exact in fp16's normal range)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v[q] << 16),
+                                                        __uint_as_float(v[q] & 0xFFFF0000u));
+              v[q] = __builtin_bit_cast(uint32_t, h);
+            }
+          }
+          bfr[g][j] = __builtin_bit_cast(V, v);
         }
 #pragma unroll
       for (int g = 0; g < C::G; ++g)
@@ -195,8 +233,6 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
               acc[g][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bfr[g][j], acc[g][i][j], 0, 0, 0);
           }
     }
-    if (kt + 1 < KT) sstore(buf ^ 1);
-    __syncthreads();
   }
 
   // C layout of a 32x32 fragment: lane holds column lane%32, rows (v/4)*8 + (lane/32)*4 + v%4
@@ -217,20 +253,25 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
       }
 }
 
-// tile sets: 0 = small row tiles (decode-like batches), 1 = large row tiles
-using GuSmall = Cfg<32, 64, 1, 2, true>;
-using DnSmall = Cfg<32, 64, 1, 2, false>;
-using GuLarge = Cfg<128, 64, 2, 2, true>;
-using DnLarge = Cfg<128, 128, 2, 2, false>;
+// tile sets by batch size (rows per expert ~ T/8), chosen by measurement on MI355X.  Up to a
+// few hundred tokens the layer is bound by streaming the weights once; marking gate/up loads
+// non-temporal keeps them from displacing the token rows that every column tile re-reads.
+using GuTiny = Cfg<32, 64, 1, 2, true, 4, 64, 1, true>;
+using DnTiny = Cfg<32, 64, 1, 2, false, 4>;
+using GuSmall = Cfg<64, 64, 2, 2, true, 3, 64, 1, true>;
+using DnSmall = Cfg<64, 128, 2, 2, false, 3>;
+using GuLarge = Cfg<128, 128, 2, 2, true, 3, 64, 0>;
+using DnLarge = Cfg<128, 128, 2, 2, false, 2>;
 
 template <class C>
 hipError_t launch_cfg(const bf16_t* A, const bf16_t* W0, const bf16_t* W1, const GemmArgs& a,
-                      const int32_t* tile_prefix, bf16_t* out, hipStream_t stream) {
-  const int tiles = max_row_tiles(a.T, C::BM);
-  if (tiles == 0) return hipSuccess;
-  dim3 grid(C::ND / C::BN, tiles);
-  hipLaunchKernelGGL(grouped_gemm_kernel<C>, grid, dim3(C::NT), 0, stream, A, W0, W1, a.perm,
-                     a.offsets, tile_prefix, out);
+                      const int32_t* tile_prefix, const int2* tiles, bf16_t* out, hipStream_t stream) {
+  const int max_tiles = max_row_tiles(a.T, C::BM);
+  if (max_tiles == 0) return hipSuccess;
+  const int n_blocks = C::ND / C::BN;
+  const int grid = (max_tiles * n_blocks + 7) / 8 * 8;
+  hipLaunchKernelGGL(grouped_gemm_kernel<C>, dim3(grid), dim3(C::NT), 0, stream, A, W0, W1, a.perm,
+                     tile_prefix + E, tiles, n_blocks, out);
   return hipGetLastError();
 }
 
@@ -246,12 +287,16 @@ int max_row_tiles(int T, int bm) {
 
 GemmPlan plan_gemm(int T) {
   GemmPlan p;
-  if (T <= 384) {
+  if (T <= 48) {
     p.variant = 0;
+    p.bm_gu = GuTiny::BM;
+    p.bm_dn = DnTiny::BM;
+  } else if (T <= 640) {
+    p.variant = 1;
     p.bm_gu = GuSmall::BM;
     p.bm_dn = DnSmall::BM;
   } else {
-    p.variant = 1;
+    p.variant = 2;
     p.bm_gu = GuLarge::BM;
     p.bm_dn = DnLarge::BM;
   }
@@ -259,15 +304,19 @@ GemmPlan plan_gemm(int T) {
 }
 
 hipError_t launch_gateup(const GemmArgs& a, const GemmPlan& p, hipStream_t stream) {
-  if (p.variant == 0)
-    return launch_cfg<GuSmall>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.h, stream);
-  return launch_cfg<GuLarge>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.h, stream);
+  switch (p.variant) {
+    case 0: return launch_cfg<GuTiny>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
+    case 1: return launch_cfg<GuSmall>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
+    default: return launch_cfg<GuLarge>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
+  }
 }
 
 hipError_t launch_down(const GemmArgs& a, const GemmPlan& p, hipStream_t stream) {
-  if (p.variant == 0)
-    return launch_cfg<DnSmall>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.y, stream);
-  return launch_cfg<DnLarge>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.y, stream);
+  switch (p.variant) {
+    case 0: return launch_cfg<DnTiny>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
+    case 1: return launch_cfg<DnSmall>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
+    default: return launch_cfg<DnLarge>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
+  }
 }
 
 }  // namespace olmoe

@@ -10,6 +10,15 @@ struct RouterArgs {
   const uint16_t* x;      // bf16 [T,2048]
   const float* wr;        // fp32 [64,2048]
   int T;
+  float2* partial;        // [4,T,64] per-k-quarter (sum, compensation) of the logits (scratch)
+  uint16_t* planes;       // bf16 [3,64,2048] exact split of wr in fragment order (scratch, T > 2048)
+};
+// router logits in four k-quarter partials (one launch)
+hipError_t launch_router_partial(const RouterArgs& a, hipStream_t stream);
+
+struct SelectArgs {
+  const float2* partial;
+  int T;
   int32_t* ids;           // [T,8]
   float* probs;           // [T,8]
   uint8_t* lrank;         // [T,8] rank of the token among its routing block's tokens of that expert
@@ -17,7 +26,10 @@ struct RouterArgs {
   float* blk_psum;        // [nblk,64]
   float* blk_lse2;        // [nblk]
 };
-hipError_t launch_router(const RouterArgs& a, hipStream_t stream);
+// softmax + top-8 per routing block (one launch, one wavefront per block)
+hipError_t launch_router_select(const SelectArgs& a, hipStream_t stream);
+
+constexpr int SMALL_TOKENS = 2048;   // up to here scan and permutation share one launch
 
 struct ScanArgs {
   int T;
@@ -27,8 +39,10 @@ struct ScanArgs {
   int32_t* blk_base;        // [nblk,64] first row of each (block, expert)
   int32_t* offsets;         // [65]
   int32_t* tile_prefix_gu;  // [65] prefix of gate/up row tiles per expert
+  int2* tiles_gu;           // per gate/up row tile: (first row, expert | rows << 8)
   int bm_gu;
   int32_t* tile_prefix_dn;  // [65] prefix of down row tiles per expert
+  int2* tiles_dn;
   int bm_dn;
   int32_t* expert_counts;   // [64] or null
   float* aux_loss;          // [1] or null
@@ -45,6 +59,8 @@ struct PermuteArgs {
   int32_t* inv;             // [T,8]
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
+// scan + permutation in one workgroup, for T <= SMALL_TOKENS
+hipError_t launch_scan_permute(const ScanArgs& sa, const PermuteArgs& pa, hipStream_t stream);
 
 // Grouped GEMM tile shapes, chosen from T (rows per expert ~ T/8).
 struct GemmPlan {
@@ -53,6 +69,7 @@ struct GemmPlan {
 };
 GemmPlan plan_gemm(int T);
 int max_row_tiles(int T, int bm);
+constexpr int MIN_TILE_ROWS = 32;   // smallest row tile of any plan (sizes the tile lists)
 
 struct GemmArgs {
   int T;
@@ -62,8 +79,10 @@ struct GemmArgs {
   const uint16_t* w_down;   // bf16 [64,2048,1024]
   const int32_t* perm;
   const int32_t* offsets;
-  const int32_t* tile_prefix_gu;
+  const int32_t* tile_prefix_gu;   // [64] holds the tile count
   const int32_t* tile_prefix_dn;
+  const int2* tiles_gu;
+  const int2* tiles_dn;
   uint16_t* h;              // fp16 [8T,1024] SwiGLU activations, expert-contiguous rows
   uint16_t* y;              // fp16 [8T,2048] expert outputs, expert-contiguous rows
 };

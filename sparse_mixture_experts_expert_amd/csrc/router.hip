@@ -1,200 +1,220 @@
-// Router of the OLMoE MoE layer: logits = x W_router^T (2048 -> 64), softmax over
-// all 64 experts, top-8 ("OLMoE Guide: 64-Expert Fine-Grained Open MoE
-// Architecture", item 1 of Router Mechanics; "Mixture-of-experts LLMs from
-// scratch with OLMoE", section 2, softmax first then the k largest, no
-// renormalisation).
+// Router of the OLMoE MoE layer: logits = x W_router^T (2048 -> 64), the
+// linear layer that scores all experts ("OLMoE Guide: 64-Expert Fine-Grained
+// Open MoE Architecture", item 1 of Router Mechanics; "Mixture-of-experts LLMs
+// from scratch with OLMoE", section 2), then softmax and top-8 (select_block in
+// routing.hpp).
 //
-// fp32 router on bf16 matrix cores: every fp32 weight w is split into three
+// The logits are produced in four k-quarter partials, each a (sum,
+// compensation) pair whose fp64 sum the selection forms.
+//
+// Up to 2048 tokens: fp32 MFMA (16x16x4) straight from the fp32 router weights
+// and the bf16 tokens.  One wavefront per (16 tokens, 16 experts, k-quarter):
+// a workgroup reads only a 32 KiB slice of W_router, so the router spreads over
+// many CUs even for a handful of tokens (one workgroup pulling the whole router
+// through one CU would be bound by that CU's load bandwidth).  Each lane loads
+// 4 consecutive k of its row, and MFMA step s takes element s of every lane:
+// the k-order inside a 16-k block is permuted identically for both operands,
+// which leaves the dot product unchanged.
+//
+// Larger batches, where the router's MFMA work matters: bf16 matrix cores at
+// one eighth of the fp32-MFMA cost.  Every fp32 weight w is split into three
 // bf16 values hi + mid + lo == w exactly (8 + 8 + 8 significand bits cover
 // fp32's 24), so x*w = x*hi + x*mid + x*lo with every product exact (x is
-// bf16).  Three bf16 MFMAs per tile give the fp32 dot product at one eighth of
-// the fp32-MFMA cost.  Summation error is kept far below the 1e-5 logit window
-// inside which two routings count as equally correct: the hi products of each
-// 64-wide k-chunk are summed into a fresh partial, and the partials are added
-// to the running logit with Knuth's TwoSum, whose exact rounding error goes to
-// a compensation term; the mid and lo products (2^-8 of the total and less)
-// share one plain accumulator.  A plain fp32 accumulator over k = 2048 drifts
-// by ~2e-5 on rows scaled by 8; this scheme stays near 2e-6.
+// bf16); the prep kernel writes the three planes once per call in MFMA
+// fragment order (every wavefront load is one contiguous 1 KiB), and each
+// wavefront reuses a weight fragment for 4 token sub-blocks.
 //
-// One wavefront owns 16 tokens (a routing block).  Lane e of the wavefront
-// holds expert e's logit for one token at a time, so the softmax and the top-8
-// are wavefront reductions over the 64 lanes; ties between equal logits go to
-// the lowest lane, i.e. the lower expert id.  Lane e also counts how many of
-// the block's tokens chose expert e, which gives each (token, slot) its rank
-// inside the block for a stable dispatch.
+// Both paths keep the summation error far below the 1e-5 logit window inside
+// which two routings count as equally correct: each 64-wide k-chunk is summed
+// into a fresh partial, and the partials are added to the running sum with
+// Knuth's TwoSum, whose exact rounding error goes to a compensation term (the
+// bf16 path sums the small mid and lo products in one plain accumulator).  A
+// plain fp32 accumulator over k = 2048 drifts by ~2e-5 on rows scaled by 8;
+// this scheme stays near 2e-6.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "routing.hpp"
 
 namespace olmoe {
 
 namespace {
 
-constexpr int KC = 64;              // k-chunk of the router weights staged in LDS
-constexpr int WSTRIDE = KC + 8;     // padded row (144 bytes): conflict-free 16-byte reads
+constexpr int KQ = D / 4;        // k-range of one partial wavefront
+constexpr int KSTEPS = D / 32;   // bf16 MFMA k-steps over a whole row
 
 __device__ __forceinline__ void split3(float w, bf16_t& hi, bf16_t& mid, bf16_t& lo) {
   hi = f32_to_bf16(w);
-  const float r1 = w - bf16_to_f32(hi);
+  const float r1 = w - bf16_to_f32(hi);     // exact
   mid = f32_to_bf16(r1);
-  const float r2 = r1 - bf16_to_f32(mid);
+  const float r2 = r1 - bf16_to_f32(mid);   // exact, at most 8 significant bits
   lo = f32_to_bf16(r2);
 }
 
-template <int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void router_top8_kernel(
-    const bf16_t* __restrict__ x, const float* __restrict__ wr, int T,
-    int32_t* __restrict__ ids, float* __restrict__ probs, uint8_t* __restrict__ lrank,
-    int32_t* __restrict__ blk_counts, float* __restrict__ blk_psum, float* __restrict__ blk_lse2) {
-  constexpr int NT = WAVES * 64;
-  constexpr int WCH = E * KC / 4 / NT;  // float4 chunks of a weight k-chunk per thread
-  __shared__ __align__(16) bf16_t wsm[3][E * WSTRIDE];
-  __shared__ float lsm[WAVES][ROUTE_BLOCK][E + 1];
+// W_router fp32 [64,2048] -> planes[p][g][kstep][lane][8] with expert 16g + lane%16,
+// k = 32*kstep + 8*(lane/16) + i: the B fragment of a 16x16x32 MFMA, one 16-byte
+// chunk per lane
+__global__ __launch_bounds__(256) void router_prep_kernel(const float* __restrict__ wr,
+                                                          bf16_t* __restrict__ planes) {
+  const int c = blockIdx.x * 256 + threadIdx.x;      // one 8-wide k chunk of one expert
+  if (c >= E * D / 8) return;
+  const int e = c / (D / 8), k = (c % (D / 8)) * 8;
+  const float4 v0 = *reinterpret_cast<const float4*>(wr + e * D + k);
+  const float4 v1 = *reinterpret_cast<const float4*>(wr + e * D + k + 4);
+  const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  bf16_t h[8], m[8], l[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) split3(f[j], h[j], m[j], l[j]);
+  const int g = e >> 4, lane = ((k & 31) >> 3) * 16 + (e & 15), ks = k >> 5;
+  const size_t o = (((size_t)g * KSTEPS + ks) * 64 + lane) * 8;
+  const size_t P = (size_t)E * D;
+  u32x4 vh, vm, vl;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    vh[j] = h[2 * j] | (uint32_t(h[2 * j + 1]) << 16);
+    vm[j] = m[2 * j] | (uint32_t(m[2 * j + 1]) << 16);
+    vl[j] = l[2 * j] | (uint32_t(l[2 * j + 1]) << 16);
+  }
+  *reinterpret_cast<u32x4*>(planes + o) = vh;
+  *reinterpret_cast<u32x4*>(planes + P + o) = vm;
+  *reinterpret_cast<u32x4*>(planes + 2 * P + o) = vl;
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int blk = blockIdx.x * WAVES + w;   // routing block of this wavefront
-  const int tok0 = blk * ROUTE_BLOCK;
-
-  // A operand: lane holds token (lane % 16), k-group (lane / 16) of 8 values
-  const int arow = tok0 + (lane & 15);
-  const bool arow_ok = arow < T;
-  const bf16_t* xrow = x + (size_t)(arow_ok ? arow : 0) * D + (lane >> 4) * 8;
-
-  f32x4 acc_hi[4], acc_lm[4], tot[4], cmp[4];
+__device__ __forceinline__ void twosum_into(f32x4& tot, f32x4& cmp, const f32x4& part) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    acc_hi[i] = acc_lm[i] = tot[i] = cmp[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float s0 = tot[i], p = part[i];
+    const float t = s0 + p;
+    const float b = t - s0;
+    cmp[i] += (s0 - (t - b)) + (p - b);
+    tot[i] = t;
   }
+}
 
-  float4 wreg[WCH];
-  auto load_w = [&](int k0) {
-#pragma unroll
-    for (int q = 0; q < WCH; ++q) {
-      const int c = tid + q * NT;
-      const int row = c / (KC / 4), c4 = c % (KC / 4);
-      wreg[q] = *reinterpret_cast<const float4*>(wr + (size_t)row * D + k0 + c4 * 4);
-    }
-  };
-  auto store_w = [&]() {
-#pragma unroll
-    for (int q = 0; q < WCH; ++q) {
-      const int c = tid + q * NT;
-      const int row = c / (KC / 4), c4 = c % (KC / 4);
-      const float v[4] = {wreg[q].x, wreg[q].y, wreg[q].z, wreg[q].w};
-      bf16_t h[4], m[4], l[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) split3(v[i], h[i], m[i], l[i]);
-      const int o = row * WSTRIDE + c4 * 4;
-      *reinterpret_cast<uint2*>(&wsm[0][o]) = make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
-      *reinterpret_cast<uint2*>(&wsm[1][o]) = make_uint2(m[0] | (uint32_t(m[1]) << 16), m[2] | (uint32_t(m[3]) << 16));
-      *reinterpret_cast<uint2*>(&wsm[2][o]) = make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
-    }
-  };
+// fp32 path: partial[kq][t][e] for 16 tokens, 16 experts, one k-quarter
+__global__ __launch_bounds__(64) void router_partial_f32_kernel(const bf16_t* __restrict__ x,
+                                                                const float* __restrict__ wr, int T,
+                                                                float2* __restrict__ partial) {
+  const int lane = threadIdx.x;
+  const int g = blockIdx.y & 3;              // expert group of 16
+  const int kq = blockIdx.y >> 2;            // k-quarter
+  const int tok0 = blockIdx.x * 16;
+  const int row = tok0 + (lane & 15);
+  const bool aok = row < T;
+  // lane (n, q) = (lane % 16, lane / 16) loads k = kb + 4q .. kb + 4q + 3 of its rows
+  const float* bp = wr + (size_t)(g * 16 + (lane & 15)) * D + kq * KQ + (lane >> 4) * 4;
+  const bf16_t* ap = x + (size_t)(aok ? row : 0) * D + kq * KQ + (lane >> 4) * 4;
 
-  load_w(0);
-  for (int k0 = 0; k0 < D; k0 += KC) {
-    // this wavefront's x fragments for the chunk (two k-steps of 32)
-    bf16x8 a[KC / 32];
-#pragma unroll
-    for (int s = 0; s < KC / 32; ++s) {
-      if (arow_ok) {
-        a[s] = *reinterpret_cast<const bf16x8*>(xrow + k0 + s * 32);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a[s][i] = (__bf16)0.0f;
-      }
-    }
-    __syncthreads();          // previous chunk fully consumed
-    store_w();
-    __syncthreads();
-    if (k0 + KC < D) load_w(k0 + KC);   // in flight during the MFMAs
-#pragma unroll
-    for (int s = 0; s < KC / 32; ++s) {
-#pragma unroll
-      for (int eb = 0; eb < 4; ++eb) {
-        const int o = (eb * 16 + (lane & 15)) * WSTRIDE + s * 32 + (lane >> 4) * 8;
-        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&wsm[0][o]);
-        const bf16x8 bm = *reinterpret_cast<const bf16x8*>(&wsm[1][o]);
-        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&wsm[2][o]);
-        acc_lm[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bl, acc_lm[eb], 0, 0, 0);
-        acc_lm[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bm, acc_lm[eb], 0, 0, 0);
-        acc_hi[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bh, acc_hi[eb], 0, 0, 0);
-      }
-    }
-    // tot + cmp += chunk partial, with the rounding error of the add kept exactly (TwoSum)
-#pragma unroll
-    for (int eb = 0; eb < 4; ++eb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float s0 = tot[eb][i], p = acc_hi[eb][i];
-        const float t = s0 + p;
-        const float bp = t - s0;
-        const float err = (s0 - (t - bp)) + (p - bp);
-        tot[eb][i] = t;
-        cmp[eb][i] += err;
-      }
-      acc_hi[eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 part = {0.f, 0.f, 0.f, 0.f}, tot = part, cmp = part;
+#pragma unroll 4
+  for (int kb = 0; kb < KQ; kb += 16) {
+    const float4 b = *reinterpret_cast<const float4*>(bp + kb);
+    uint2 av = *reinterpret_cast<const uint2*>(ap + kb);
+    if (!aok) av = make_uint2(0u, 0u);
+    part = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av.x << 16), b.x, part, 0, 0, 0);
+    part = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av.x & 0xFFFF0000u), b.y, part, 0, 0, 0);
+    part = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av.y << 16), b.z, part, 0, 0, 0);
+    part = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av.y & 0xFFFF0000u), b.w, part, 0, 0, 0);
+    if ((kb & 63) == 48) {   // every 64 k: fold the chunk partial in with TwoSum
+      twosum_into(tot, cmp, part);
+      part = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
+  // element i: token tok0 + (lane/16)*4 + i, expert 16g + lane%16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = tok0 + (lane >> 4) * 4 + i;
+    if (t < T) partial[((size_t)kq * T + t) * E + g * 16 + (lane & 15)] = make_float2(tot[i], cmp[i]);
+  }
+}
 
-  // logit of token (lane/16)*4+i, expert eb*16 + lane%16
-#pragma unroll
-  for (int eb = 0; eb < 4; ++eb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      lsm[w][(lane >> 4) * 4 + i][eb * 16 + (lane & 15)] = tot[eb][i] + (cmp[eb][i] + acc_lm[eb][i]);
-  __syncthreads();
+// bf16x3 path: partial[kq][t][e] for TS x 16 tokens, 16 experts, one k-quarter
+template <int TS>
+__global__ __launch_bounds__(64) void router_partial_bf16x3_kernel(const bf16_t* __restrict__ x,
+                                                                   const bf16_t* __restrict__ planes, int T,
+                                                                   float2* __restrict__ partial) {
+  const int lane = threadIdx.x;
+  const int g = blockIdx.y & 3;              // expert group of 16
+  const int kq = blockIdx.y >> 2;            // k-quarter
+  const int tok0 = blockIdx.x * TS * 16;
 
-  if (tok0 >= T) return;
-  int cnt = 0;          // tokens of this block that chose expert `lane` so far
-  float psum = 0.f;     // sum of expert `lane`'s probabilities over the block
-  float lse2 = 0.f;     // sum of lse^2 over the block
-  const int ntok = min(ROUTE_BLOCK, T - tok0);
-  for (int r = 0; r < ntok; ++r) {
-    const int t = tok0 + r;
-    const float v = lsm[w][r][lane];
-    const float m = wave_max(v);
-    const float ex = expf(v - m);          // v - m is exact (Sterbenz) near the top
-    const float s = wave_sum(ex);
-    const float lse = m + logf(s);
-    const float p = ex / s;
-    psum += p;
-    lse2 += lse * lse;
-    float cand = v;
-    bool taken = false;
+  const bf16_t* bp = planes + (((size_t)g * KSTEPS + kq * (KQ / 32)) * 64 + lane) * 8;
+  const bf16_t* ap[TS];
+  bool aok[TS];
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const float mx = wave_max(taken ? -INFINITY : cand);
-      uint64_t hit = __ballot(!taken && cand == mx);
-      if (hit == 0) hit = __ballot(!taken);   // only NaN logits left: lowest free expert
-      const int win = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-      if (lane == win) {
-        ids[t * K + j] = lane;
-        probs[t * K + j] = p;
-        lrank[t * K + j] = static_cast<uint8_t>(cnt);
-        ++cnt;
-        taken = true;
+  for (int s = 0; s < TS; ++s) {
+    const int row = tok0 + s * 16 + (lane & 15);
+    aok[s] = row < T;
+    ap[s] = x + (size_t)(aok[s] ? row : 0) * D + kq * KQ + (lane >> 4) * 8;
+  }
+
+  f32x4 acc_hi[TS], acc_lm[TS], tot[TS], cmp[TS];
+#pragma unroll
+  for (int s = 0; s < TS; ++s) acc_hi[s] = acc_lm[s] = tot[s] = cmp[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int ks = 0; ks < KQ / 32; ++ks) {
+    const bf16x8 bh = *reinterpret_cast<const bf16x8*>(bp + ks * 512);
+    const bf16x8 bm = *reinterpret_cast<const bf16x8*>(bp + (size_t)E * D + ks * 512);
+    const bf16x8 bl = *reinterpret_cast<const bf16x8*>(bp + 2 * (size_t)E * D + ks * 512);
+#pragma unroll
+    for (int s = 0; s < TS; ++s) {
+      bf16x8 a = *reinterpret_cast<const bf16x8*>(ap[s] + ks * 32);
+      if (!aok[s]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = (__bf16)0.0f;
+      }
+      acc_lm[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc_lm[s], 0, 0, 0);
+      acc_lm[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bm, acc_lm[s], 0, 0, 0);
+      acc_hi[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc_hi[s], 0, 0, 0);
+    }
+    if (ks & 1) {   // every 64 k: fold the hi partial in with TwoSum
+#pragma unroll
+      for (int s = 0; s < TS; ++s) {
+        twosum_into(tot[s], cmp[s], acc_hi[s]);
+        acc_hi[s] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
   }
-  blk_counts[blk * E + lane] = cnt;
-  blk_psum[blk * E + lane] = psum;
-  if (lane == 0) blk_lse2[blk] = lse2;
+  // element i of sub-block s: token s*16 + (lane/16)*4 + i, expert 16g + lane%16
+#pragma unroll
+  for (int s = 0; s < TS; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = tok0 + s * 16 + (lane >> 4) * 4 + i;
+      if (t < T)
+        partial[((size_t)kq * T + t) * E + g * 16 + (lane & 15)] =
+            make_float2(tot[s][i], cmp[s][i] + acc_lm[s][i]);
+    }
+}
+
+__global__ __launch_bounds__(256) void router_select_kernel(SelectArgs a) {
+  __shared__ SelectLds L;
+  select_block(a.partial, a.T, blockIdx.x, L, a.ids, a.probs, a.lrank, a.blk_counts, a.blk_psum,
+               a.blk_lse2);
 }
 
 }  // namespace
 
-hipError_t launch_router(const RouterArgs& a, hipStream_t stream) {
-  const int nblk = (a.T + ROUTE_BLOCK - 1) / ROUTE_BLOCK;
-  if (a.T > 1024) {
-    const int grid = (nblk + 3) / 4;
-    hipLaunchKernelGGL(router_top8_kernel<4>, dim3(grid), dim3(256), 0, stream, a.x, a.wr, a.T,
-                       a.ids, a.probs, a.lrank, a.blk_counts, a.blk_psum, a.blk_lse2);
-  } else {
-    hipLaunchKernelGGL(router_top8_kernel<1>, dim3(nblk), dim3(64), 0, stream, a.x, a.wr, a.T,
-                       a.ids, a.probs, a.lrank, a.blk_counts, a.blk_psum, a.blk_lse2);
+hipError_t launch_router_partial(const RouterArgs& a, hipStream_t stream) {
+  if (a.T == 0) return hipSuccess;
+  if (a.T <= 2048) {
+    hipLaunchKernelGGL(router_partial_f32_kernel, dim3((a.T + 15) / 16, 16), dim3(64), 0, stream, a.x, a.wr,
+                       a.T, a.partial);
+    return hipGetLastError();
   }
+  hipLaunchKernelGGL(router_prep_kernel, dim3(E * D / 8 / 256), dim3(256), 0, stream, a.wr, a.planes);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int TS = 4;
+  hipLaunchKernelGGL(router_partial_bf16x3_kernel<TS>, dim3((a.T + TS * 16 - 1) / (TS * 16), 16), dim3(64), 0,
+                     stream, a.x, a.planes, a.T, a.partial);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_select(const SelectArgs& a, hipStream_t stream) {
+  if (a.T == 0) return hipSuccess;
+  const int nblk = (a.T + ROUTE_BLOCK - 1) / ROUTE_BLOCK;
+  hipLaunchKernelGGL(router_select_kernel, dim3(nblk), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -40,11 +40,11 @@ def test_workspace_bytes_formula():
     assert binding.workspace_bytes(-1) == 0
     assert binding.workspace_bytes((1 << 24) + 1) == 0
     w0 = binding.workspace_bytes(0)
-    assert 0 < w0 < 4096
+    assert 0 < w0 < 4096 + 786432 + 4096
     for T in (1, 32, 256, 4096, 16384):
         w = binding.workspace_bytes(T)
         act = 8 * T * (1024 + 2048) * 2
-        assert act <= w <= act + 8 * T * 20 + (T // 16 + 1) * 64 * 12 + 64 * 1024
+        assert act <= w <= act + 8 * T * 20 + T * 2048 + (T // 16 + 1) * 64 * 16 + 786432 + 64 * 1024
         lay = binding.workspace_layout(T)
         assert lay["offsets"] % 256 == 0 and lay["perm"] % 256 == 0 and lay["inv"] % 256 == 0
         assert lay["perm"] + 4 * 8 * T <= lay["inv"] <= w
@@ -97,9 +97,9 @@ def test_glue_entry_points_reject_bad_arguments(L):
 
 def test_timing_stage_names(L):
     assert L.olmoe_timing_enable(0) == binding.OK
-    names = [L.olmoe_timing_stage_name(i).decode() for i in range(6)]
-    assert names == ["router", "scan", "permute", "gateup", "down", "combine"]
-    assert L.olmoe_timing_stage_name(6) == b""
+    names = [L.olmoe_timing_stage_name(i).decode() for i in range(5)]
+    assert names == ["router", "dispatch", "gateup", "down", "combine"]
+    assert L.olmoe_timing_stage_name(5) == b""
     stats, calls = binding.timing_read()
     assert calls == 0 and set(stats) == set(names)
 
