@@ -80,15 +80,7 @@ def traffic_from_profiles(workload, stage):
     return rec.get("hbm_bytes_per_launch")
 
 
-def time_steps(step, steps, warmup, sync):
-    for _ in range(warmup):
-        step()
-    sync()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    sync()
-    return (time.perf_counter() - t0) / steps
+N_WEIGHT_SETS = 4   # single-layer steps cycle through distinct weight sets (3.2 GB, far above the 256 MB MALL)
 
 
 def measure(workload, steps, warmup, seed=0):
@@ -109,42 +101,68 @@ def measure(workload, steps, warmup, seed=0):
         out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
         ids = torch.empty((T, K), dtype=torch.int32, device=dev)
         probs = torch.empty((T, K), dtype=torch.float32, device=dev)
+        # set 0 is the workload's own layer; the others are further layers of the same recipe, so
+        # consecutive steps never find the previous step's weights in a cache
+        sets = [d] + [inputs.device_weights(seed, workload, layer=r, skew=wl.skew)
+                      for r in range(1, N_WEIGHT_SETS)]
+        it = [0]
 
         def step():
-            binding.moe_forward(d["x"], d["w_router"], d["w_gate"], d["w_up"], d["w_down"], out=out,
+            w = sets[it[0] % N_WEIGHT_SETS]
+            it[0] += 1
+            binding.moe_forward(d["x"], w["w_router"], w["w_gate"], w["w_up"], w["w_down"], out=out,
                                 route_ids=ids, route_probs=probs, expert_counts=counts, aux_loss=aux,
                                 z_loss=z, workspace=ws)
-        step()
-        sync()
-        touched_per_layer = [int((counts > 0).sum().item())]
+        touched_per_layer = []
+        for _ in range(N_WEIGHT_SETS):
+            step()
+            touched_per_layer.append(int((counts > 0).sum().item()))
     else:
         h = d["h0"].clone()
-        stack_ws = ws
 
         def step():
-            binding.moe_stack_forward(h, d["layers"], workspace=stack_ws)
-        r = binding.moe_stack_forward(d["h0"].clone(), d["layers"], workspace=stack_ws)
+            binding.moe_stack_forward(h, d["layers"], workspace=ws)
+        r = binding.moe_stack_forward(d["h0"].clone(), d["layers"], workspace=ws)
         sync()
         touched_per_layer = [int(v) for v in (r["expert_counts"] > 0).sum(1).tolist()]
 
-    sec = time_steps(step, steps, warmup, sync)
-
-    # per-stage durations with HIP events on the launch stream (separate pass)
+    for _ in range(warmup):
+        step()
+    sync()
+    # short pass with every stage bracketed: the per-stage split, and which expert GEMM dominates
     binding.timing_enable(True)
-    for _ in range(steps):
+    for _ in range(max(3, steps // 5)):
         step()
     sync()
     stage_sum, calls = binding.timing_read()
-    binding.timing_enable(False)
     stage_ms = {k: v / calls for k, v in stage_sum.items()}     # per launch
+    dom = max(("gateup", "down"), key=lambda s: stage_ms[s])
+    # event-free pass: the plain wall clock of K steps
+    binding.timing_enable(False)
+    sync()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    sync()
+    sec_plain = (time.perf_counter() - t0) / steps
+    # timed region: K steps with the dominant kernel bracketed by HIP events on its launch stream
+    binding.timing_enable([dom])
+    sync()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    sync()
+    sec = (time.perf_counter() - t0) / steps
+    dom_sum, dom_calls = binding.timing_read()
+    binding.timing_enable(False)
+    dom_ms = dom_sum[dom] / dom_calls
 
     L = wl.layers
-    touched = sum(touched_per_layer) / L
+    touched = sum(touched_per_layer) / len(touched_per_layer)      # per layer call
     flop = FLOP_PER_TOKEN * T * L
-    byts = sum(layer_bytes(T, t) for t in touched_per_layer)
-    dom = max(("gateup", "down"), key=lambda s: stage_ms[s])
+    byts = layer_bytes(T, touched) * L
     f_k, b_k = stage_model(dom, T, touched)
-    dur = stage_ms[dom] * 1e-3
+    dur = dom_ms * 1e-3
     intensity = f_k / b_k
     if intensity < RIDGE:
         achieved = b_k / dur / 1e9
@@ -155,12 +173,12 @@ def measure(workload, steps, warmup, seed=0):
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
     roof["kernel"] = dom
-    roof["kernel_ms"] = round(stage_ms[dom], 5)
+    roof["kernel_ms"] = round(dom_ms, 5)
     roof["algorithmic_flop"] = f_k
     roof["algorithmic_bytes"] = b_k
     roof["traffic"] = traffic_from_profiles(workload, dom)
     res = {
-        "workload": workload, "tokens": T, "layers": L, "sec": sec,
+        "workload": workload, "tokens": T, "layers": L, "sec": sec, "sec_plain": sec_plain,
         "tokens_per_s": T / sec, "tflops": flop / sec / 1e12, "hbm_gbs": byts / sec / 1e9,
         "layer_hbm_frac": byts / sec / 1e9 / HBM_PEAK_GBS,
         "layer_mfma_frac": flop / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
@@ -205,6 +223,131 @@ def cpu_baseline(d, workload, budget_s=20.0):
                       f"{el:.1f} s, float64 NumPy"}
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries: kernel-trace statistics and HBM traffic from counters
+# ---------------------------------------------------------------------------
+COPY_PROBE_BYTES = 1 << 30
+
+
+def copy_probe():
+    """A plain elementwise copy of known size (reads and writes 1 GiB), the calibration
+    kernel for the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES}), flush=True)
+
+
+def _stage_of(kernel_name):
+    n = kernel_name
+    if "grouped_gemm_kernel" in n:
+        cfg = n[n.index("Cfg<") + 4:n.index(">")].split(",")
+        return "gateup" if cfg[4].strip() == "true" else "down"
+    for key, stage in (("router", "router"), ("scan", "dispatch"), ("permute", "dispatch"),
+                       ("combine_kernel", "combine"), ("rmsnorm", "rmsnorm"), ("residual", "residual")):
+        if key in n:
+            return stage
+    return None
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        rows += list(csv.DictReader(open(f)))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return rows
+
+
+def _per_dispatch(rows, counter, select):
+    """Median over dispatches of the counter's per-dispatch total, for kernels `select` accepts."""
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] == counter and select(r["Kernel_Name"]):
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    v = sorted(per.values())
+    return (v[len(v) // 2], len(v)) if v else (None, 0)
+
+
+def traffic_summary(args):
+    """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE over the workload and over
+    the copy probe) into per-launch HBM bytes per stage, scaled so that the copy probe reads
+    and writes exactly its known size."""
+    wl = args.workload
+    fetch, write = _counter_rows(args.fetch_dir), _counter_rows(args.write_dir)
+    cf, cw = _counter_rows(args.copy_fetch_dir), _counter_rows(args.copy_write_dir)
+    is_copy = lambda n: "elementwise" in n
+    copy_f, _ = _per_dispatch(cf, "FETCH_SIZE", is_copy)
+    copy_w, _ = _per_dispatch(cw, "WRITE_SIZE", is_copy)
+    kf = COPY_PROBE_BYTES / copy_f      # bytes per counted unit (nominally KiB)
+    kw = COPY_PROBE_BYTES / copy_w
+    src_hash = kernel_source_hash()
+    lines = [f"# HBM traffic per launch, {wl}", "",
+             "Counters FETCH_SIZE and WRITE_SIZE (rocprofv3, one counter per run), median over",
+             "dispatches, scaled by the same counters for a plain 1 GiB elementwise copy",
+             f"(torch.neg over float32: reads and writes {COPY_PROBE_BYTES} B).", "",
+             f"- copy probe: FETCH_SIZE {copy_f:.1f}, WRITE_SIZE {copy_w:.1f} per dispatch",
+             f"- scale: fetch {kf:.2f} B/unit, write {kw:.2f} B/unit",
+             f"- kernel sources hash: {src_hash}", "",
+             "| stage | dispatches | fetch bytes | write bytes | HBM bytes / launch | algorithmic bytes | ratio |",
+             "|---|---|---|---|---|---|---|"]
+    T = None
+    from sparse_mixture_experts_expert_amd import inputs
+    T = inputs.WORKLOADS[wl].tokens
+    touched = args.touched
+    for stage in ("router", "dispatch", "gateup", "down", "combine"):
+        f, nf = _per_dispatch(fetch, "FETCH_SIZE", lambda n, st=stage: _stage_of(n) == st)
+        w, nw = _per_dispatch(write, "WRITE_SIZE", lambda n, st=stage: _stage_of(n) == st)
+        if f is None or w is None:
+            continue
+        fb, wb = f * kf, w * kw
+        _, alg = stage_model(stage, T, touched)
+        ratio = f"{(fb + wb) / alg:.3f}" if alg else "-"
+        lines.append(f"| {stage} | {nf} | {fb:.4g} | {wb:.4g} | {fb + wb:.4g} | {alg:.4g} | {ratio} |")
+        rec = {"workload": wl, "stage": stage, "hbm_bytes_per_launch": round(fb + wb),
+               "fetch_bytes": round(fb), "write_bytes": round(wb), "algorithmic_bytes": alg,
+               "source_hash": src_hash, "copy_scale_fetch": kf, "copy_scale_write": kw}
+        with open(os.path.join(ROOT, "profiles", f"traffic_{stage}_{wl}.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+    lines += ["", "Commands (from the repository root, TMPDIR=/tmp):", "", "```"] + args.commands + ["```", ""]
+    with open(os.path.join(ROOT, "profiles", f"traffic_{wl}.md"), "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def stats_summary(args):
+    """Short text summary of a rocprofv3 --kernel-trace --stats run."""
+    import csv
+    import glob
+    fs = glob.glob(os.path.join(args.stats_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not fs:
+        raise SystemExit(f"no kernel_stats.csv under {args.stats_dir}")
+    rows = list(csv.DictReader(open(fs[0])))
+    lines = [f"# Kernel durations, {args.workload}", "",
+             "rocprofv3 --kernel-trace --stats; durations in microseconds per dispatch.", "",
+             "| kernel | stage | calls | average | min | max |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        n = r["Name"]
+        st = _stage_of(n)
+        if st is None:
+            continue    # input generation and copies made by the harness around the layer
+        short = n.replace("olmoe::(anonymous namespace)::", "").replace("void ", "")
+        short = short.split("(")[0] if "Cfg" not in short else short[:short.index(">") + 1].replace(
+            "grouped_gemm_kernel<", "grouped_gemm_kernel ")
+        lines.append(f"| {short} | {st} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    lines += ["", f"kernel sources hash: {kernel_source_hash()}", "",
+              "Command (from the repository root, TMPDIR=/tmp):", "", "```"] + args.commands + ["```", ""]
+    with open(os.path.join(ROOT, "profiles", f"kernels_{args.workload}.md"), "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,7 +357,23 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true", help="run the counter-calibration copy and exit")
+    ap.add_argument("--traffic-summary", action="store_true", help="summarise --pmc runs into profiles/")
+    ap.add_argument("--stats-summary", metavar="DIR", dest="stats_dir", help="summarise a --stats run")
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
+    ap.add_argument("--copy-fetch-dir")
+    ap.add_argument("--copy-write-dir")
+    ap.add_argument("--touched", type=float, default=64.0, help="experts touched per layer (traffic model)")
+    ap.add_argument("--command", dest="commands", action="append", default=[],
+                    help="command line recorded in a summary (repeatable)")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args)
+        return
+    if args.stats_dir:
+        stats_summary(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share: this build runs on a single MI355X "
               "(the data-parallel shard needs no communication); use --gpus 1", file=sys.stderr)
@@ -224,6 +383,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU available", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        copy_probe()
+        return
     from sparse_mixture_experts_expert_amd import binding
     binding.lib()
 
@@ -236,11 +398,13 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(main_res["sec"] * 1e3, 5),
+        "ms_per_step_without_events": round(main_res["sec_plain"] * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded; N(0,1) tokens, N(0,0.02) weights, random init)",
+        "data": f"synthetic (seeded; N(0,1) tokens, N(0,0.02) weights, random init; "
+                f"{N_WEIGHT_SETS if main_res['layers'] == 1 else main_res['layers']} distinct weight sets cycled)",
         "config": {"workload": args.workload, "tokens": main_res["tokens"], "layers": main_res["layers"],
                    "hidden": D, "expert_width": F, "experts": E, "top_k": K},
         "tflops": round(main_res["tflops"], 2),
@@ -259,6 +423,7 @@ def main():
         s.pop("host_inputs")
         line["secondary"] = {"workload": "prefill-4096", "value": round(s["tokens_per_s"], 1),
                              "unit": "tokens/s", "ms_per_step": round(s["sec"] * 1e3, 5),
+                             "ms_per_step_without_events": round(s["sec_plain"] * 1e3, 5),
                              "tflops": round(s["tflops"], 2), "layer_mfma_frac": round(s["layer_mfma_frac"], 4),
                              "stage_ms": s["stage_ms"], "roofline": s["roofline"]}
         d = None

@@ -146,15 +146,19 @@ OLMOE_API olmoe_status_t olmoe_rmsnorm_bf16(const float* h, float eps, int64_t T
 OLMOE_API olmoe_status_t olmoe_residual_add(float* h, const void* y, int64_t T, void* stream);
 
 /* Per-stage timing of olmoe_moe_forward with HIP events recorded on the
- * caller's stream between its stages: router (logits, softmax, top-8),
- * dispatch (scan and permutation), gateup, down, combine.  olmoe_timing_enable(1) starts recording for later calls
- * on this thread and clears the sums; olmoe_timing_read() waits for the
- * recorded events, fills up to `max_stages` per-stage sums in milliseconds,
- * writes the number of timed calls to *calls, and returns the number of
- * stages (or -1 on error).  Names of the stages: olmoe_timing_stage_name(i).
- * Recording adds one event per stage boundary; leave it disabled for
- * end-to-end timing. */
-OLMOE_API olmoe_status_t olmoe_timing_enable(int enable);
+ * caller's stream at the boundaries of its stages: 0 router (logits,
+ * softmax, top-8), 1 dispatch (scan and permutation), 2 gateup, 3 down,
+ * 4 combine.  olmoe_timing_enable(stage_mask) starts recording for later
+ * calls on this thread (bit i of the mask brackets stage i; 0 stops
+ * recording; OLMOE_TIMING_ALL brackets every stage) and clears the sums; a
+ * mask with bits beyond the stages gives OLMOE_EINVAL.  olmoe_timing_read()
+ * waits for the recorded events, fills up to `max_stages` per-stage sums in
+ * milliseconds (0 for stages outside the mask), writes the number of timed
+ * calls to *calls, and returns the number of stages (or -1 on error).  Names
+ * of the stages: olmoe_timing_stage_name(i).  Each recorded boundary costs
+ * the stream a little time, so bracket only the stages of interest. */
+#define OLMOE_TIMING_ALL 0x1F
+OLMOE_API olmoe_status_t olmoe_timing_enable(int stage_mask);
 OLMOE_API int olmoe_timing_read(double* stage_ms, int max_stages, int* calls);
 OLMOE_API const char* olmoe_timing_stage_name(int stage);
 

@@ -191,16 +191,35 @@ def moe_stack_forward(h, layers, eps: float = 1e-5, keep_inputs: bool = False, w
             "inputs": inputs}
 
 
-def timing_enable(flag: bool = True):
-    _check(lib().olmoe_timing_enable(1 if flag else 0))
+TIMING_STAGES = ("router", "dispatch", "gateup", "down", "combine")
+
+
+def timing_enable(stages=True):
+    """Bracket stages of later forward calls with HIP events: True = every stage,
+    False = off, or an iterable of stage names."""
+    if stages is True:
+        mask = (1 << len(TIMING_STAGES)) - 1
+    elif not stages:
+        mask = 0
+    else:
+        mask = 0
+        for name in stages:
+            mask |= 1 << TIMING_STAGES.index(name)
+    _check(lib().olmoe_timing_enable(mask))
+    global _timing_mask
+    _timing_mask = mask
+
+
+_timing_mask = 0
 
 
 def timing_read():
-    """Per-stage summed milliseconds and the number of timed calls since timing_enable."""
+    """Summed milliseconds of each bracketed stage and the number of timed calls since
+    timing_enable."""
     buf = (ctypes.c_double * 16)()
     calls = ctypes.c_int()
     n = lib().olmoe_timing_read(buf, 16, ctypes.byref(calls))
     if n < 0:
         raise OlmoeError(EHIP, lib().olmoe_last_error().decode())
     names = [lib().olmoe_timing_stage_name(i).decode() for i in range(n)]
-    return {names[i]: buf[i] for i in range(n)}, calls.value
+    return {names[i]: buf[i] for i in range(n) if _timing_mask >> i & 1}, calls.value

@@ -112,28 +112,37 @@ constexpr int N_STAGES = 5;
 const char* kStageNames[N_STAGES] = {"router", "dispatch", "gateup", "down", "combine"};
 
 struct TimingState {
-  bool enabled = false;
-  std::vector<std::vector<hipEvent_t>> pending;  // one set of N_STAGES+1 events per call
+  int mask = 0;   // bit i: bracket stage i with events
+  std::vector<std::vector<hipEvent_t>> pending;  // one set of N_STAGES+1 boundary events per call
 };
 thread_local TimingState g_timing;
+
+// boundary b lies between stage b-1 and stage b; it is recorded when either side is timed
+bool boundary_needed(int mask, int b) {
+  return (b > 0 && (mask >> (b - 1) & 1)) || (b < N_STAGES && (mask >> b & 1));
+}
 
 struct StageRecorder {
   std::vector<hipEvent_t>* ev = nullptr;
   hipStream_t s;
   int next = 0;
   explicit StageRecorder(hipStream_t st) : s(st) {
-    if (!g_timing.enabled || g_timing.pending.size() >= 65536) return;
-    g_timing.pending.emplace_back(N_STAGES + 1);
+    if (!g_timing.mask || g_timing.pending.size() >= 65536) return;
+    g_timing.pending.emplace_back(N_STAGES + 1, nullptr);
     ev = &g_timing.pending.back();
-    for (auto& x : *ev) (void)hipEventCreate(&x);
-    (void)hipEventRecord((*ev)[0], s);
-    next = 1;
+    for (int b = 0; b <= N_STAGES; ++b)
+      if (boundary_needed(g_timing.mask, b)) (void)hipEventCreate(&(*ev)[b]);
+    record();
+  }
+  void record() {
+    if ((*ev)[next]) (void)hipEventRecord((*ev)[next], s);
+    ++next;
   }
   void mark() {
-    if (ev && next <= N_STAGES) (void)hipEventRecord((*ev)[next++], s);
+    if (ev && next <= N_STAGES) record();
   }
   void finish() {
-    while (ev && next <= N_STAGES) (void)hipEventRecord((*ev)[next++], s);
+    while (ev && next <= N_STAGES) record();
   }
 };
 
@@ -293,11 +302,14 @@ olmoe_status_t olmoe_residual_add(float* h, const void* y, int64_t T, void* stre
   return ok();
 }
 
-olmoe_status_t olmoe_timing_enable(int enable) {
+olmoe_status_t olmoe_timing_enable(int stage_mask) {
+  if (stage_mask < 0 || stage_mask >= (1 << N_STAGES))
+    return fail(OLMOE_EINVAL, "stage mask 0x%x has bits beyond the %d stages", stage_mask, N_STAGES);
   for (auto& set : g_timing.pending)
-    for (auto& e : set) (void)hipEventDestroy(e);
+    for (auto& e : set)
+      if (e) (void)hipEventDestroy(e);
   g_timing.pending.clear();
-  g_timing.enabled = enable != 0;
+  g_timing.mask = stage_mask;
   return ok();
 }
 
@@ -309,11 +321,14 @@ int olmoe_timing_read(double* stage_ms, int max_stages, int* calls) {
   for (int i = 0; i < max_stages && i < N_STAGES; ++i) stage_ms[i] = 0.0;
   int n = 0;
   for (auto& set : g_timing.pending) {
-    if (hipEventSynchronize(set[N_STAGES]) != hipSuccess) {
+    int last = N_STAGES;
+    while (last > 0 && !set[last]) --last;
+    if (set[last] && hipEventSynchronize(set[last]) != hipSuccess) {
       fail(OLMOE_EHIP, "hipEventSynchronize failed");
       return -1;
     }
     for (int i = 0; i < N_STAGES; ++i) {
+      if (!set[i] || !set[i + 1] || !(g_timing.mask >> i & 1)) continue;
       float ms = 0.f;
       (void)hipEventElapsedTime(&ms, set[i], set[i + 1]);
       if (i < max_stages) stage_ms[i] += ms;

@@ -101,7 +101,16 @@ def test_timing_stage_names(L):
     assert names == ["router", "dispatch", "gateup", "down", "combine"]
     assert L.olmoe_timing_stage_name(5) == b""
     stats, calls = binding.timing_read()
-    assert calls == 0 and set(stats) == set(names)
+    assert calls == 0 and stats == {}
+    binding.timing_enable(["gateup", "down"])
+    stats, calls = binding.timing_read()
+    assert calls == 0 and set(stats) == {"gateup", "down"}
+    binding.timing_enable(True)
+    stats, calls = binding.timing_read()
+    assert set(stats) == set(names)
+    assert L.olmoe_timing_enable(1 << 5) == binding.EINVAL
+    assert L.olmoe_timing_enable(-1) == binding.EINVAL
+    binding.timing_enable(False)
 
 
 def test_binding_raises_loudly_without_library(monkeypatch):
