@@ -53,8 +53,8 @@ Layout make_layout(int64_t T) {
   L.offsets = take(65 * 4);
   L.tp_gu = take(65 * 4);
   L.tp_dn = take(65 * 4);
-  // +8: the GEMM grids are rounded up to a multiple of 8 workgroups, and a surplus
-  // workgroup reads one entry past the last possible tile before it returns
+  // sized for the largest possible tile count (+8 spare entries); GEMM workgroups beyond the
+  // real count return before reading the list
   const size_t max_tiles = static_cast<size_t>(max_row_tiles(static_cast<int>(T), MIN_TILE_ROWS)) + 8;
   L.tiles_gu = take(max_tiles * 8);
   L.tiles_dn = take(max_tiles * 8);
