@@ -83,13 +83,13 @@ def traffic_from_profiles(workload, stage):
 N_WEIGHT_SETS = 4   # single-layer steps cycle through distinct weight sets (3.2 GB, far above the 256 MB MALL)
 
 
-def measure(workload, steps, warmup, seed=0):
+def measure(workload, steps, warmup, seed=0, tokens=None):
     import torch
     from sparse_mixture_experts_expert_amd import binding, inputs
 
     wl = inputs.WORKLOADS[workload]
-    T = wl.tokens
-    d = inputs.device_workload(workload, seed=seed)
+    T = wl.tokens if tokens is None else tokens
+    d = inputs.device_workload(workload, seed=seed, tokens=T)
     ws = binding.make_workspace(T)
     dev = "cuda"
     counts = torch.empty(E, dtype=torch.int32, device=dev)
@@ -355,6 +355,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode-256")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--tokens", type=int, default=None, help="override the workload's token count")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help="run the counter-calibration copy and exit")
@@ -389,7 +390,7 @@ def main():
     from sparse_mixture_experts_expert_amd import binding
     binding.lib()
 
-    main_res = measure(args.workload, args.steps, args.warmup, args.seed)
+    main_res = measure(args.workload, args.steps, args.warmup, args.seed, args.tokens)
     line = {
         "metric": METRIC,
         "value": round(main_res["tokens_per_s"], 1),

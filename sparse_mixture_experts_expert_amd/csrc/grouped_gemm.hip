@@ -23,7 +23,7 @@
 //
 // Operand staging: an S-stage ring of LDS tiles, BK k wide, filled by direct
 // global->LDS 16-byte loads (each lane supplies its own address, so the row
-// gather costs nothing extra).  A wavefront's load covers 1 KiB: 1024/(2 BK)
+// gather costs nothing extra), issued a slice per MFMA k-step.  A wavefront's load covers 1 KiB: 1024/(2 BK)
 // rows x 2 BK contiguous bytes, whole cache lines per row.  The 16-byte chunks
 // land with the low 3 bits of their index XOR-swizzled by row, so the MFMA
 // fragment reads (8 rows x 16 bytes per group of lanes) hit distinct banks.  One barrier per k-step,
@@ -131,8 +131,15 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches below
   const int wm = wv / C::WN, wn = wv % C::WN;
+  // fragment i of wave row wm covers tile rows (i * WM + wm) * 32 .. +32, so the fragments of a
+  // partly filled tile spread over all waves (and SIMDs).  This wave's fragments past `valid`
+  // (always a suffix) are skipped: nf, the count of the others, picks one of FM+1 copies of
+  // the k-loop once, so no branch sits between the MFMAs of a loop.
+  int nf = 0;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) nf += (i * C::WM + wm) * 32 < valid;
 
   // LDS-DMA sources: load j of wavefront wv fills stage rows (j*NW + wv)*RPL .. +RPL;
   // lane -> row + lane/CPR, slot lane%CPR, which holds chunk slot ^ (row & 7)
@@ -162,11 +169,13 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
   // requests over the memory channels (every tile row starts on a 4 KiB boundary); the
   // order is a function of the unit only, so results stay reproducible
   const int k0 = C::ROT ? (logical * 5) % C::KT : 0;
-  auto issue = [&](int kt, int sl) {
+  // loads j0 .. j1-1 of stage kt into ring slot sl
+  auto issue = [&](int kt, int sl, int j0, int j1) {
     int kr = kt + k0;
     kr = kr >= C::KT ? kr - C::KT : kr;
 #pragma unroll
     for (int j = 0; j < C::IPS; ++j) {
+      if (j < j0 || j >= j1) continue;
       const auto src = GPTR(gp[j] + kr * BK);
       const auto dst = LPTR(&smem[sl][(j * C::NW + wv) * C::RPL * BK]);
       if (C::NTW && j >= C::JA)
@@ -188,52 +197,68 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
 
 #pragma unroll
   for (int s = 0; s < C::STAGES - 1; ++s)
-    if (s < C::KT) issue(s, s);
+    if (s < C::KT) issue(s, s, 0, C::IPS);
 
-  for (int kt = 0; kt < C::KT; ++kt) {
-    wait_stage<C, C::STAGES - 2>(min(C::STAGES - 2, C::KT - 1 - kt));
-    if (kt + C::STAGES - 1 < C::KT) issue(kt + C::STAGES - 1, (kt + C::STAGES - 1) % C::STAGES);
-    const bf16_t* As = smem[kt % C::STAGES];
-    const bf16_t* Bs = As + C::BM * BK;
+  constexpr int NKK = BK / 16;   // MFMA k-steps per stage
+  auto kloop = [&](auto nf_tag) __attribute__((always_inline)) {
+    constexpr int NF = decltype(nf_tag)::value;
+    for (int kt = 0; kt < C::KT; ++kt) {
+      wait_stage<C, C::STAGES - 2>(min(C::STAGES - 2, C::KT - 1 - kt));
+      const bool more = kt + C::STAGES - 1 < C::KT;
+      const int next_slot = (kt + C::STAGES - 1) % C::STAGES;
+      const bf16_t* As = smem[kt % C::STAGES];
+      const bf16_t* Bs = As + C::BM * BK;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int kc = kk * 2 + (lane >> 5);
-      using V = typename C::V;
-      V af[C::FM], bfr[C::G][C::FN];
+      for (int kk = 0; kk < NKK; ++kk) {
+        // the next stage's loads go out a slice per MFMA k-step: issuing them all at once
+        // stalls the wave on the memory queue before its MFMAs can start
+        if (more) issue(kt + C::STAGES - 1, next_slot, kk * C::IPS / NKK, (kk + 1) * C::IPS / NKK);
+        if constexpr (NF > 0) {
+          const int kc = kk * 2 + (lane >> 5);
+          using V = typename C::V;
+          V af[NF], bfr[C::G][C::FN];
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
-        const int r = wm * (C::BM / C::WM) + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const V*>(&As[swz<BK>(r, kc)]);
-      }
+          for (int i = 0; i < NF; ++i) {
+            const int r = (i * C::WM + wm) * 32 + (lane & 31);
+            af[i] = *reinterpret_cast<const V*>(&As[swz<BK>(r, kc)]);
+          }
 #pragma unroll
-      for (int g = 0; g < C::G; ++g)
+          for (int g = 0; g < C::G; ++g)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          const int r = g * C::BN + wn * (C::BN / C::WN) + j * 32 + (lane & 31);
-          u32x4 v = *reinterpret_cast<const u32x4*>(&Bs[swz<BK>(r, kc)]);
-          if constexpr (!C::GATEUP) {   // bf16 -> fp16 (exact in fp16's normal range)
+            for (int j = 0; j < C::FN; ++j) {
+              const int r = g * C::BN + wn * (C::BN / C::WN) + j * 32 + (lane & 31);
+              u32x4 v = *reinterpret_cast<const u32x4*>(&Bs[swz<BK>(r, kc)]);
+              if constexpr (!C::GATEUP) {   // bf16 -> fp16 (exact in fp16's normal range)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v[q] << 16),
-                                                        __uint_as_float(v[q] & 0xFFFF0000u));
-              v[q] = __builtin_bit_cast(uint32_t, h);
+                for (int q = 0; q < 4; ++q) {
+                  const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v[q] << 16),
+                                                            __uint_as_float(v[q] & 0xFFFF0000u));
+                  v[q] = __builtin_bit_cast(uint32_t, h);
+                }
+              }
+              bfr[g][j] = __builtin_bit_cast(V, v);
             }
-          }
-          bfr[g][j] = __builtin_bit_cast(V, v);
+#pragma unroll
+          for (int g = 0; g < C::G; ++g)
+#pragma unroll
+            for (int i = 0; i < NF; ++i)
+#pragma unroll
+              for (int j = 0; j < C::FN; ++j) {
+                if constexpr (C::GATEUP)
+                  acc[g][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[g][j], acc[g][i][j], 0, 0, 0);
+                else
+                  acc[g][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bfr[g][j], acc[g][i][j], 0, 0, 0);
+              }
         }
-#pragma unroll
-      for (int g = 0; g < C::G; ++g)
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j) {
-            if constexpr (C::GATEUP)
-              acc[g][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[g][j], acc[g][i][j], 0, 0, 0);
-            else
-              acc[g][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bfr[g][j], acc[g][i][j], 0, 0, 0);
-          }
+      }
     }
-  }
+  };
+  static_assert(C::FM <= 4, "k-loop copies");
+  if (nf >= C::FM) kloop(std::integral_constant<int, C::FM>{});
+  else if (C::FM > 1 && nf == 1) kloop(std::integral_constant<int, (C::FM > 1 ? 1 : 0)>{});
+  else if (C::FM > 2 && nf == 2) kloop(std::integral_constant<int, (C::FM > 2 ? 2 : 0)>{});
+  else if (C::FM > 3 && nf == 3) kloop(std::integral_constant<int, (C::FM > 3 ? 3 : 0)>{});
+  else kloop(std::integral_constant<int, 0>{});
 
   // C layout of a 32x32 fragment: lane holds column lane%32, rows (v/4)*8 + (lane/32)*4 + v%4
 #pragma unroll
@@ -242,7 +267,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
     for (int j = 0; j < C::FN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = wm * (C::BM / C::WM) + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        const int r = (i * C::WM + wm) * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
         const int c = nt * C::BN + wn * (C::BN / C::WN) + j * 32 + (lane & 31);
         if (r < valid) {
           float o;
@@ -256,12 +281,15 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
 // tile sets by batch size (rows per expert ~ T/8), chosen by measurement on MI355X.  Up to a
 // few hundred tokens the layer is bound by streaming the weights once; marking gate/up loads
 // non-temporal keeps them from displacing the token rows that every column tile re-reads.
+// Large batches use 8 waves (2 per SIMD) on 256-row tiles: more MFMA work per byte staged.
 using GuTiny = Cfg<32, 64, 1, 2, true, 4, 64, 1, true>;
 using DnTiny = Cfg<32, 64, 1, 2, false, 4>;
 using GuSmall = Cfg<64, 64, 2, 2, true, 3, 64, 1, true>;
 using DnSmall = Cfg<64, 128, 2, 2, false, 3>;
-using GuLarge = Cfg<128, 128, 2, 2, true, 3, 64, 0>;
-using DnLarge = Cfg<128, 128, 2, 2, false, 2>;
+using GuMedium = Cfg<128, 128, 2, 2, true, 3, 64, 0>;
+using DnMedium = Cfg<128, 128, 2, 2, false, 2>;
+using GuLarge = Cfg<256, 128, 4, 2, true, 2, 64, 0>;
+using DnLarge = Cfg<256, 256, 4, 2, false, 2, 64, 0>;
 
 template <class C>
 hipError_t launch_cfg(const bf16_t* A, const bf16_t* W0, const bf16_t* W1, const GemmArgs& a,
@@ -295,8 +323,12 @@ GemmPlan plan_gemm(int T) {
     p.variant = 1;
     p.bm_gu = GuSmall::BM;
     p.bm_dn = DnSmall::BM;
-  } else {
+  } else if (T <= LARGE_TOKENS) {
     p.variant = 2;
+    p.bm_gu = GuMedium::BM;
+    p.bm_dn = DnMedium::BM;
+  } else {
+    p.variant = 3;
     p.bm_gu = GuLarge::BM;
     p.bm_dn = DnLarge::BM;
   }
@@ -307,6 +339,7 @@ hipError_t launch_gateup(const GemmArgs& a, const GemmPlan& p, hipStream_t strea
   switch (p.variant) {
     case 0: return launch_cfg<GuTiny>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
     case 1: return launch_cfg<GuSmall>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
+    case 2: return launch_cfg<GuMedium>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
     default: return launch_cfg<GuLarge>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
   }
 }
@@ -315,6 +348,7 @@ hipError_t launch_down(const GemmArgs& a, const GemmPlan& p, hipStream_t stream)
   switch (p.variant) {
     case 0: return launch_cfg<DnTiny>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
     case 1: return launch_cfg<DnSmall>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
+    case 2: return launch_cfg<DnMedium>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
     default: return launch_cfg<DnLarge>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
   }
 }

@@ -179,8 +179,8 @@ struct ScanLds {
   int tgu[E + 1], tdn[E + 1];   // row-tile prefixes
 };
 
-// write the row-tile list of one GEMM: tile t of expert e (tp[e] <= t < tp[e+1])
-// covers rows off[e] + (t - tp[e]) * bm .. of that expert
+// write the row-tile list of one GEMM: tile t of expert e (tp[e] <= t < tp[e+1]) covers
+// rows off[e] + (t - tp[e]) * q .. of that expert, q <= bm as below
 __device__ __forceinline__ void fill_tiles(const int* tp, const int* off, int bm, int2* tiles) {
   const int n = tp[E];
   for (int t = threadIdx.x; t < n; t += blockDim.x) {
@@ -189,8 +189,13 @@ __device__ __forceinline__ void fill_tiles(const int* tp, const int* off, int bm
       const int mid = (lo + hi) >> 1;
       if (tp[mid] <= t) lo = mid; else hi = mid;
     }
-    const int row0 = off[lo] + (t - tp[lo]) * bm;
-    const int rows = min(bm, off[lo + 1] - row0);
+    // the expert's c rows go to its ceil(c/bm) tiles in near-equal parts, each a multiple of
+    // 32 rows (one MFMA fragment) except the last, so no tile is mostly padding
+    const int c = off[lo + 1] - off[lo];
+    const int n = tp[lo + 1] - tp[lo];
+    const int q = min(bm, ((c + n - 1) / n + 31) & ~31);
+    const int row0 = off[lo] + (t - tp[lo]) * q;
+    const int rows = min(q, off[lo + 1] - row0);
     tiles[t] = make_int2(row0, lo | (rows << 8));
   }
 }
