@@ -17,8 +17,9 @@ Sources (page title, then section / equation):
        dropless token choice), 4.1.6 and 4.1.7 (loss weights 0.01 and 0.001).
   [X]  "Mixture-of-experts LLMs from scratch with OLMoE": section 2 "The router
        and the experts" (softmax over all experts then top-k, grouped dispatch,
-       every-expert brute force) and section 3 "OLMoE in PyTorch" (no
-       renormalisation, float32 residual stream, RMSNorm).
+       every-expert brute force, the renormalised router variant), section 3
+       "OLMoE in PyTorch" (no renormalisation, float32 residual stream, RMSNorm)
+       and section 5 "A smaller model for one kind of text" (pruned experts).
 
 Readings taken where the pages are silent or disagree:
   * routing weights are the 64-way softmax probabilities of the chosen experts,
@@ -29,6 +30,12 @@ Readings taken where the pages are silent or disagree:
     (as [G]'s code does), the z-loss is beta*mean_t(lse_t^2); both are returned
     separately and their sum is [G]'s total auxiliary loss;
   * for T = 0 both losses are 0 and nothing else is produced;
+  * router variants (off by default): `renormalize` divides the chosen weights
+    by their sum (the Mixtral / Qwen3 router of [X] section 2, equal to [G]'s
+    softmax over the top-8 logits); `keep` prunes experts by giving them score
+    -inf before the softmax ([X] section 5), so their probability, count and
+    share of the load-balancing term are 0 and lse runs over the kept experts;
+    at least k experts must be kept;
   * RMSNorm of the stack uses weight 1 and eps 1e-5 and its output is rounded
     to bf16 (round to nearest even), the type the layer takes.
 
@@ -107,6 +114,19 @@ def top_k(logits, k):
     return ids, gap
 
 
+def mask_logits(logits, keep):
+    """Pruning ([X] section 5): experts outside `keep` (bool [E]) get score -inf
+    before the softmax, so the router can never choose them."""
+    keep = np.asarray(keep, dtype=bool)
+    return np.where(keep[None, :], logits, -np.inf)
+
+
+def renormalize_top_k(probs):
+    """The renormalised router ([X] section 2, Mixtral and Qwen3): the k chosen
+    softmax weights divided by their sum."""
+    return probs / probs.sum(axis=-1, keepdims=True)
+
+
 # -------------------------------------------------------------------- dispatch
 
 
@@ -165,19 +185,24 @@ def losses(probs, counts, lse, k, alpha=ALPHA, beta=BETA):
 
 
 def moe_layer_ref(x, w_router, w_gate, w_up, w_down, k=8, forced_ids=None,
-                  keep_y=False):
+                  keep_y=False, renormalize=False, keep=None):
     """One MoE layer, grouped by expert ([X] section 2 dispatch; [P] "Pretraining
     architecture"; [G] item 1 for the weighted sum).
 
     x [T,D] bf16 bits or float; w_router [E,D]; w_gate, w_up [E,F,D];
     w_down [E,D,F]. forced_ids [T,k] replaces the router's choice (used where
-    two routings are both correct within rounding).
+    two routings are both correct within rounding). renormalize / keep select
+    the router variants described in the module docstring.
     Returns a dict: out [T,D], ids, probs (route_probs [T,k]), p_all [T,E],
     logits, lse, gap, counts, offsets, perm, inv, aux, z (and y [Tk,D] if keep_y)."""
     x64 = to_f64(x)
     T, D = x64.shape
     E = np.asarray(w_router).shape[0]
     logits = router_logits(x64, w_router) if T else np.zeros((0, E))
+    if keep is not None:
+        if int(np.sum(np.asarray(keep, dtype=bool))) < k:
+            raise ValueError("fewer than k experts kept")
+        logits = mask_logits(logits, keep)
     if T:
         lse, p_all = softmax_all(logits)
     else:
@@ -187,7 +212,9 @@ def moe_layer_ref(x, w_router, w_gate, w_up, w_down, k=8, forced_ids=None,
     else:
         ids = np.asarray(forced_ids, dtype=np.int64).reshape(T, k)
         gap = np.full(T, np.nan)
-    probs = np.take_along_axis(p_all, ids, axis=-1)          # not renormalised
+    probs = np.take_along_axis(p_all, ids, axis=-1)          # not renormalised by default
+    if renormalize and T:
+        probs = renormalize_top_k(probs)
     counts, offsets, perm, inv = dispatch(ids, E)
     y = np.zeros((T * k, D))
     for e in range(E):

@@ -155,6 +155,52 @@ def test_router_variant_statistics_match_page(golden_dir):
     assert (ids_p == ids).all() and (ids_s == ids).all() == g["all_routers_choose_same_experts"]
 
 
+def test_renormalised_router_is_softmax_over_chosen_logits():
+    # the renormalised router ("Mixture-of-experts LLMs from scratch with OLMoE", section 2)
+    # equals a softmax over the k chosen logits (the OLMoE guide's item-1 formula)
+    L = inputs.host_layer(50, dims=(32, 16, 64), w_std=0.3)
+    a = oracle.moe_layer_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], 8)
+    b = oracle.moe_layer_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], 8,
+                             renormalize=True)
+    chosen = np.take_along_axis(a["logits"], a["ids"], -1)
+    ref = np.exp(chosen - chosen.max(-1, keepdims=True))
+    ref /= ref.sum(-1, keepdims=True)
+    np.testing.assert_allclose(b["probs"], ref, rtol=1e-13, atol=1e-16)
+    np.testing.assert_allclose(b["probs"].sum(-1), 1.0, rtol=1e-14)
+    # only the combine weights change: same experts, rows, losses; out rescaled per token
+    assert (a["ids"] == b["ids"]).all() and (a["perm"] == b["perm"]).all()
+    assert a["aux"] == b["aux"] and a["z"] == b["z"]
+    scale = 1.0 / a["probs"].sum(-1, keepdims=True)
+    np.testing.assert_allclose(b["out"], a["out"] * scale, rtol=1e-11, atol=1e-14)
+
+
+def test_keep_mask_equals_reduced_router():
+    # pruning ("... from scratch with OLMoE", section 5): experts outside the mask get score
+    # -inf before the softmax. Brute force: run the layer with only the kept experts' router
+    # rows and weights, then map the ids back.
+    rng = np.random.default_rng(5)
+    L = inputs.host_layer(40, dims=(32, 16, 64), w_std=0.3)
+    for n_keep in (64, 48, 16, 8):
+        keep = np.zeros(64, bool)
+        keep[rng.choice(64, n_keep, replace=False)] = True
+        kept = np.flatnonzero(keep)
+        a = oracle.moe_layer_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], 8,
+                                 keep=keep)
+        b = oracle.moe_layer_ref(L["x"], L["w_router"][kept], L["w_gate"][kept], L["w_up"][kept],
+                                 L["w_down"][kept], 8)
+        assert (a["ids"] == kept[b["ids"]]).all()
+        np.testing.assert_allclose(a["probs"], b["probs"], rtol=1e-13)
+        np.testing.assert_allclose(a["out"], b["out"], rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(a["lse"], b["lse"], rtol=1e-14)
+        assert a["z"] == pytest.approx(b["z"], rel=1e-13)
+        assert (a["counts"][~keep] == 0).all() and (a["p_all"][:, ~keep] == 0).all()
+        # the load-balancing term over 64 experts: E*sum f P with the pruned terms 0
+        assert a["aux"] == pytest.approx(b["aux"] * 64 / n_keep, rel=1e-13)
+    with pytest.raises(ValueError):
+        oracle.moe_layer_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], 8,
+                             keep=np.arange(64) < 7)
+
+
 # --------------------------------------------------------------------- dispatch
 
 
