@@ -47,7 +47,7 @@ extern "C" {
 #define OLMOE_API
 #endif
 
-#define OLMOE_ABI_VERSION 1
+#define OLMOE_ABI_VERSION 2
 
 #define OLMOE_D 2048 /* hidden size */
 #define OLMOE_F 1024 /* expert width (SwiGLU intermediate size) */
@@ -128,6 +128,29 @@ OLMOE_API olmoe_status_t olmoe_moe_forward(const void* x, const float* W_router,
                                  int32_t* route_ids, float* route_probs,
                                  int32_t* expert_counts, float* aux_loss, float* z_loss,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Router variants ("Mixture-of-experts LLMs from scratch with OLMoE"):
+ *   OLMOE_ROUTE_RENORMALIZE in route_flags: route_probs (and so the weights of
+ *     the sum) are the chosen probabilities divided by their sum over the 8
+ *     slots, the renormalised router of that page's section 2 (equal to a
+ *     softmax over the 8 chosen logits, the formula of "OLMoE Guide", item 1);
+ *   keep_mask: bit e clear prunes expert e, whose score becomes -inf before the
+ *     softmax (section 5 of that page), so it is never chosen, its probability
+ *     and count are 0, and lse (hence the z-loss) runs over the kept experts.
+ *     OLMOE_KEEP_ALL keeps every expert.
+ * The losses always use the (masked) 64-way softmax, not the renormalised
+ * weights.  Everything else is as olmoe_moe_forward, which equals
+ * olmoe_moe_forward_ex with route_flags 0 and OLMOE_KEEP_ALL.
+ * Errors: as olmoe_moe_forward, plus OLMOE_EINVAL for unknown route_flags bits
+ * or a keep_mask with fewer than 8 bits set. */
+#define OLMOE_ROUTE_RENORMALIZE 1u
+#define OLMOE_KEEP_ALL (~(uint64_t)0)
+OLMOE_API olmoe_status_t olmoe_moe_forward_ex(const void* x, const float* W_router, const void* W_gate,
+                                    const void* W_up, const void* W_down, int64_t T, void* out,
+                                    int32_t* route_ids, float* route_probs,
+                                    int32_t* expert_counts, float* aux_loss, float* z_loss,
+                                    uint32_t route_flags, uint64_t keep_mask,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* RMSNorm of the residual stream with unit weight, rounded to the layer's
  * input type: x_out[t] = bf16(h[t] / sqrt(mean_k h[t,k]^2 + eps)), computed in

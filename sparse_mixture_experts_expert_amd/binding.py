@@ -14,6 +14,8 @@ LIB_PATH = os.path.join(PKG, "libolmoe_moe.so")
 
 D, F, E, K = 2048, 1024, 64, 8
 OK, EINVAL, EWORKSPACE, EHIP, ENODEVICE = range(5)
+ROUTE_RENORMALIZE = 1
+KEEP_ALL = (1 << 64) - 1
 STATUS_NAMES = {0: "OLMOE_OK", 1: "OLMOE_EINVAL", 2: "OLMOE_EWORKSPACE", 3: "OLMOE_EHIP", 4: "OLMOE_ENODEVICE"}
 
 _lib = None
@@ -45,6 +47,9 @@ def lib() -> ctypes.CDLL:
     L.olmoe_moe_workspace_layout.argtypes = [i64, ctypes.POINTER(sz), ctypes.POINTER(sz), ctypes.POINTER(sz)]
     L.olmoe_moe_forward.restype = i32
     L.olmoe_moe_forward.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.olmoe_moe_forward_ex.restype = i32
+    L.olmoe_moe_forward_ex.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp,
+                                       ctypes.c_uint32, ctypes.c_uint64, vp, sz, vp]
     L.olmoe_rmsnorm_bf16.restype = i32
     L.olmoe_rmsnorm_bf16.argtypes = [vp, ctypes.c_float, i64, vp, vp]
     L.olmoe_residual_add.restype = i32
@@ -100,13 +105,31 @@ def make_workspace(T: int, device="cuda"):
     return torch.empty(max(workspace_bytes(T), 256), dtype=torch.uint8, device=device)
 
 
+def keep_mask_bits(keep) -> int:
+    """A keep mask as the ABI's 64-bit integer (bit e set: expert e may be chosen).
+    Accepts None (every expert), an int, a boolean array of 64 entries, or expert ids."""
+    import numpy as np
+    if keep is None:
+        return KEEP_ALL
+    if isinstance(keep, int):
+        return keep & KEEP_ALL
+    arr = np.asarray(keep.cpu() if hasattr(keep, "cpu") else keep)
+    if arr.dtype == bool:
+        if arr.shape != (E,):
+            raise ValueError(f"boolean keep mask must have {E} entries, got {arr.shape}")
+        arr = np.flatnonzero(arr)
+    return sum(1 << int(e) for e in set(arr.ravel().tolist()))
+
+
 def moe_forward(x, w_router, w_gate, w_up, w_down, *, out=None, route_ids=None, route_probs=None,
                 expert_counts=None, aux_loss=None, z_loss=None, workspace=None, stream=None,
-                want_routing=True):
-    """One MoE layer (olmoe_moe_forward).  Tensors are torch CUDA tensors:
-    x bf16 [T,2048], w_router fp32 [64,2048], w_gate / w_up bf16 [64,1024,2048],
-    w_down bf16 [64,2048,1024].  Missing outputs are allocated (routing outputs
-    only when want_routing).  Returns a dict of the output tensors."""
+                want_routing=True, renormalize=False, keep=None):
+    """One MoE layer (olmoe_moe_forward, or olmoe_moe_forward_ex for the router
+    variants: renormalize=True, keep = experts that may be chosen).  Tensors are
+    torch CUDA tensors: x bf16 [T,2048], w_router fp32 [64,2048], w_gate / w_up
+    bf16 [64,1024,2048], w_down bf16 [64,2048,1024].  Missing outputs are
+    allocated (routing outputs only when want_routing).  Returns a dict of the
+    output tensors."""
     import torch
     T = x.shape[0]
     dev = x.device
@@ -125,10 +148,17 @@ def moe_forward(x, w_router, w_gate, w_up, w_down, *, out=None, route_ids=None, 
         z_loss = z_loss if z_loss is not None else torch.empty(1, dtype=torch.float32, device=dev)
     if workspace is None:
         workspace = make_workspace(T, dev)
-    _check(lib().olmoe_moe_forward(
-        _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), int(T), _ptr(out),
-        _ptr(route_ids), _ptr(route_probs), _ptr(expert_counts), _ptr(aux_loss), _ptr(z_loss),
-        _ptr(workspace), workspace.numel(), _stream(stream)))
+    if renormalize or keep is not None:
+        _check(lib().olmoe_moe_forward_ex(
+            _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), int(T), _ptr(out),
+            _ptr(route_ids), _ptr(route_probs), _ptr(expert_counts), _ptr(aux_loss), _ptr(z_loss),
+            ROUTE_RENORMALIZE if renormalize else 0, keep_mask_bits(keep),
+            _ptr(workspace), workspace.numel(), _stream(stream)))
+    else:
+        _check(lib().olmoe_moe_forward(
+            _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), int(T), _ptr(out),
+            _ptr(route_ids), _ptr(route_probs), _ptr(expert_counts), _ptr(aux_loss), _ptr(z_loss),
+            _ptr(workspace), workspace.numel(), _stream(stream)))
     return {"out": out, "route_ids": route_ids, "route_probs": route_probs,
             "expert_counts": expert_counts, "aux_loss": aux_loss, "z_loss": z_loss,
             "workspace": workspace}

@@ -174,7 +174,23 @@ olmoe_status_t olmoe_moe_forward(const void* x, const float* W_router, const voi
                                  int32_t* route_ids, float* route_probs, int32_t* expert_counts,
                                  float* aux_loss, float* z_loss, void* workspace,
                                  size_t workspace_bytes, void* stream) {
+  return olmoe_moe_forward_ex(x, W_router, W_gate, W_up, W_down, T, out, route_ids, route_probs,
+                              expert_counts, aux_loss, z_loss, 0u, OLMOE_KEEP_ALL, workspace,
+                              workspace_bytes, stream);
+}
+
+olmoe_status_t olmoe_moe_forward_ex(const void* x, const float* W_router, const void* W_gate,
+                                    const void* W_up, const void* W_down, int64_t T, void* out,
+                                    int32_t* route_ids, float* route_probs, int32_t* expert_counts,
+                                    float* aux_loss, float* z_loss, uint32_t route_flags,
+                                    uint64_t keep_mask, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
   // ---- host-side checks; nothing is enqueued unless all pass
+  if (route_flags & ~static_cast<uint32_t>(OLMOE_ROUTE_RENORMALIZE))
+    return fail(OLMOE_EINVAL, "unknown route flags 0x%x", route_flags);
+  if (__builtin_popcountll(keep_mask) < OLMOE_K)
+    return fail(OLMOE_EINVAL, "keep_mask keeps %d experts, at least %d needed", __builtin_popcountll(keep_mask),
+                OLMOE_K);
   if (T < 0 || T > OLMOE_MAX_TOKENS)
     return fail(OLMOE_EINVAL, "T=%lld out of range [0, %lld]", (long long)T, (long long)OLMOE_MAX_TOKENS);
   if (!W_router || !W_gate || !W_up || !W_down)
@@ -215,7 +231,8 @@ olmoe_status_t olmoe_moe_forward(const void* x, const float* W_router, const voi
                 reinterpret_cast<uint16_t*>(ws + L.planes)};
   SelectArgs se{reinterpret_cast<const float2*>(ws + L.partial), Ti, ids, probs,
                 reinterpret_cast<uint8_t*>(ws + L.lrank), reinterpret_cast<int32_t*>(ws + L.blk_counts),
-                reinterpret_cast<float*>(ws + L.blk_psum), reinterpret_cast<float*>(ws + L.blk_lse2)};
+                reinterpret_cast<float*>(ws + L.blk_psum), reinterpret_cast<float*>(ws + L.blk_lse2),
+                keep_mask, (route_flags & OLMOE_ROUTE_RENORMALIZE) ? 1 : 0};
   ScanArgs sa{Ti,
               reinterpret_cast<const int32_t*>(ws + L.blk_counts),
               reinterpret_cast<const float*>(ws + L.blk_psum),

@@ -25,8 +25,10 @@ struct SelectArgs {
   int32_t* blk_counts;    // [nblk,64]
   float* blk_psum;        // [nblk,64]
   float* blk_lse2;        // [nblk]
+  uint64_t keep;          // bit e set: expert e may be chosen (at least 8 bits set)
+  int renormalize;        // nonzero: route_probs divided by their sum over the 8 slots
 };
-// softmax + top-8 per routing block (one launch, one wavefront per block)
+// softmax + top-8 per routing block (one launch, one workgroup per block)
 hipError_t launch_router_select(const SelectArgs& a, hipStream_t stream);
 
 constexpr int SMALL_TOKENS = 2048;   // up to here scan and permutation share one launch

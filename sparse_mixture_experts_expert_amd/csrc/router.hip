@@ -190,7 +190,7 @@ __global__ __launch_bounds__(64) void router_partial_bf16x3_kernel(const bf16_t*
 __global__ __launch_bounds__(256) void router_select_kernel(SelectArgs a) {
   __shared__ SelectLds L;
   select_block(a.partial, a.T, blockIdx.x, L, a.ids, a.probs, a.lrank, a.blk_counts, a.blk_psum,
-               a.blk_lse2);
+               a.blk_lse2, a.keep, a.renormalize);
 }
 
 }  // namespace

@@ -55,6 +55,11 @@ struct SelectLds {
 // scratch with OLMoE", section 2: softmax first, then the k largest, not
 // renormalised).
 //
+// Router variants: experts outside `keep` get score -inf before the softmax
+// (pruning, "... from scratch with OLMoE", section 5), and `renormalize`
+// divides the 8 chosen weights by their sum (the renormalised router of that
+// page's section 2).  The caller guarantees at least 8 kept experts.
+//
 // The logits are the fp64 sum of the four k-quarter (sum, compensation) pairs
 // left by the partial kernel.  Wavefront w holds tokens 4w..4w+3; lane
 // (r, j) = (lane / 16, lane % 16) holds token 4w + r's logits of experts
@@ -72,7 +77,8 @@ __device__ __forceinline__ void select_block(const float2* __restrict__ partial,
                                              float* __restrict__ probs, uint8_t* __restrict__ lrank,
                                              int32_t* __restrict__ blk_counts,
                                              float* __restrict__ blk_psum,
-                                             float* __restrict__ blk_lse2) {
+                                             float* __restrict__ blk_lse2, uint64_t keep,
+                                             int renormalize) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -94,7 +100,7 @@ __device__ __forceinline__ void select_block(const float2* __restrict__ partial,
       acc[3] += (double)b[2] + (double)b[3];
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (float)acc[i];
+    for (int i = 0; i < 4; ++i) v[i] = (keep >> (j * 4 + i)) & 1u ? (float)acc[i] : -INFINITY;
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = 0.f;
@@ -133,11 +139,21 @@ __device__ __forceinline__ void select_block(const float2* __restrict__ partial,
       my_slot[1] = i == 1 ? s : my_slot[1];
       my_slot[2] = i == 2 ? s : my_slot[2];
       my_slot[3] = i == 3 ? s : my_slot[3];
-      if (valid) {
-        ids[t * K + s] = be;
-        probs[t * K + s] = i == 0 ? p[0] : i == 1 ? p[1] : i == 2 ? p[2] : p[3];
-      }
+      if (valid) ids[t * K + s] = be;
     }
+  }
+  // weights of the chosen experts, optionally divided by their sum (fixed DPP order)
+  float wsc = 1.0f;
+  if (renormalize) {
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q += (taken >> i) & 1u ? p[i] : 0.f;
+    wsc = 1.0f / row16_sum(q);
+  }
+  if (valid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (my_slot[i] >= 0) probs[t * K + my_slot[i]] = renormalize ? p[i] * wsc : p[i];
   }
   L.chosen[rt][j] = valid ? static_cast<uint8_t>(taken) : 0;
 #pragma unroll

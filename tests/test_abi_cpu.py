@@ -1,6 +1,8 @@
 """The C ABI without a GPU: the library loads, exports every declared symbol,
 sizes its workspace, and rejects bad arguments before touching the device."""
 import ctypes
+
+import numpy as np
 import os
 import re
 
@@ -80,6 +82,25 @@ def test_forward_rejects_bad_arguments_before_any_device_call(L):
     assert _fwd(L, ws=(8 << 36) + 16)[0] == binding.EINVAL
     # out overlapping the workspace
     assert _fwd(L, out=(8 << 36) + 256)[0] == binding.EINVAL
+
+
+def test_router_variant_arguments_are_checked_first(L):
+    # every call here fails validation, so nothing reaches a device (fake pointers)
+    vp = ctypes.c_void_p
+    T = 16
+    wsb = binding.workspace_bytes(T)
+
+    def ex(flags, keep):
+        return L.olmoe_moe_forward_ex(vp(1 << 20), vp(2 << 20), vp(1 << 32), vp(2 << 32), vp(3 << 32), T,
+                                      vp(3 << 20), None, None, None, None, None, flags, keep,
+                                      vp(8 << 36), wsb, None)
+    assert ex(2, binding.KEEP_ALL) == binding.EINVAL
+    assert "route flags" in L.olmoe_last_error().decode()
+    assert ex(0, (1 << 7) - 1) == binding.EINVAL
+    assert "keep_mask" in L.olmoe_last_error().decode()
+    assert binding.keep_mask_bits(None) == binding.KEEP_ALL
+    assert binding.keep_mask_bits([0, 3, 63]) == 1 | 8 | (1 << 63)
+    assert binding.keep_mask_bits(np.arange(64) < 8) == 0xFF
 
 
 def test_glue_entry_points_reject_bad_arguments(L):

@@ -48,8 +48,8 @@ def host_of(r):
     return out
 
 
-def run_layer(x, w):
-    r = binding.moe_forward(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"])
+def run_layer(x, w, **variant):
+    r = binding.moe_forward(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], **variant)
     torch.cuda.synchronize()
     T = x.shape[0]
     tables = binding.dispatch_tables(r["workspace"], T)
@@ -59,13 +59,14 @@ def run_layer(x, w):
     return h
 
 
-def full_check(g, hw, label):
-    """Whole-oracle comparison for one call."""
-    ref = oracle.moe_layer_ref(g["x"], hw["w_router"], hw["w_gate"], hw["w_up"], hw["w_down"], 8)
-    ntie = parity.check_routing(g["route_ids"], g["route_probs"], ref, label)
+def full_check(g, hw, label, renormalize=False, keep=None):
+    """Whole-oracle comparison for one call (router variant as given)."""
+    var = dict(renormalize=renormalize, keep=keep)
+    ref = oracle.moe_layer_ref(g["x"], hw["w_router"], hw["w_gate"], hw["w_up"], hw["w_down"], 8, **var)
+    ntie = parity.check_routing(g["route_ids"], g["route_probs"], ref, label, renormalize=renormalize)
     if ntie or not np.array_equal(g["route_ids"], ref["ids"]):
         ref = oracle.moe_layer_ref(g["x"], hw["w_router"], hw["w_gate"], hw["w_up"], hw["w_down"], 8,
-                                   forced_ids=g["route_ids"])
+                                   forced_ids=g["route_ids"], **var)
     parity.check_dispatch(g["route_ids"], g["expert_counts"], g["perm"], g["inv"], g["offsets"], label=label)
     rel, mx = parity.check_out(oracle.to_f64(g["out"]), ref["out"], label)
     parity.check_losses(float(g["aux_loss"][0]), float(g["z_loss"][0]), ref["aux"], ref["z"], label)
@@ -88,6 +89,26 @@ def test_layer_matches_oracle_large_tile_plans(weights, T):
     _log(f"layer T={T}")
     x = inputs.device_x(T, seed=4, workload="parity")
     full_check(run_layer(x, w), hw, f"T={T}")
+
+
+@pytest.mark.parametrize("T,renorm,n_keep", [(1, True, 64), (100, True, 64), (300, False, 48),
+                                              (257, True, 16), (64, False, 8), (1500, True, 32)])
+def test_router_variants(weights, T, renorm, n_keep):
+    """Renormalised router and pruned experts ("Mixture-of-experts LLMs from scratch with
+    OLMoE", sections 2 and 5) against the oracle's variants."""
+    w, hw = weights
+    rng = np.random.default_rng(T * 131 + n_keep)
+    keep = np.zeros(64, bool)
+    keep[rng.choice(64, n_keep, replace=False)] = True
+    _log(f"variant T={T} renormalize={renorm} keep={n_keep}")
+    x = inputs.device_x(T, seed=6, workload="parity")
+    g = run_layer(x, w, renormalize=renorm, keep=None if n_keep == 64 else keep)
+    kp = None if n_keep == 64 else keep
+    full_check(g, hw, f"variant T={T} renorm={renorm} keep={n_keep}", renormalize=renorm, keep=kp)
+    if kp is not None:
+        assert (g["expert_counts"][~keep] == 0).all()
+    if renorm:
+        np.testing.assert_allclose(g["route_probs"].sum(1), 1.0, rtol=2e-6)
 
 
 def test_scaled_rows_and_large_logits(weights):
