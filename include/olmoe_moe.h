@@ -152,6 +152,27 @@ OLMOE_API olmoe_status_t olmoe_moe_forward_ex(const void* x, const float* W_rout
                                     uint32_t route_flags, uint64_t keep_mask,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* One layer of the residual stack with the residual update and the next
+ * layer's RMSNorm fused into the layer's last kernel ("Mixture-of-experts LLMs
+ * from scratch with OLMoE", section 3: the block adds the MoE output of
+ * RMSNorm(h) to the fp32 residual h):
+ *   h[t]      += sum_j w[t,j] * Y[t,j]   in fp32 (the layer output is not
+ *                rounded to bf16 on the way; h fp32 [T,2048], updated in place)
+ *   x_next[t]  = bf16(h[t] / sqrt(mean_k h[t,k]^2 + eps))   if x_next != NULL
+ * x is the layer's bf16 input (normally the previous call's x_next); x_next may
+ * be the same buffer as x.  Routing outputs, losses, route_flags, keep_mask and
+ * the workspace are as olmoe_moe_forward_ex.
+ * Errors: as olmoe_moe_forward_ex, plus OLMOE_EINVAL when h is NULL (T > 0),
+ * misaligned or overlapping an input or the workspace, when x_next overlaps h,
+ * the workspace or an input other than x, or when eps is not > 0 with x_next. */
+OLMOE_API olmoe_status_t olmoe_moe_forward_residual(const void* x, const float* W_router,
+                                          const void* W_gate, const void* W_up, const void* W_down,
+                                          int64_t T, float* h, void* x_next, float eps,
+                                          int32_t* route_ids, float* route_probs,
+                                          int32_t* expert_counts, float* aux_loss, float* z_loss,
+                                          uint32_t route_flags, uint64_t keep_mask,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* RMSNorm of the residual stream with unit weight, rounded to the layer's
  * input type: x_out[t] = bf16(h[t] / sqrt(mean_k h[t,k]^2 + eps)), computed in
  * fp32 ("Mixture-of-experts LLMs from scratch with OLMoE", section 3, RMSNorm;

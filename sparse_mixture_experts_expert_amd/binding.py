@@ -50,6 +50,9 @@ def lib() -> ctypes.CDLL:
     L.olmoe_moe_forward_ex.restype = i32
     L.olmoe_moe_forward_ex.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp,
                                        ctypes.c_uint32, ctypes.c_uint64, vp, sz, vp]
+    L.olmoe_moe_forward_residual.restype = i32
+    L.olmoe_moe_forward_residual.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, ctypes.c_float, vp, vp, vp, vp,
+                                             vp, ctypes.c_uint32, ctypes.c_uint64, vp, sz, vp]
     L.olmoe_rmsnorm_bf16.restype = i32
     L.olmoe_rmsnorm_bf16.argtypes = [vp, ctypes.c_float, i64, vp, vp]
     L.olmoe_residual_add.restype = i32
@@ -193,32 +196,70 @@ def residual_add(h, y, stream=None):
     return h
 
 
-def moe_stack_forward(h, layers, eps: float = 1e-5, keep_inputs: bool = False, workspace=None,
-                      stream=None):
+def moe_forward_residual(x, w_router, w_gate, w_up, w_down, h, *, x_next=None, eps: float = 1e-5,
+                         route_ids=None, route_probs=None, expert_counts=None, aux_loss=None,
+                         z_loss=None, workspace=None, stream=None, renormalize=False, keep=None):
+    """One layer of the residual stack with the fused epilogue
+    (olmoe_moe_forward_residual): h (fp32 [T,2048]) += the layer's output of x,
+    and x_next (bf16 [T,2048], may be x itself) = bf16(RMSNorm(h)) if given."""
+    import torch
+    T = x.shape[0]
+    _need(x, "x", torch.bfloat16, (T, D))
+    _need(h, "h", torch.float32, (T, D))
+    if x_next is not None:
+        _need(x_next, "x_next", torch.bfloat16, (T, D))
+    if workspace is None:
+        workspace = make_workspace(T, x.device)
+    _check(lib().olmoe_moe_forward_residual(
+        _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), int(T), _ptr(h), _ptr(x_next),
+        ctypes.c_float(eps), _ptr(route_ids), _ptr(route_probs), _ptr(expert_counts), _ptr(aux_loss),
+        _ptr(z_loss), ROUTE_RENORMALIZE if renormalize else 0, keep_mask_bits(keep),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return h
+
+
+def moe_stack_forward(h, layers, eps: float = 1e-5, keep_inputs: bool = False, keep_states: bool = False,
+                      workspace=None, stream=None, fused: bool = True):
     """Residual stack h <- h + MoE_l(RMSNorm(h)) over `layers` (dicts of weight
-    tensors), in place on the fp32 residual `h` [T,2048].  Returns h and, per
-    layer, expert counts / aux / z (and the bf16 layer inputs if keep_inputs)."""
+    tensors), in place on the fp32 residual `h` [T,2048].  fused: each layer's
+    combine also updates h and writes the next layer's input
+    (olmoe_moe_forward_residual); otherwise RMSNorm, layer and residual add run
+    as separate calls (the layer output then passes through bf16).  Returns h
+    and, per layer, expert counts / aux / z / route ids, plus the bf16 layer
+    inputs (keep_inputs) and h after each layer (keep_states)."""
     import torch
     T = h.shape[0]
     dev = h.device
     workspace = workspace if workspace is not None else make_workspace(T, dev)
     xbuf = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
-    ybuf = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    ybuf = None if fused else torch.empty((T, D), dtype=torch.bfloat16, device=dev)
     counts = torch.empty((len(layers), E), dtype=torch.int32, device=dev)
     aux = torch.empty(len(layers), dtype=torch.float32, device=dev)
     z = torch.empty(len(layers), dtype=torch.float32, device=dev)
     ids = torch.empty((len(layers), T, K), dtype=torch.int32, device=dev)
-    inputs = []
+    inputs, states = [], []
+    rmsnorm_bf16(h, eps, xbuf, stream)
     for l, w in enumerate(layers):
-        rmsnorm_bf16(h, eps, xbuf, stream)
         if keep_inputs:
             inputs.append(xbuf.clone())
-        moe_forward(xbuf, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], out=ybuf,
-                    route_ids=ids[l], route_probs=None, expert_counts=counts[l], aux_loss=aux[l:l + 1],
-                    z_loss=z[l:l + 1], workspace=workspace, stream=stream, want_routing=False)
-        residual_add(h, ybuf, stream)
+        last = l == len(layers) - 1
+        if fused:
+            moe_forward_residual(xbuf, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], h,
+                                 x_next=None if last else xbuf, eps=eps, route_ids=ids[l],
+                                 expert_counts=counts[l], aux_loss=aux[l:l + 1], z_loss=z[l:l + 1],
+                                 workspace=workspace, stream=stream)
+        else:
+            moe_forward(xbuf, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], out=ybuf,
+                        route_ids=ids[l], route_probs=None, expert_counts=counts[l],
+                        aux_loss=aux[l:l + 1], z_loss=z[l:l + 1], workspace=workspace, stream=stream,
+                        want_routing=False)
+            residual_add(h, ybuf, stream)
+            if not last:
+                rmsnorm_bf16(h, eps, xbuf, stream)
+        if keep_states:
+            states.append(h.clone())
     return {"h": h, "expert_counts": counts, "aux_loss": aux, "z_loss": z, "route_ids": ids,
-            "inputs": inputs}
+            "inputs": inputs, "states": states}
 
 
 TIMING_STAGES = ("router", "dispatch", "gateup", "down", "combine")

@@ -146,6 +146,12 @@ struct StageRecorder {
   }
 };
 
+olmoe_status_t forward_impl(const void* x, const float* W_router, const void* W_gate, const void* W_up,
+                            const void* W_down, int64_t T, void* out, float* hres, void* x_next, float eps,
+                            int32_t* route_ids, float* route_probs, int32_t* expert_counts, float* aux_loss,
+                            float* z_loss, uint32_t route_flags, uint64_t keep_mask, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -185,6 +191,34 @@ olmoe_status_t olmoe_moe_forward_ex(const void* x, const float* W_router, const 
                                     float* aux_loss, float* z_loss, uint32_t route_flags,
                                     uint64_t keep_mask, void* workspace, size_t workspace_bytes,
                                     void* stream) {
+  return forward_impl(x, W_router, W_gate, W_up, W_down, T, out, nullptr, nullptr, 0.f, route_ids,
+                      route_probs, expert_counts, aux_loss, z_loss, route_flags, keep_mask, workspace,
+                      workspace_bytes, stream);
+}
+
+olmoe_status_t olmoe_moe_forward_residual(const void* x, const float* W_router, const void* W_gate,
+                                          const void* W_up, const void* W_down, int64_t T, float* h,
+                                          void* x_next, float eps, int32_t* route_ids, float* route_probs,
+                                          int32_t* expert_counts, float* aux_loss, float* z_loss,
+                                          uint32_t route_flags, uint64_t keep_mask, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  if (T > 0 && !h) return fail(OLMOE_EINVAL, "h is NULL");
+  return forward_impl(x, W_router, W_gate, W_up, W_down, T, nullptr, h, x_next, eps, route_ids,
+                      route_probs, expert_counts, aux_loss, z_loss, route_flags, keep_mask, workspace,
+                      workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// the layer; out (bf16) for the plain forward, or h (+ x_next) for the residual epilogue
+olmoe_status_t forward_impl(const void* x, const float* W_router, const void* W_gate, const void* W_up,
+                            const void* W_down, int64_t T, void* out, float* hres, void* x_next, float eps,
+                            int32_t* route_ids, float* route_probs, int32_t* expert_counts, float* aux_loss,
+                            float* z_loss, uint32_t route_flags, uint64_t keep_mask, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  const bool residual = hres != nullptr;
   // ---- host-side checks; nothing is enqueued unless all pass
   if (route_flags & ~static_cast<uint32_t>(OLMOE_ROUTE_RENORMALIZE))
     return fail(OLMOE_EINVAL, "unknown route flags 0x%x", route_flags);
@@ -195,25 +229,37 @@ olmoe_status_t olmoe_moe_forward_ex(const void* x, const float* W_router, const 
     return fail(OLMOE_EINVAL, "T=%lld out of range [0, %lld]", (long long)T, (long long)OLMOE_MAX_TOKENS);
   if (!W_router || !W_gate || !W_up || !W_down)
     return fail(OLMOE_EINVAL, "a weight pointer is NULL");
-  if (T > 0 && (!x || !out)) return fail(OLMOE_EINVAL, "x or out is NULL");
-  const void* ptrs[] = {x, W_router, W_gate, W_up, W_down, out, route_ids, route_probs, expert_counts};
-  const char* names[] = {"x", "W_router", "W_gate", "W_up", "W_down", "out", "route_ids", "route_probs", "expert_counts"};
-  for (int i = 0; i < 9; ++i)
+  if (T > 0 && (!x || (!residual && !out))) return fail(OLMOE_EINVAL, "x or out is NULL");
+  const void* ptrs[] = {x, W_router, W_gate, W_up, W_down, out, route_ids, route_probs, expert_counts, hres, x_next};
+  const char* names[] = {"x", "W_router", "W_gate", "W_up", "W_down", "out", "route_ids", "route_probs",
+                         "expert_counts", "h", "x_next"};
+  for (int i = 0; i < 11; ++i)
     if (ptrs[i] && misaligned(ptrs[i])) return fail(OLMOE_EINVAL, "%s is not 16-byte aligned", names[i]);
   if ((aux_loss && misaligned(aux_loss, 4)) || (z_loss && misaligned(z_loss, 4)))
     return fail(OLMOE_EINVAL, "aux_loss / z_loss not 4-byte aligned");
+  if (residual && x_next && !(eps > 0.f)) return fail(OLMOE_EINVAL, "eps must be > 0");
   const size_t act = static_cast<size_t>(T) * OLMOE_D * 2;
   const size_t wexp = static_cast<size_t>(OLMOE_E) * OLMOE_F * OLMOE_D * 2;
-  if (overlaps(out, act, x, act) || overlaps(out, act, W_router, (size_t)OLMOE_E * OLMOE_D * 4) ||
-      overlaps(out, act, W_gate, wexp) || overlaps(out, act, W_up, wexp) || overlaps(out, act, W_down, wexp))
-    return fail(OLMOE_EINVAL, "out overlaps an input");
+  const size_t wr_bytes = (size_t)OLMOE_E * OLMOE_D * 4;
+  // a written buffer may not overlap an input (x_next may be x itself: x is last read before
+  // the epilogue runs, in stream order)
+  auto hits_inputs = [&](const void* p, size_t n, bool allow_x) {
+    return (!(allow_x && p == x) && overlaps(p, n, x, act)) || overlaps(p, n, W_router, wr_bytes) ||
+           overlaps(p, n, W_gate, wexp) || overlaps(p, n, W_up, wexp) || overlaps(p, n, W_down, wexp);
+  };
+  if (hits_inputs(out, act, false)) return fail(OLMOE_EINVAL, "out overlaps an input");
+  if (hits_inputs(hres, act * 2, false)) return fail(OLMOE_EINVAL, "h overlaps an input");
+  if (hits_inputs(x_next, act, true)) return fail(OLMOE_EINVAL, "x_next overlaps an input other than x");
+  if (overlaps(x_next, act, hres, act * 2)) return fail(OLMOE_EINVAL, "x_next overlaps h");
   const Layout L = make_layout(T);
   if (!workspace) return fail(OLMOE_EWORKSPACE, "workspace is NULL");
   if (misaligned(workspace, 256)) return fail(OLMOE_EINVAL, "workspace is not 256-byte aligned");
   if (workspace_bytes < L.total)
     return fail(OLMOE_EWORKSPACE, "workspace has %zu bytes, %zu needed for T=%lld", workspace_bytes, L.total,
                 (long long)T);
-  if (overlaps(out, act, workspace, L.total)) return fail(OLMOE_EINVAL, "out overlaps the workspace");
+  if (overlaps(out, act, workspace, L.total) || overlaps(hres, act * 2, workspace, L.total) ||
+      overlaps(x_next, act, workspace, L.total))
+    return fail(OLMOE_EINVAL, "an output overlaps the workspace");
   olmoe_status_t st = check_device();
   if (st != OLMOE_OK) return st;
 
@@ -280,13 +326,17 @@ olmoe_status_t olmoe_moe_forward_ex(const void* x, const float* W_router, const 
   he = launch_down(ga, plan, s);
   if (he != hipSuccess) return fail(OLMOE_EHIP, "down launch: %s", hipGetErrorString(he));
   rec.mark();
-  CombineArgs ca{Ti, reinterpret_cast<const uint16_t*>(ws + L.y), reinterpret_cast<const int32_t*>(ws + L.inv),
-                 probs, static_cast<uint16_t*>(out)};
+  CombineArgs ca{Ti,    reinterpret_cast<const uint16_t*>(ws + L.y), reinterpret_cast<const int32_t*>(ws + L.inv),
+                 probs, static_cast<uint16_t*>(out), hres, static_cast<uint16_t*>(x_next), eps};
   he = launch_combine(ca, s);
   if (he != hipSuccess) return fail(OLMOE_EHIP, "combine launch: %s", hipGetErrorString(he));
   rec.mark();
   return ok();
 }
+
+}  // namespace
+
+extern "C" {
 
 olmoe_status_t olmoe_rmsnorm_bf16(const float* h, float eps, int64_t T, void* x_out, void* stream) {
   if (T < 0 || T > OLMOE_MAX_TOKENS) return fail(OLMOE_EINVAL, "T=%lld out of range", (long long)T);

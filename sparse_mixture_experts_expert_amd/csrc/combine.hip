@@ -9,6 +9,10 @@
 //
 // rmsnorm / residual_add: the pre-norm residual block of the same page's
 // section 3, h <- h + MoE(RMSNorm(h)) with h kept in fp32 and unit norm weight.
+// The residual epilogue of combine fuses both into the layer: the fp32 sum goes
+// straight into h (no bf16 rounding of the layer output) and the wave that owns
+// the token's row then writes the next layer's input bf16(RMSNorm(h)), so the
+// stack reads and writes h once per layer.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -19,6 +23,7 @@ namespace {
 // one wavefront per token: 64 lanes x 32 columns (four 16-byte chunks per lane)
 constexpr int CMB_TOK_PER_WG = 4;
 
+template <bool RESIDUAL>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int t = blockIdx.x * CMB_TOK_PER_WG + (threadIdx.x >> 6);
   if (t >= a.T) return;
@@ -30,25 +35,54 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     pos[j] = a.inv[t * K + j];
     p[j] = a.probs[t * K + j];
   }
+  constexpr int NC = D / (64 * 8);   // 16-byte output chunks per lane
+  float acc[NC][8];
 #pragma unroll
-  for (int c = 0; c < D / (64 * 8); ++c) {
+  for (int c = 0; c < NC; ++c) {
     const int col = (c * 64 + lane) * 8;
-    float acc[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int i = 0; i < 8; ++i) acc[c][i] = 0.f;
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(a.y + (size_t)pos[j] * D + col);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = fmaf(p[j], f16_to_f32(static_cast<uint16_t>(v[i] & 0xFFFFu)), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(p[j], f16_to_f32(static_cast<uint16_t>(v[i] >> 16)), acc[2 * i + 1]);
+        acc[c][2 * i] = fmaf(p[j], f16_to_f32(static_cast<uint16_t>(v[i] & 0xFFFFu)), acc[c][2 * i]);
+        acc[c][2 * i + 1] = fmaf(p[j], f16_to_f32(static_cast<uint16_t>(v[i] >> 16)), acc[c][2 * i + 1]);
       }
     }
-    u32x4 o;
+    if constexpr (!RESIDUAL) {
+      u32x4 o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-    *reinterpret_cast<u32x4*>(a.out + (size_t)t * D + col) = o;
+      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[c][2 * i], acc[c][2 * i + 1]);
+      *reinterpret_cast<u32x4*>(a.out + (size_t)t * D + col) = o;
+    }
+  }
+  if constexpr (RESIDUAL) {
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float4* hp = reinterpret_cast<float4*>(a.h + (size_t)t * D + (c * 64 + lane) * 8);
+      float4 u = hp[0], w = hp[1];
+      u.x += acc[c][0]; u.y += acc[c][1]; u.z += acc[c][2]; u.w += acc[c][3];
+      w.x += acc[c][4]; w.y += acc[c][5]; w.z += acc[c][6]; w.w += acc[c][7];
+      hp[0] = u;
+      hp[1] = w;
+      acc[c][0] = u.x; acc[c][1] = u.y; acc[c][2] = u.z; acc[c][3] = u.w;
+      acc[c][4] = w.x; acc[c][5] = w.y; acc[c][6] = w.z; acc[c][7] = w.w;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf(acc[c][i], acc[c][i], ss);
+    }
+    if (a.x_next) {
+      const float r = 1.0f / sqrtf(wave_sum(ss) / D + a.eps);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[c][2 * i] * r, acc[c][2 * i + 1] * r);
+        *reinterpret_cast<u32x4*>(a.x_next + (size_t)t * D + (c * 64 + lane) * 8) = o;
+      }
+    }
   }
 }
 
@@ -98,8 +132,11 @@ __global__ __launch_bounds__(256) void residual_add_kernel(float* __restrict__ h
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3((a.T + CMB_TOK_PER_WG - 1) / CMB_TOK_PER_WG), dim3(256), 0,
-                     stream, a);
+  const dim3 grid((a.T + CMB_TOK_PER_WG - 1) / CMB_TOK_PER_WG);
+  if (a.h)
+    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -97,7 +97,10 @@ struct CombineArgs {
   const uint16_t* y;
   const int32_t* inv;
   const float* probs;
-  uint16_t* out;            // bf16 [T,2048]
+  uint16_t* out;            // bf16 [T,2048]; unused when h is set
+  float* h;                 // fp32 [T,2048] residual: h += layer output (fused residual epilogue)
+  uint16_t* x_next;         // bf16 [T,2048] RMSNorm(h) after the update, or null
+  float eps;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 

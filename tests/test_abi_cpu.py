@@ -103,6 +103,26 @@ def test_router_variant_arguments_are_checked_first(L):
     assert binding.keep_mask_bits(np.arange(64) < 8) == 0xFF
 
 
+def test_residual_entry_point_checks_arguments_first(L):
+    # every call here fails validation, so nothing reaches a device (fake pointers)
+    vp = ctypes.c_void_p
+    T = 16
+    wsb = binding.workspace_bytes(T)
+
+    def res(h, x_next, eps=1e-5, x=1 << 20):
+        return L.olmoe_moe_forward_residual(vp(x), vp(2 << 20), vp(1 << 32), vp(2 << 32), vp(3 << 32), T,
+                                            vp(h), vp(x_next), ctypes.c_float(eps), None, None, None, None,
+                                            None, 0, binding.KEEP_ALL, vp(8 << 36), wsb, None)
+    assert res(0, 0) == binding.EINVAL                      # h NULL
+    assert res((4 << 20) + 4, 0) == binding.EINVAL          # h misaligned
+    assert res((1 << 20) + 4096, 0) == binding.EINVAL       # h overlaps x
+    assert res(4 << 20, 5 << 20, eps=0.0) == binding.EINVAL  # eps with x_next
+    assert res(4 << 20, (4 << 20) + 4096) == binding.EINVAL  # x_next overlaps h
+    assert res(4 << 20, (1 << 20) + 16) == binding.EINVAL    # x_next partly over x
+    assert res(4 << 20, (8 << 36) + 512) == binding.EINVAL   # x_next in the workspace
+    assert "x_next" in L.olmoe_last_error().decode() or "workspace" in L.olmoe_last_error().decode()
+
+
 def test_glue_entry_points_reject_bad_arguments(L):
     vp = ctypes.c_void_p
     assert L.olmoe_rmsnorm_bf16(vp(1 << 20), ctypes.c_float(0.0), 4, vp(1 << 30), None) == binding.EINVAL

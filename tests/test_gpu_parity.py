@@ -200,7 +200,38 @@ def test_rmsnorm_and_residual_add():
     np.testing.assert_array_equal(h.cpu().numpy(), expect)
 
 
-def test_stack_teacher_forced_and_free_running():
+def test_fused_residual_epilogue(weights):
+    """olmoe_moe_forward_residual: h += layer output in fp32 and x_next = bf16(RMSNorm(h)),
+    x_next aliasing x (the stack's use)."""
+    w, hw = weights
+    T = 300
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12)
+    h = torch.randn((T, 2048), generator=g, device="cuda") * 2
+    x = binding.rmsnorm_bf16(h, 1e-5)
+    x_bits = parity.bf16_tensor_to_bits(x)
+    h_old = h.cpu().numpy().astype(np.float64)
+    ids = torch.empty((T, 8), dtype=torch.int32, device="cuda")
+    counts = torch.empty(64, dtype=torch.int32, device="cuda")
+    binding.moe_forward_residual(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], h, x_next=x,
+                                 eps=1e-5, route_ids=ids, expert_counts=counts)
+    torch.cuda.synchronize()
+    ids = ids.cpu().numpy()
+    ref = oracle.moe_layer_ref(x_bits, hw["w_router"], hw["w_gate"], hw["w_up"], hw["w_down"], 8,
+                               forced_ids=ids)
+    np.testing.assert_array_equal(counts.cpu().numpy(), ref["counts"])
+    h_new = h.cpu().numpy().astype(np.float64)
+    rel, mx = parity.check_out(h_new - h_old, ref["out"], "fused residual update")
+    # the next input is RMSNorm of the updated residual, within one bf16 unit of fp64
+    want = oracle.rmsnorm_bf16(h_new, 1e-5)
+    got = oracle.to_f64(parity.bf16_tensor_to_bits(x))
+    assert (np.abs(got - want) <= np.abs(want) * 2.0 ** -7 + 1e-30).all()
+    assert (got != want).mean() < 1e-3
+    _log(f"fused residual: relL2={rel:.2e} maxabs/rms={mx:.2e}")
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_stack_teacher_forced_and_free_running(fused):
     T, L = 64, 3
     layers = [inputs.device_weights(seed=10 + l, workload="stack-16x8192", layer=l) for l in range(L)]
     hw = [{k: (v.cpu().numpy() if v.dtype == torch.float32 else parity.bf16_tensor_to_bits(v))
@@ -209,23 +240,35 @@ def test_stack_teacher_forced_and_free_running():
     g.manual_seed(11)
     h0 = torch.randn((T, 2048), generator=g, device="cuda")
     h0_host = h0.cpu().numpy()
-    r = binding.moe_stack_forward(h0.clone(), layers, keep_inputs=True)
+    r = binding.moe_stack_forward(h0.clone(), layers, keep_inputs=True, keep_states=True, fused=fused)
     torch.cuda.synchronize()
     xs = [parity.bf16_tensor_to_bits(x) for x in r["inputs"]]
-    # teacher forcing: each layer judged on the GPU's own input
+    states = [h0_host.astype(np.float64)] + [st.cpu().numpy().astype(np.float64) for st in r["states"]]
+    # teacher forcing: each layer judged on the GPU's own input and its own residual update
     for l in range(L):
         ids = r["route_ids"][l].cpu().numpy()
         ref = oracle.moe_layer_ref(xs[l], hw[l]["w_router"], hw[l]["w_gate"], hw[l]["w_up"], hw[l]["w_down"], 8,
                                    forced_ids=ids)
         np.testing.assert_array_equal(r["expert_counts"][l].cpu().numpy(), ref["counts"])
         parity.check_losses(float(r["aux_loss"][l]), float(r["z_loss"][l]), ref["aux"], ref["z"], f"layer {l}")
-    # free running against the oracle's own stack
-    h_ref, _ = oracle.moe_stack_ref(h0_host, hw, k=8)
+        parity.check_out(states[l + 1] - states[l], ref["out"], f"layer {l} residual update")
+        if l + 1 < L:   # the next input is RMSNorm of this state
+            want = oracle.rmsnorm_bf16(states[l + 1], 1e-5)
+            got = oracle.to_f64(xs[l + 1])
+            assert (np.abs(got - want) <= np.abs(want) * 2.0 ** -7 + 1e-30).all()
+    # free running against the oracle's own stack.  A token whose top-8 flips at a near tie
+    # (either routing is correct) follows a different path from then on, so the update is
+    # judged on the tokens routed identically at every layer; the flipped ones must be few.
+    h_ref, per_ref = oracle.moe_stack_ref(h0_host, hw, k=8)
     hg = r["h"].cpu().numpy().astype(np.float64)
     rel = np.linalg.norm(hg - h_ref) / np.linalg.norm(h_ref)
-    upd = np.linalg.norm((hg - h0_host) - (h_ref - h0_host)) / np.linalg.norm(h_ref - h0_host)
-    _log(f"stack free-running rel L2 {rel:.2e}, update rel L2 {upd:.2e}")
-    assert rel <= 1e-2 and upd <= 3e-2
+    same = np.ones(T, bool)
+    for l in range(L):
+        same &= (np.sort(r["route_ids"][l].cpu().numpy(), 1) == np.sort(per_ref[l]["ids"], 1)).all(1)
+    du, dr = (hg - h0_host)[same], (h_ref - h0_host)[same]
+    upd = np.linalg.norm(du - dr) / np.linalg.norm(dr)
+    _log(f"stack free-running rel L2 {rel:.2e}, update rel L2 {upd:.2e} on {same.sum()}/{T} tokens")
+    assert rel <= 1e-2 and (~same).sum() <= max(2, T // 10) and upd <= 1e-2
 
 
 # ------------------------------------------------------------------ full sizes
