@@ -279,13 +279,14 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
 }
 
 // tile sets by batch size (rows per expert ~ T/8), chosen by measurement on MI355X.  Up to a
-// few hundred tokens the layer is bound by streaming the weights once; marking gate/up loads
-// non-temporal keeps them from displacing the token rows that every column tile re-reads.
-// Large batches use 8 waves (2 per SIMD) on 256-row tiles: more MFMA work per byte staged.
+// few hundred tokens the layer is bound by streaming the weights once; marking the weight loads
+// non-temporal keeps them from displacing the activation rows that every column tile re-reads.
+// 8 waves (2 per SIMD) keep more loads in flight per CU at small batches and give more MFMA
+// work per byte staged on the 256-row tiles of large batches.
 using GuTiny = Cfg<32, 64, 1, 2, true, 4, 64, 1, true>;
 using DnTiny = Cfg<32, 64, 1, 2, false, 4>;
-using GuSmall = Cfg<64, 64, 2, 2, true, 3, 64, 1, true>;
-using DnSmall = Cfg<64, 128, 2, 2, false, 3>;
+using GuSmall = Cfg<64, 128, 2, 4, true, 2, 64, 1, true>;
+using DnSmall = Cfg<64, 256, 2, 4, false, 2, 64, 1, true>;
 using GuMedium = Cfg<128, 128, 2, 2, true, 3, 64, 0>;
 using DnMedium = Cfg<128, 128, 2, 2, false, 2>;
 using GuLarge = Cfg<256, 128, 4, 2, true, 2, 64, 0>;
