@@ -59,7 +59,7 @@ Layout make_layout(int64_t T) {
   L.tiles_gu = take(max_tiles * 8);
   L.tiles_dn = take(max_tiles * 8);
   L.planes = take(3 * 64 * 2048 * 2);
-  L.partial = take(static_cast<size_t>(T) * 4 * 64 * 8);
+  L.partial = take(static_cast<size_t>(T) * router_slices(static_cast<int>(T)) * 64 * 8);
   L.ids = take(rows * 4);
   L.probs = take(rows * 4);
   L.lrank = take(rows);

@@ -10,10 +10,12 @@ struct RouterArgs {
   const uint16_t* x;      // bf16 [T,2048]
   const float* wr;        // fp32 [64,2048]
   int T;
-  float2* partial;        // [4,T,64] per-k-quarter (sum, compensation) of the logits (scratch)
+  float2* partial;        // [S,T,64] per-k-slice (sum, compensation) of the logits (scratch)
   uint16_t* planes;       // bf16 [3,64,2048] exact split of wr in fragment order (scratch, T > 2048)
 };
-// router logits in four k-quarter partials (one launch)
+// router logits in router_slices(T) k-slice partials
+constexpr int ROUTER_F32_TOKENS = 2048;   // up to here the fp32-MFMA router path
+constexpr int router_slices(int T) { return T <= ROUTER_F32_TOKENS ? 16 : 4; }
 hipError_t launch_router_partial(const RouterArgs& a, hipStream_t stream);
 
 struct SelectArgs {

@@ -4,12 +4,12 @@
 // from scratch with OLMoE", section 2), then softmax and top-8 (select_block in
 // routing.hpp).
 //
-// The logits are produced in four k-quarter partials, each a (sum,
-// compensation) pair whose fp64 sum the selection forms.
+// The logits are produced in k-slice partials (16 slices up to 2048 tokens, 4
+// above), each a (sum, compensation) pair whose fp64 sum the selection forms.
 //
 // Up to 2048 tokens: fp32 MFMA (16x16x4) straight from the fp32 router weights
-// and the bf16 tokens.  One wavefront per (16 tokens, 16 experts, k-quarter):
-// a workgroup reads only a 32 KiB slice of W_router, so the router spreads over
+// and the bf16 tokens.  One wavefront per (16 tokens, 16 experts, k-slice):
+// a workgroup reads only an 8 KiB slice of W_router, so the router spreads over
 // many CUs even for a handful of tokens (one workgroup pulling the whole router
 // through one CU would be bound by that CU's load bandwidth).  Each lane loads
 // 4 consecutive k of its row, and MFMA step s takes element s of every lane:
@@ -90,31 +90,42 @@ __device__ __forceinline__ void twosum_into(f32x4& tot, f32x4& cmp, const f32x4&
   }
 }
 
-// fp32 path: partial[kq][t][e] for 16 tokens, 16 experts, one k-quarter
+// fp32 path: partial[ks][t][e] for 16 tokens, 16 experts, one of KS k-slices.  Every load of
+// the slice is issued before the first MFMA: with one wavefront per workgroup and a handful of
+// workgroups per CU, a loop that waits on each load in turn is bound by memory latency.
+template <int KS>
 __global__ __launch_bounds__(64) void router_partial_f32_kernel(const bf16_t* __restrict__ x,
                                                                 const float* __restrict__ wr, int T,
                                                                 float2* __restrict__ partial) {
+  constexpr int KW = D / KS;                 // k per slice
+  constexpr int NB = KW / 16;                // 16-k blocks per slice
+  static_assert(KW % 64 == 0, "TwoSum chunks of 64 k");
   const int lane = threadIdx.x;
   const int g = blockIdx.y & 3;              // expert group of 16
-  const int kq = blockIdx.y >> 2;            // k-quarter
+  const int ks = blockIdx.y >> 2;            // k-slice
   const int tok0 = blockIdx.x * 16;
   const int row = tok0 + (lane & 15);
   const bool aok = row < T;
   // lane (n, q) = (lane % 16, lane / 16) loads k = kb + 4q .. kb + 4q + 3 of its rows
-  const float* bp = wr + (size_t)(g * 16 + (lane & 15)) * D + kq * KQ + (lane >> 4) * 4;
-  const bf16_t* ap = x + (size_t)(aok ? row : 0) * D + kq * KQ + (lane >> 4) * 4;
+  const float* bp = wr + (size_t)(g * 16 + (lane & 15)) * D + ks * KW + (lane >> 4) * 4;
+  const bf16_t* ap = x + (size_t)(aok ? row : 0) * D + ks * KW + (lane >> 4) * 4;
+  float4 b[NB];
+  uint2 av[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    b[i] = *reinterpret_cast<const float4*>(bp + i * 16);
+    av[i] = *reinterpret_cast<const uint2*>(ap + i * 16);
+  }
 
   f32x4 part = {0.f, 0.f, 0.f, 0.f}, tot = part, cmp = part;
-#pragma unroll 4
-  for (int kb = 0; kb < KQ; kb += 16) {
-    const float4 b = *reinterpret_cast<const float4*>(bp + kb);
-    uint2 av = *reinterpret_cast<const uint2*>(ap + kb);
-    if (!aok) av = make_uint2(0u, 0u);
-    part = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av.x << 16), b.x, part, 0, 0, 0);
-    part = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av.x & 0xFFFF0000u), b.y, part, 0, 0, 0);
-    part = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av.y << 16), b.z, part, 0, 0, 0);
-    part = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av.y & 0xFFFF0000u), b.w, part, 0, 0, 0);
-    if ((kb & 63) == 48) {   // every 64 k: fold the chunk partial in with TwoSum
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const uint2 a = aok ? av[i] : make_uint2(0u, 0u);
+    part = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x << 16), b[i].x, part, 0, 0, 0);
+    part = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x & 0xFFFF0000u), b[i].y, part, 0, 0, 0);
+    part = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y << 16), b[i].z, part, 0, 0, 0);
+    part = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y & 0xFFFF0000u), b[i].w, part, 0, 0, 0);
+    if ((i & 3) == 3) {   // every 64 k: fold the chunk partial in with TwoSum
       twosum_into(tot, cmp, part);
       part = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -123,7 +134,7 @@ __global__ __launch_bounds__(64) void router_partial_f32_kernel(const bf16_t* __
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = tok0 + (lane >> 4) * 4 + i;
-    if (t < T) partial[((size_t)kq * T + t) * E + g * 16 + (lane & 15)] = make_float2(tot[i], cmp[i]);
+    if (t < T) partial[((size_t)ks * T + t) * E + g * 16 + (lane & 15)] = make_float2(tot[i], cmp[i]);
   }
 }
 
@@ -187,21 +198,24 @@ __global__ __launch_bounds__(64) void router_partial_bf16x3_kernel(const bf16_t*
     }
 }
 
+template <int NS>
 __global__ __launch_bounds__(256) void router_select_kernel(SelectArgs a) {
   __shared__ SelectLds L;
-  select_block(a.partial, a.T, blockIdx.x, L, a.ids, a.probs, a.lrank, a.blk_counts, a.blk_psum,
-               a.blk_lse2, a.keep, a.renormalize);
+  select_block<NS>(a.partial, a.T, blockIdx.x, L, a.ids, a.probs, a.lrank, a.blk_counts, a.blk_psum,
+                   a.blk_lse2, a.keep, a.renormalize);
 }
 
 }  // namespace
 
 hipError_t launch_router_partial(const RouterArgs& a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
-  if (a.T <= 2048) {
-    hipLaunchKernelGGL(router_partial_f32_kernel, dim3((a.T + 15) / 16, 16), dim3(64), 0, stream, a.x, a.wr,
-                       a.T, a.partial);
+  if (a.T <= ROUTER_F32_TOKENS) {
+    static_assert(router_slices(ROUTER_F32_TOKENS) == 16, "slices of the fp32 path");
+    hipLaunchKernelGGL(router_partial_f32_kernel<16>, dim3((a.T + 15) / 16, 4 * 16), dim3(64), 0, stream, a.x,
+                       a.wr, a.T, a.partial);
     return hipGetLastError();
   }
+  static_assert(router_slices(ROUTER_F32_TOKENS + 1) == 4, "slices of the bf16x3 path");
   hipLaunchKernelGGL(router_prep_kernel, dim3(E * D / 8 / 256), dim3(256), 0, stream, a.wr, a.planes);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -214,7 +228,10 @@ hipError_t launch_router_partial(const RouterArgs& a, hipStream_t stream) {
 hipError_t launch_router_select(const SelectArgs& a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
   const int nblk = (a.T + ROUTE_BLOCK - 1) / ROUTE_BLOCK;
-  hipLaunchKernelGGL(router_select_kernel, dim3(nblk), dim3(256), 0, stream, a);
+  if (router_slices(a.T) == 16)
+    hipLaunchKernelGGL(router_select_kernel<16>, dim3(nblk), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(router_select_kernel<4>, dim3(nblk), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

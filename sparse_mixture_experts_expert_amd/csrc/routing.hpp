@@ -60,8 +60,8 @@ struct SelectLds {
 // divides the 8 chosen weights by their sum (the renormalised router of that
 // page's section 2).  The caller guarantees at least 8 kept experts.
 //
-// The logits are the fp64 sum of the four k-quarter (sum, compensation) pairs
-// left by the partial kernel.  Wavefront w holds tokens 4w..4w+3; lane
+// The logits are the fp64 sum of the NS k-slice (sum, compensation) pairs left
+// by the partial kernel.  Wavefront w holds tokens 4w..4w+3; lane
 // (r, j) = (lane / 16, lane % 16) holds token 4w + r's logits of experts
 // 4j..4j+3, so each of the 8 selection rounds is a 4-element register argmax
 // plus a 16-lane DPP all-reduce.  Ties: the lower expert id wins (ascending
@@ -72,6 +72,7 @@ struct SelectLds {
 // among the block's tokens of the same expert (for the stable dispatch); per
 // block: expert counts, probability sums and the sum of lse^2 (fixed token
 // order).  Called by all 256 threads of a workgroup (two barriers inside).
+template <int NS>
 __device__ __forceinline__ void select_block(const float2* __restrict__ partial, int T, int blk,
                                              SelectLds& L, int32_t* __restrict__ ids,
                                              float* __restrict__ probs, uint8_t* __restrict__ lrank,
@@ -91,7 +92,7 @@ __device__ __forceinline__ void select_block(const float2* __restrict__ partial,
   if (valid) {
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int kq = 0; kq < 4; ++kq) {
+    for (int kq = 0; kq < NS; ++kq) {
       const f32x4* src = reinterpret_cast<const f32x4*>(partial + ((size_t)kq * T + t) * E + j * 4);
       const f32x4 a = src[0], b = src[1];
       acc[0] += (double)a[0] + (double)a[1];

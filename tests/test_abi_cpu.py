@@ -46,7 +46,8 @@ def test_workspace_bytes_formula():
     for T in (1, 32, 256, 4096, 16384):
         w = binding.workspace_bytes(T)
         act = 8 * T * (1024 + 2048) * 2
-        assert act <= w <= act + 8 * T * 20 + T * 2048 + (T // 16 + 1) * 64 * 16 + 786432 + 64 * 1024
+        partial = T * (16 if T <= 2048 else 4) * 64 * 8     # router k-slice partials
+        assert act <= w <= act + 8 * T * 20 + partial + (T // 16 + 1) * 64 * 16 + 786432 + 64 * 1024
         lay = binding.workspace_layout(T)
         assert lay["offsets"] % 256 == 0 and lay["perm"] % 256 == 0 and lay["inv"] % 256 == 0
         assert lay["perm"] + 4 * 8 * T <= lay["inv"] <= w
