@@ -232,6 +232,76 @@ def moe_layer_ref(x, w_router, w_gate, w_up, w_down, k=8, forced_ids=None,
     return r
 
 
+# -------------------------------------------------------------------- backward
+
+
+def silu_grad(g):
+    """d/dg [g * sigma(g)] = sigma(g) * (1 + g * (1 - sigma(g)))."""
+    sig = 1.0 / (1.0 + np.exp(-g))
+    return sig * (1.0 + g * (1.0 - sig))
+
+
+def moe_layer_backward_ref(x, w_router, w_gate, w_up, w_down, dout, g_aux=0.0, g_z=0.0, k=8):
+    """Gradients of  L = sum_t <dout_t, out_t> + g_aux * aux + g_z * z  for one layer with the
+    default router (64-way softmax, top-k, not renormalised), by the chain rule through the
+    forward steps of moe_layer_ref ([G] items 1-3; [X] section 2). The routing choice and the
+    counts f_e are piecewise constant and carry no gradient.
+
+    Returns dict(dx [T,D], dw_router [E,D], dw_gate [E,F,D], dw_up [E,F,D], dw_down [E,D,F],
+    dw [T,k] (gradient of the routing weights), dlogits [T,E], fwd (the forward dict))."""
+    fwd = moe_layer_ref(x, w_router, w_gate, w_up, w_down, k, keep_y=True)
+    x64 = to_f64(x)
+    g = to_f64(dout)
+    T, D = x64.shape
+    wr = to_f64(w_router)
+    E = wr.shape[0]
+    F = np.asarray(w_gate).shape[1]
+    dx = np.zeros((T, D))
+    dw_gate = np.zeros((E, F, D))
+    dw_up = np.zeros((E, F, D))
+    dw_down = np.zeros((E, D, F))
+    dw = np.zeros((T, k))
+    perm, inv, offsets, probs = fwd["perm"], fwd["inv"], fwd["offsets"], fwd["probs"]
+    slot = np.zeros(T * k, dtype=np.int64)          # row -> slot j of its (token, slot) pair
+    for j in range(k):
+        slot[inv[:, j]] = j
+    for e in range(E):
+        a, b = offsets[e], offsets[e + 1]
+        if b == a:
+            continue
+        t = perm[a:b]
+        j = slot[a:b]
+        X = x64[t]
+        wg, wu, wd = to_f64(w_gate[e]), to_f64(w_up[e]), to_f64(w_down[e])
+        G = X @ wg.T
+        U = X @ wu.T
+        S = silu(G)
+        H = S * U
+        go = g[t]                                  # upstream gradient of each row's token
+        dw[t, j] = np.sum(go * fwd["y"][a:b], axis=1)   # out = sum_j w_j Y_j
+        dY = probs[t, j][:, None] * go
+        dw_down[e] = dY.T @ H                      # Y = H W_down^T
+        dH = dY @ wd
+        dG = dH * U * silu_grad(G)                 # H = silu(G) * U
+        dU = dH * S
+        dw_gate[e] = dG.T @ X                      # G = X W_gate^T, U = X W_up^T
+        dw_up[e] = dU.T @ X
+        np.add.at(dx, t, dG @ wg + dU @ wu)
+    # router: probabilities of the chosen experts, the load-balancing term and the z-loss
+    p = fwd["p_all"]
+    dp = np.zeros((T, E))
+    np.put_along_axis(dp, fwd["ids"], dw, axis=1)
+    if T:
+        f = fwd["counts"] / (k * T)
+        dp += g_aux * ALPHA * E * f[None, :] / T     # aux = alpha E sum_e f_e mean_t p_te
+    dlogits = p * (dp - np.sum(p * dp, axis=1, keepdims=True))     # softmax Jacobian
+    if T:
+        dlogits += g_z * BETA * (2.0 * fwd["lse"] / T)[:, None] * p   # z = beta mean_t lse_t^2
+    dx += dlogits @ wr
+    return dict(dx=dx, dw_router=dlogits.T @ x64, dw_gate=dw_gate, dw_up=dw_up, dw_down=dw_down,
+                dw=dw, dlogits=dlogits, fwd=fwd)
+
+
 # ----------------------------------------------------------------- brute force
 
 

@@ -364,3 +364,90 @@ def test_stack_with_zero_down_is_identity_and_one_layer_matches_layer():
     r = oracle.moe_layer_ref(xin, **{k: layers[0][k] for k in ("w_router", "w_gate", "w_up", "w_down")}, k=4)
     np.testing.assert_array_equal(h, h0 + r["out"])
     np.testing.assert_array_equal(per[0]["x_in"], oracle.bf16_bits(xin))
+
+
+# --------------------------------------------------------------------- backward
+
+
+def _small_layer(T, D, F, E, seed, w_std=0.3):
+    rng = np.random.default_rng(seed)
+    return dict(x=rng.standard_normal((T, D)), w_router=rng.standard_normal((E, D)) * w_std,
+                w_gate=rng.standard_normal((E, F, D)) * w_std, w_up=rng.standard_normal((E, F, D)) * w_std,
+                w_down=rng.standard_normal((E, D, F)) * w_std, dout=rng.standard_normal((T, D)))
+
+
+def _loss(L, k, g_aux, g_z, forced_ids=None, delta=None, eps=0.0):
+    P = {n: L[n] + (eps * delta[n] if delta is not None else 0.0)
+         for n in ("x", "w_router", "w_gate", "w_up", "w_down")}
+    r = oracle.moe_layer_ref(P["x"], P["w_router"], P["w_gate"], P["w_up"], P["w_down"], k,
+                             forced_ids=forced_ids)
+    return float(np.sum(L["dout"] * r["out"]) + g_aux * r["aux"] + g_z * r["z"])
+
+
+def test_silu_grad_matches_autograd():
+    g = torch.linspace(-12, 12, 1001, dtype=torch.float64, requires_grad=True)
+    torch.nn.functional.silu(g).sum().backward()
+    np.testing.assert_allclose(oracle.silu_grad(g.detach().numpy()), g.grad.numpy(), rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("g_aux,g_z", [(0.0, 0.0), (1.0, 1.0), (3.0, -2.0)])
+def test_backward_matches_dense_autograd(g_aux, g_z):
+    # an independent formulation: every expert on every token, masked by the chosen set, the
+    # losses written in torch, derivatives by autograd in float64
+    T, D, F, E, k = 20, 32, 16, 16, 4
+    L = _small_layer(T, D, F, E, seed=8)
+    b = oracle.moe_layer_backward_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], L["dout"],
+                                      g_aux, g_z, k)
+    tt = {n: torch.tensor(L[n], requires_grad=(n != "dout")) for n in L}
+    logits = tt["x"] @ tt["w_router"].T
+    p = torch.softmax(logits, -1)
+    lse = torch.logsumexp(logits, -1)
+    ids = torch.topk(logits.detach(), k, -1).indices
+    mask = torch.zeros(T, E, dtype=torch.float64).scatter_(1, ids, 1.0)
+    out = torch.zeros(T, D, dtype=torch.float64)
+    for e in range(E):
+        G = tt["x"] @ tt["w_gate"][e].T
+        U = tt["x"] @ tt["w_up"][e].T
+        out = out + (mask[:, e] * p[:, e])[:, None] * ((torch.nn.functional.silu(G) * U) @ tt["w_down"][e].T)
+    f = mask.sum(0) / (k * T)
+    aux = oracle.ALPHA * E * torch.sum(f * p.mean(0))
+    z = oracle.BETA * torch.mean(lse ** 2)
+    (torch.sum(tt["dout"] * out) + g_aux * aux + g_z * z).backward()
+    assert (np.sort(b["fwd"]["ids"], 1) == np.sort(ids.numpy(), 1)).all()   # same routing
+    for mine, name in (("dx", "x"), ("dw_router", "w_router"), ("dw_gate", "w_gate"), ("dw_up", "w_up"),
+                       ("dw_down", "w_down")):
+        np.testing.assert_allclose(b[mine], tt[name].grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=mine)
+
+
+def test_backward_directional_finite_differences():
+    # the loss with the routing held fixed is smooth: central differences along a random
+    # direction of every input agree with <gradient, direction>
+    T, D, F, E, k = 12, 16, 8, 8, 2
+    L = _small_layer(T, D, F, E, seed=9)
+    g_aux, g_z = 2.0, 5.0
+    b = oracle.moe_layer_backward_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], L["dout"],
+                                      g_aux, g_z, k)
+    ids = b["fwd"]["ids"]
+    rng = np.random.default_rng(10)
+    names = ("x", "w_router", "w_gate", "w_up", "w_down")
+    grads = dict(x=b["dx"], w_router=b["dw_router"], w_gate=b["dw_gate"], w_up=b["dw_up"], w_down=b["dw_down"])
+    for only in names + (None,):
+        V = {n: (rng.standard_normal(L[n].shape) if only in (None, n) else np.zeros(L[n].shape)) for n in names}
+        eps = 1e-5
+        fd = (_loss(L, k, g_aux, g_z, ids, V, eps) - _loss(L, k, g_aux, g_z, ids, V, -eps)) / (2 * eps)
+        an = sum(float(np.sum(grads[n] * V[n])) for n in names)
+        assert fd == pytest.approx(an, rel=1e-7, abs=1e-9), only
+
+
+def test_backward_zero_upstream_is_zero_and_unused_experts_get_none():
+    T, D, F, E, k = 6, 16, 8, 16, 2
+    L = _small_layer(T, D, F, E, seed=11)
+    b = oracle.moe_layer_backward_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"],
+                                      np.zeros((T, D)), 0.0, 0.0, k)
+    for n in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down"):
+        assert not np.any(b[n]), n
+    b = oracle.moe_layer_backward_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], L["dout"],
+                                      1.0, 1.0, k)
+    unused = b["fwd"]["counts"] == 0
+    assert unused.any()
+    assert not np.any(b["dw_gate"][unused]) and not np.any(b["dw_down"][unused])
