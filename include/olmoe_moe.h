@@ -47,7 +47,7 @@ extern "C" {
 #define OLMOE_API
 #endif
 
-#define OLMOE_ABI_VERSION 2
+#define OLMOE_ABI_VERSION 3
 
 #define OLMOE_D 2048 /* hidden size */
 #define OLMOE_F 1024 /* expert width (SwiGLU intermediate size) */
@@ -188,6 +188,41 @@ OLMOE_API olmoe_status_t olmoe_rmsnorm_bf16(const float* h, float eps, int64_t T
  * adds the MoE output to the fp32 residual stream).
  *   h  fp32 [T,2048] (updated in place);  y  bf16 [T,2048], must not overlap h. */
 OLMOE_API olmoe_status_t olmoe_residual_add(float* h, const void* y, int64_t T, void* stream);
+
+/* Backward pass of one layer with the default router (64-way softmax, top-8,
+ * not renormalised, every expert kept): the gradients of
+ *     L = sum_t <dout[t], out[t]> + g_aux * aux_loss + g_z * z_loss
+ * with respect to x and every weight, by the chain rule through the steps of
+ * olmoe_moe_forward ("OLMoE Guide", items 1-3; "Mixture-of-experts LLMs from
+ * scratch with OLMoE", section 2).  The routing choice and the routed shares
+ * f_e are piecewise constant and carry no gradient.  The forward is recomputed
+ * inside (no state is kept between calls): routing, G = x W_gate^T and
+ * U = x W_up^T of every routed row, and the expert outputs.
+ *
+ *   dout       bf16 [T,2048]          upstream gradient of out
+ *   g_aux, g_z                        upstream gradients of the two losses (finite)
+ *   dx         fp32 [T,2048]          written
+ *   dW_router  fp32 [64,2048]         written (not accumulated)
+ *   dW_gate    fp32 [64,1024,2048]    written; zero for experts no token chose
+ *   dW_up      fp32 [64,1024,2048]
+ *   dW_down    fp32 [64,2048,1024]
+ *   workspace  device buffer of olmoe_moe_backward_workspace_bytes(T) bytes,
+ *              256-byte aligned (about 290 KiB per token)
+ *
+ * Arithmetic: the gradient GEMMs run on bf16 MFMA with fp32 accumulation; their
+ * bf16 operands are the upstream gradient, the weights, the gathered inputs,
+ * dG / dU and w*H (rounded to nearest even); G and U are kept in fp32; the
+ * router gradient and the sums into dx run in fp32 in a fixed order.
+ * Errors: OLMOE_EINVAL for NULL / misaligned pointers, T out of range,
+ * non-finite g_aux / g_z, outputs overlapping an input, each other or the
+ * workspace; OLMOE_EWORKSPACE for a NULL or short workspace; OLMOE_ENODEVICE /
+ * OLMOE_EHIP as olmoe_moe_forward. */
+OLMOE_API size_t olmoe_moe_backward_workspace_bytes(int64_t T);
+OLMOE_API olmoe_status_t olmoe_moe_backward(const void* x, const float* W_router, const void* W_gate,
+                                  const void* W_up, const void* W_down, int64_t T, const void* dout,
+                                  float g_aux, float g_z, float* dx, float* dW_router, float* dW_gate,
+                                  float* dW_up, float* dW_down, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /* Per-stage timing of olmoe_moe_forward with HIP events recorded on the
  * caller's stream at the boundaries of its stages: 0 router (logits,

@@ -241,15 +241,20 @@ def silu_grad(g):
     return sig * (1.0 + g * (1.0 - sig))
 
 
-def moe_layer_backward_ref(x, w_router, w_gate, w_up, w_down, dout, g_aux=0.0, g_z=0.0, k=8):
+def moe_layer_backward_ref(x, w_router, w_gate, w_up, w_down, dout, g_aux=0.0, g_z=0.0, k=8,
+                           forced_ids=None, magnitudes=False):
     """Gradients of  L = sum_t <dout_t, out_t> + g_aux * aux + g_z * z  for one layer with the
     default router (64-way softmax, top-k, not renormalised), by the chain rule through the
     forward steps of moe_layer_ref ([G] items 1-3; [X] section 2). The routing choice and the
     counts f_e are piecewise constant and carry no gradient.
 
+    forced_ids fixes the routing as in moe_layer_ref (for near ties). magnitudes=True also
+    returns mag_gate / mag_up / mag_down / mag_dx: the same contractions over |operands|
+    (sums of |a| |b| over the terms of each element), which scale the rounding error any
+    evaluation of those gradients in a finite precision can make.
     Returns dict(dx [T,D], dw_router [E,D], dw_gate [E,F,D], dw_up [E,F,D], dw_down [E,D,F],
     dw [T,k] (gradient of the routing weights), dlogits [T,E], fwd (the forward dict))."""
-    fwd = moe_layer_ref(x, w_router, w_gate, w_up, w_down, k, keep_y=True)
+    fwd = moe_layer_ref(x, w_router, w_gate, w_up, w_down, k, keep_y=True, forced_ids=forced_ids)
     x64 = to_f64(x)
     g = to_f64(dout)
     T, D = x64.shape
@@ -261,6 +266,8 @@ def moe_layer_backward_ref(x, w_router, w_gate, w_up, w_down, dout, g_aux=0.0, g
     dw_up = np.zeros((E, F, D))
     dw_down = np.zeros((E, D, F))
     dw = np.zeros((T, k))
+    mags = dict(mag_gate=np.zeros((E, F, D)), mag_up=np.zeros((E, F, D)), mag_down=np.zeros((E, D, F)),
+                mag_dx=np.zeros((T, D))) if magnitudes else None
     perm, inv, offsets, probs = fwd["perm"], fwd["inv"], fwd["offsets"], fwd["probs"]
     slot = np.zeros(T * k, dtype=np.int64)          # row -> slot j of its (token, slot) pair
     for j in range(k):
@@ -287,6 +294,11 @@ def moe_layer_backward_ref(x, w_router, w_gate, w_up, w_down, dout, g_aux=0.0, g
         dw_gate[e] = dG.T @ X                      # G = X W_gate^T, U = X W_up^T
         dw_up[e] = dU.T @ X
         np.add.at(dx, t, dG @ wg + dU @ wu)
+        if magnitudes:
+            mags["mag_gate"][e] = np.abs(dG).T @ np.abs(X)
+            mags["mag_up"][e] = np.abs(dU).T @ np.abs(X)
+            mags["mag_down"][e] = np.abs(dY).T @ np.abs(H)
+            np.add.at(mags["mag_dx"], t, np.abs(dG) @ np.abs(wg) + np.abs(dU) @ np.abs(wu))
     # router: probabilities of the chosen experts, the load-balancing term and the z-loss
     p = fwd["p_all"]
     dp = np.zeros((T, E))
@@ -298,8 +310,12 @@ def moe_layer_backward_ref(x, w_router, w_gate, w_up, w_down, dout, g_aux=0.0, g
     if T:
         dlogits += g_z * BETA * (2.0 * fwd["lse"] / T)[:, None] * p   # z = beta mean_t lse_t^2
     dx += dlogits @ wr
-    return dict(dx=dx, dw_router=dlogits.T @ x64, dw_gate=dw_gate, dw_up=dw_up, dw_down=dw_down,
-                dw=dw, dlogits=dlogits, fwd=fwd)
+    r = dict(dx=dx, dw_router=dlogits.T @ x64, dw_gate=dw_gate, dw_up=dw_up, dw_down=dw_down,
+             dw=dw, dlogits=dlogits, fwd=fwd)
+    if magnitudes:
+        mags["mag_dx"] += np.abs(dlogits) @ np.abs(wr)
+        r.update(mags)
+    return r
 
 
 # ----------------------------------------------------------------- brute force

@@ -53,6 +53,11 @@ def lib() -> ctypes.CDLL:
     L.olmoe_moe_forward_residual.restype = i32
     L.olmoe_moe_forward_residual.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, ctypes.c_float, vp, vp, vp, vp,
                                              vp, ctypes.c_uint32, ctypes.c_uint64, vp, sz, vp]
+    L.olmoe_moe_backward_workspace_bytes.restype = sz
+    L.olmoe_moe_backward_workspace_bytes.argtypes = [i64]
+    L.olmoe_moe_backward.restype = i32
+    L.olmoe_moe_backward.argtypes = [vp, vp, vp, vp, vp, i64, vp, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp,
+                                     vp, vp, sz, vp]
     L.olmoe_rmsnorm_bf16.restype = i32
     L.olmoe_rmsnorm_bf16.argtypes = [vp, ctypes.c_float, i64, vp, vp]
     L.olmoe_residual_add.restype = i32
@@ -164,6 +169,41 @@ def moe_forward(x, w_router, w_gate, w_up, w_down, *, out=None, route_ids=None, 
             _ptr(workspace), workspace.numel(), _stream(stream)))
     return {"out": out, "route_ids": route_ids, "route_probs": route_probs,
             "expert_counts": expert_counts, "aux_loss": aux_loss, "z_loss": z_loss,
+            "workspace": workspace}
+
+
+def backward_workspace_bytes(T: int) -> int:
+    return int(lib().olmoe_moe_backward_workspace_bytes(int(T)))
+
+
+def moe_backward(x, w_router, w_gate, w_up, w_down, dout, *, g_aux: float = 1.0, g_z: float = 1.0,
+                 dx=None, dw_router=None, dw_gate=None, dw_up=None, dw_down=None, workspace=None,
+                 stream=None):
+    """Gradients of <dout, out> + g_aux * aux + g_z * z (olmoe_moe_backward) for the default
+    router.  dout bf16 [T,2048]; outputs (allocated when missing) are fp32: dx [T,2048],
+    dw_router [64,2048], dw_gate / dw_up [64,1024,2048], dw_down [64,2048,1024]."""
+    import torch
+    T = x.shape[0]
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, D))
+    _need(dout, "dout", torch.bfloat16, (T, D))
+    _need(w_router, "w_router", torch.float32, (E, D))
+    _need(w_gate, "w_gate", torch.bfloat16, (E, F, D))
+    _need(w_up, "w_up", torch.bfloat16, (E, F, D))
+    _need(w_down, "w_down", torch.bfloat16, (E, D, F))
+    f32 = torch.float32
+    dx = dx if dx is not None else torch.empty((T, D), dtype=f32, device=dev)
+    dw_router = dw_router if dw_router is not None else torch.empty((E, D), dtype=f32, device=dev)
+    dw_gate = dw_gate if dw_gate is not None else torch.empty((E, F, D), dtype=f32, device=dev)
+    dw_up = dw_up if dw_up is not None else torch.empty((E, F, D), dtype=f32, device=dev)
+    dw_down = dw_down if dw_down is not None else torch.empty((E, D, F), dtype=f32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(backward_workspace_bytes(T), 256), dtype=torch.uint8, device=dev)
+    _check(lib().olmoe_moe_backward(
+        _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), int(T), _ptr(dout),
+        ctypes.c_float(g_aux), ctypes.c_float(g_z), _ptr(dx), _ptr(dw_router), _ptr(dw_gate), _ptr(dw_up),
+        _ptr(dw_down), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return {"dx": dx, "dw_router": dw_router, "dw_gate": dw_gate, "dw_up": dw_up, "dw_down": dw_down,
             "workspace": workspace}
 
 

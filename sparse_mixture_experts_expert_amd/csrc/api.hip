@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <cmath>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -73,6 +74,39 @@ Layout make_layout(int64_t T) {
   L.y = take(rows * OLMOE_D * 2);
   L.total = off;
   return L;
+}
+
+// backward workspace: the forward's layout followed by the backward's own buffers
+struct BwdLayout {
+  Layout f;
+  size_t p_all, lse, row_w, gu, xg, dg, dgu, hw, dxr, dlogits, dwr_part, zero, tp_bwd, tiles_bwd, total;
+};
+BwdLayout make_bwd_layout(int64_t T) {
+  BwdLayout B{};
+  B.f = make_layout(T);
+  size_t off = B.f.total;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~size_t(255);
+    return o;
+  };
+  const size_t t = static_cast<size_t>(T), rows = 8 * t;
+  B.p_all = take(t * OLMOE_E * 4);
+  B.lse = take(t * 4);
+  B.row_w = take(rows * 4);
+  B.gu = take(rows * 2 * OLMOE_F * 4);
+  B.xg = take(rows * OLMOE_D * 2);
+  B.dg = take(rows * OLMOE_D * 2);
+  B.dgu = take(rows * 2 * OLMOE_F * 2);
+  B.hw = take(rows * OLMOE_F * 2);
+  B.dxr = take(rows * OLMOE_D * 4);
+  B.dlogits = take(t * OLMOE_E * 4);
+  B.dwr_part = take(static_cast<size_t>(bwd_router_splits(static_cast<int>(T))) * OLMOE_E * OLMOE_D * 4);
+  B.zero = take(4096);
+  B.tp_bwd = take(65 * 4);
+  B.tiles_bwd = take((static_cast<size_t>(max_row_tiles(static_cast<int>(T), MIN_TILE_ROWS)) + 8) * 8);
+  B.total = off;
+  return B;
 }
 
 bool misaligned(const void* p, size_t a = 16) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
@@ -337,6 +371,148 @@ olmoe_status_t forward_impl(const void* x, const float* W_router, const void* W_
 }  // namespace
 
 extern "C" {
+
+size_t olmoe_moe_backward_workspace_bytes(int64_t T) {
+  if (T < 0 || T > OLMOE_MAX_TOKENS) return 0;
+  return make_bwd_layout(T).total;
+}
+
+olmoe_status_t olmoe_moe_backward(const void* x, const float* W_router, const void* W_gate, const void* W_up,
+                                  const void* W_down, int64_t T, const void* dout, float g_aux, float g_z,
+                                  float* dx, float* dW_router, float* dW_gate, float* dW_up, float* dW_down,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  // ---- host-side checks; nothing is enqueued unless all pass
+  if (T < 0 || T > OLMOE_MAX_TOKENS)
+    return fail(OLMOE_EINVAL, "T=%lld out of range [0, %lld]", (long long)T, (long long)OLMOE_MAX_TOKENS);
+  if (!W_router || !W_gate || !W_up || !W_down) return fail(OLMOE_EINVAL, "a weight pointer is NULL");
+  if (!dW_router || !dW_gate || !dW_up || !dW_down) return fail(OLMOE_EINVAL, "a weight-gradient pointer is NULL");
+  if (T > 0 && (!x || !dout || !dx)) return fail(OLMOE_EINVAL, "x, dout or dx is NULL");
+  const void* ptrs[] = {x, W_router, W_gate, W_up, W_down, dout, dx, dW_router, dW_gate, dW_up, dW_down};
+  const char* names[] = {"x", "W_router", "W_gate", "W_up", "W_down", "dout", "dx", "dW_router", "dW_gate",
+                         "dW_up", "dW_down"};
+  for (int i = 0; i < 11; ++i)
+    if (ptrs[i] && misaligned(ptrs[i])) return fail(OLMOE_EINVAL, "%s is not 16-byte aligned", names[i]);
+  if (!std::isfinite(g_aux) || !std::isfinite(g_z)) return fail(OLMOE_EINVAL, "g_aux / g_z not finite");
+  const size_t act = static_cast<size_t>(T) * OLMOE_D * 2;
+  const size_t wexp = static_cast<size_t>(OLMOE_E) * OLMOE_F * OLMOE_D * 2;
+  const size_t wr_bytes = (size_t)OLMOE_E * OLMOE_D * 4;
+  const void* ins[] = {x, dout, W_router, W_gate, W_up, W_down};
+  const size_t in_n[] = {act, act, wr_bytes, wexp, wexp, wexp};
+  void* outs[] = {dx, dW_router, dW_gate, dW_up, dW_down};
+  const size_t out_n[] = {act * 2, wr_bytes, wexp * 2, wexp * 2, wexp * 2};
+  const BwdLayout B = make_bwd_layout(T);
+  if (!workspace) return fail(OLMOE_EWORKSPACE, "workspace is NULL");
+  if (misaligned(workspace, 256)) return fail(OLMOE_EINVAL, "workspace is not 256-byte aligned");
+  if (workspace_bytes < B.total)
+    return fail(OLMOE_EWORKSPACE, "workspace has %zu bytes, %zu needed for T=%lld", workspace_bytes, B.total,
+                (long long)T);
+  for (int o = 0; o < 5; ++o) {
+    for (int i = 0; i < 6; ++i)
+      if (overlaps(outs[o], out_n[o], ins[i], in_n[i])) return fail(OLMOE_EINVAL, "an output overlaps an input");
+    for (int q = o + 1; q < 5; ++q)
+      if (overlaps(outs[o], out_n[o], outs[q], out_n[q])) return fail(OLMOE_EINVAL, "two outputs overlap");
+    if (overlaps(outs[o], out_n[o], workspace, B.total)) return fail(OLMOE_EINVAL, "an output overlaps the workspace");
+  }
+  olmoe_status_t st = check_device();
+  if (st != OLMOE_OK) return st;
+
+  // ---- launches: recompute the forward (keeping p, lse, G, U, Y), then the gradients
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const Layout& L = B.f;
+  const int Ti = static_cast<int>(T);
+  const GemmPlan plan = plan_gemm(Ti);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
+  float* probs = reinterpret_cast<float*>(ws + L.probs);
+  RouterArgs ra{static_cast<const uint16_t*>(x), W_router, Ti, reinterpret_cast<float2*>(ws + L.partial),
+                reinterpret_cast<uint16_t*>(ws + L.planes)};
+  SelectArgs se{reinterpret_cast<const float2*>(ws + L.partial), Ti, ids, probs,
+                reinterpret_cast<uint8_t*>(ws + L.lrank), reinterpret_cast<int32_t*>(ws + L.blk_counts),
+                reinterpret_cast<float*>(ws + L.blk_psum), reinterpret_cast<float*>(ws + L.blk_lse2),
+                OLMOE_KEEP_ALL, 0, reinterpret_cast<float*>(ws + B.p_all), reinterpret_cast<float*>(ws + B.lse)};
+  ScanArgs sa{Ti,
+              reinterpret_cast<const int32_t*>(ws + L.blk_counts),
+              reinterpret_cast<const float*>(ws + L.blk_psum),
+              reinterpret_cast<const float*>(ws + L.blk_lse2),
+              reinterpret_cast<int32_t*>(ws + L.blk_base),
+              reinterpret_cast<int32_t*>(ws + L.offsets),
+              reinterpret_cast<int32_t*>(ws + L.tp_gu), reinterpret_cast<int2*>(ws + L.tiles_gu), plan.bm_gu,
+              reinterpret_cast<int32_t*>(ws + L.tp_dn), reinterpret_cast<int2*>(ws + L.tiles_dn), plan.bm_dn,
+              nullptr, nullptr, nullptr};
+  PermuteArgs pa{Ti, ids, reinterpret_cast<const uint8_t*>(ws + L.lrank),
+                 reinterpret_cast<const int32_t*>(ws + L.blk_base), reinterpret_cast<int32_t*>(ws + L.perm),
+                 reinterpret_cast<int32_t*>(ws + L.inv), probs, reinterpret_cast<float*>(ws + B.row_w)};
+  hipError_t he = launch_router_partial(ra, s);
+  if (he == hipSuccess) he = launch_router_select(se, s);
+  if (he == hipSuccess) {
+    if (Ti <= SMALL_TOKENS) {
+      he = launch_scan_permute(sa, pa, s);
+    } else {
+      he = launch_scan(sa, s);
+      if (he == hipSuccess) he = launch_permute(pa, s);
+    }
+  }
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "routing launch: %s", hipGetErrorString(he));
+  const int32_t* perm = reinterpret_cast<const int32_t*>(ws + L.perm);
+  const int32_t* offsets = reinterpret_cast<const int32_t*>(ws + L.offsets);
+  if (Ti > 0) {
+    GemmArgs ga{Ti,
+                static_cast<const uint16_t*>(x),
+                static_cast<const uint16_t*>(W_gate),
+                static_cast<const uint16_t*>(W_up),
+                static_cast<const uint16_t*>(W_down),
+                perm, offsets,
+                reinterpret_cast<const int32_t*>(ws + L.tp_gu),
+                reinterpret_cast<const int32_t*>(ws + L.tp_dn),
+                reinterpret_cast<const int2*>(ws + L.tiles_gu),
+                reinterpret_cast<const int2*>(ws + L.tiles_dn),
+                reinterpret_cast<uint16_t*>(ws + L.h),
+                reinterpret_cast<uint16_t*>(ws + L.y),
+                reinterpret_cast<float*>(ws + B.gu)};
+    he = launch_gateup(ga, plan, s);
+    if (he == hipSuccess) he = launch_down(ga, plan, s);
+    if (he != hipSuccess) return fail(OLMOE_EHIP, "forward GEMM launch: %s", hipGetErrorString(he));
+  }
+  BwdSmallArgs ba{Ti, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dout), W_router, ids,
+                  reinterpret_cast<const float*>(ws + B.p_all), reinterpret_cast<const float*>(ws + B.lse),
+                  offsets, perm, reinterpret_cast<const int32_t*>(ws + L.inv),
+                  reinterpret_cast<const uint16_t*>(ws + L.y), g_aux, g_z,
+                  reinterpret_cast<float*>(ws + B.dlogits), reinterpret_cast<uint16_t*>(ws + B.xg),
+                  reinterpret_cast<uint16_t*>(ws + B.dg), reinterpret_cast<const float*>(ws + B.dxr), dx,
+                  reinterpret_cast<float*>(ws + B.dwr_part), dW_router, reinterpret_cast<uint16_t*>(ws + B.zero),
+                  reinterpret_cast<int32_t*>(ws + B.tp_bwd), reinterpret_cast<int2*>(ws + B.tiles_bwd)};
+  he = launch_bwd_prepare(ba, s);
+  if (he == hipSuccess) he = launch_bwd_router(ba, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "backward routing launch: %s", hipGetErrorString(he));
+  const uint16_t* dgu = reinterpret_cast<const uint16_t*>(ws + B.dgu);
+  if (Ti > 0) {
+    BwdDgradArgs dh{reinterpret_cast<const uint16_t*>(ws + B.dg), nullptr, static_cast<const uint16_t*>(W_down),
+                    nullptr, OLMOE_F, (long)OLMOE_D * OLMOE_F, 2 * OLMOE_F,
+                    reinterpret_cast<const int32_t*>(ws + B.tp_bwd) + OLMOE_E,
+                    reinterpret_cast<const int2*>(ws + B.tiles_bwd),
+                    reinterpret_cast<const float*>(ws + B.row_w), reinterpret_cast<const float*>(ws + B.gu),
+                    reinterpret_cast<uint16_t*>(ws + B.dgu), reinterpret_cast<uint16_t*>(ws + B.hw), nullptr};
+    BwdDgradArgs dxa{dgu, nullptr, static_cast<const uint16_t*>(W_gate), static_cast<const uint16_t*>(W_up),
+                     OLMOE_D, (long)OLMOE_F * OLMOE_D, OLMOE_F,
+                     reinterpret_cast<const int32_t*>(ws + B.tp_bwd) + OLMOE_E,
+                     reinterpret_cast<const int2*>(ws + B.tiles_bwd), nullptr, nullptr, nullptr, nullptr,
+                     reinterpret_cast<float*>(ws + B.dxr)};
+    he = launch_dgrad(dh, Ti, true, s);
+    if (he == hipSuccess) he = launch_dgrad(dxa, Ti, false, s);
+    if (he != hipSuccess) return fail(OLMOE_EHIP, "dgrad launch: %s", hipGetErrorString(he));
+  }
+  BwdWgradArgs wd{reinterpret_cast<const uint16_t*>(ws + B.dg), OLMOE_D, reinterpret_cast<const uint16_t*>(ws + B.hw),
+                  OLMOE_F, offsets, reinterpret_cast<const uint16_t*>(ws + B.zero), OLMOE_D, OLMOE_F, dW_down, dW_down,
+                  OLMOE_D, (long)OLMOE_D * OLMOE_F};
+  BwdWgradArgs wgu{dgu, 2 * OLMOE_F, reinterpret_cast<const uint16_t*>(ws + B.xg), OLMOE_D, offsets,
+                   reinterpret_cast<const uint16_t*>(ws + B.zero), 2 * OLMOE_F, OLMOE_D, dW_gate, dW_up, OLMOE_F,
+                   (long)OLMOE_F * OLMOE_D};
+  he = launch_wgrad(wd, s);
+  if (he == hipSuccess) he = launch_wgrad(wgu, s);
+  if (he == hipSuccess) he = launch_bwd_finish(ba, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "weight-gradient launch: %s", hipGetErrorString(he));
+  return ok();
+}
 
 olmoe_status_t olmoe_rmsnorm_bf16(const float* h, float eps, int64_t T, void* x_out, void* stream) {
   if (T < 0 || T > OLMOE_MAX_TOKENS) return fail(OLMOE_EINVAL, "T=%lld out of range", (long long)T);

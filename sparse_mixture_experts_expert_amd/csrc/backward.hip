@@ -1,0 +1,195 @@
+// The non-GEMM steps of the backward pass of the OLMoE MoE layer.
+//
+// With out[t] = sum_j w[t,j] Y[t,j] and w[t,j] = p[t, e_j] (the 64-way softmax
+// probabilities, not renormalised: "Mixture-of-experts LLMs from scratch with
+// OLMoE", section 2), the loss L = <dout, out> + g_aux * aux + g_z * z has
+//   dL/dw[t,j]   = <dout[t], Y[t,j]>
+//   dL/dp[t,e]   = dL/dw for the chosen e, plus g_aux * 0.01 * 64 * f_e / T from the
+//                  load-balancing term (f_e, the routed share, is piecewise constant)
+//   dL/dl[t,e]   = p (dL/dp - <p, dL/dp>)  +  g_z * 0.001 * 2 lse_t / T * p
+// ("OLMoE Guide: 64-Expert Fine-Grained Open MoE Architecture", items 1-3), and
+// through the router's linear layer dx += dl W_router, dW_router = dl^T x.
+// Every sum runs in a fixed order (no atomics): results are reproducible.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "routing.hpp"
+
+namespace olmoe {
+
+namespace {
+
+constexpr int WR_SPLIT_TOKENS = 256;   // tokens per partial sum of dW_router
+
+// workgroup 0: zero row and the dgrad row-tile list; the others: x and dout rows in
+// expert order (one row per workgroup)
+__global__ __launch_bounds__(256) void bwd_prepare_kernel(BwdSmallArgs a, int bm) {
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0) {
+    __shared__ int off[E + 1], tp[E + 1];
+    reinterpret_cast<u32x4*>(a.zero)[tid] = u32x4{0u, 0u, 0u, 0u};   // 4 KiB
+    if (tid <= E) off[tid] = a.offsets[tid];
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0;
+      for (int e = 0; e < E; ++e) {
+        tp[e] = acc;
+        acc += (off[e + 1] - off[e] + bm - 1) / bm;
+      }
+      tp[E] = acc;
+    }
+    __syncthreads();
+    if (tid <= E) a.tp_bwd[tid] = tp[tid];
+    fill_tiles(tp, off, bm, a.tiles_bwd);
+    return;
+  }
+  const int r = blockIdx.x - 1;
+  const int t = a.perm[r];
+  const int c = tid * 8;
+  *reinterpret_cast<u32x4*>(a.xg + (size_t)r * D + c) = *reinterpret_cast<const u32x4*>(a.x + (size_t)t * D + c);
+  *reinterpret_cast<u32x4*>(a.dg + (size_t)r * D + c) = *reinterpret_cast<const u32x4*>(a.dout + (size_t)t * D + c);
+}
+
+// one wavefront per token: dL/dw for its 8 rows, then dL/dlogits with lane = expert
+__global__ __launch_bounds__(256) void bwd_router_kernel(BwdSmallArgs a) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int lane = threadIdx.x & 63;
+  constexpr int NC = D / (64 * 8);
+  float g[NC][8];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(a.dout + (size_t)t * D + (c * 64 + lane) * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      g[c][2 * i] = __uint_as_float(v[i] << 16);
+      g[c][2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+    }
+  }
+  float dw[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const uint16_t* yr = a.y + (size_t)a.inv[t * K + j] * D;
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(yr + (c * 64 + lane) * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s = fmaf(g[c][2 * i], f16_to_f32(static_cast<uint16_t>(v[i] & 0xFFFFu)), s);
+        s = fmaf(g[c][2 * i + 1], f16_to_f32(static_cast<uint16_t>(v[i] >> 16)), s);
+      }
+    }
+    dw[j] = wave_sum(s);
+  }
+  const float p = a.p_all[(size_t)t * E + lane];
+  const float cnt = static_cast<float>(a.offsets[lane + 1] - a.offsets[lane]);
+  const float Tf = static_cast<float>(a.T);
+  float dp = a.g_aux * static_cast<float>(LB_ALPHA * E) * (cnt / (K * Tf)) / Tf;
+#pragma unroll
+  for (int j = 0; j < K; ++j) dp += a.ids[t * K + j] == lane ? dw[j] : 0.f;
+  const float s = wave_sum(p * dp);
+  a.dlogits[(size_t)t * E + lane] =
+      p * (dp - s) + a.g_z * static_cast<float>(Z_BETA) * 2.0f * a.lse[t] / Tf * p;
+}
+
+// dW_router partial sums over WR_SPLIT_TOKENS tokens: thread (column, 16 experts)
+__global__ __launch_bounds__(256) void bwd_wrouter_partial_kernel(BwdSmallArgs a) {
+  const int col = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int e0 = (threadIdx.x >> 6) * 16;
+  const int t0 = blockIdx.y * WR_SPLIT_TOKENS;
+  const int t1 = min(a.T, t0 + WR_SPLIT_TOKENS);
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int t = t0; t < t1; ++t) {
+    const float xv = bf16_to_f32(a.x[(size_t)t * D + col]);
+    const float* dl = a.dlogits + (size_t)t * E + e0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = fmaf(dl[i], xv, acc[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a.dwr_part[((size_t)blockIdx.y * E + e0 + i) * D + col] = acc[i];
+}
+
+__global__ __launch_bounds__(256) void bwd_wrouter_reduce_kernel(BwdSmallArgs a, int nsplit) {
+  const int i = blockIdx.x * 256 + threadIdx.x;   // over 64 x 2048
+  float s = 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) s += a.dwr_part[(size_t)sp * E * D + i];
+  a.dw_router[i] = s;
+}
+
+// dx for 16 tokens per workgroup, 8 columns per thread: dl W_router, then the token's 8
+// per-row input gradients in slot order
+constexpr int DX_TOK = 16;
+__global__ __launch_bounds__(256) void bwd_dx_kernel(BwdSmallArgs a) {
+  __shared__ float sdl[DX_TOK][E];
+  const int t0 = blockIdx.x * DX_TOK;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < DX_TOK * E; i += 256) {
+    const int tk = i / E;
+    sdl[tk][i % E] = t0 + tk < a.T ? a.dlogits[(size_t)(t0 + tk) * E + i % E] : 0.f;
+  }
+  __syncthreads();
+  const int c0 = tid * 8;
+  float acc[DX_TOK][8];
+#pragma unroll
+  for (int tk = 0; tk < DX_TOK; ++tk)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[tk][i] = 0.f;
+  for (int e = 0; e < E; ++e) {
+    const float4 w0 = *reinterpret_cast<const float4*>(a.w_router + (size_t)e * D + c0);
+    const float4 w1 = *reinterpret_cast<const float4*>(a.w_router + (size_t)e * D + c0 + 4);
+    const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int tk = 0; tk < DX_TOK; ++tk) {
+      const float d = sdl[tk][e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[tk][i] = fmaf(d, w[i], acc[tk][i]);
+    }
+  }
+#pragma unroll
+  for (int tk = 0; tk < DX_TOK; ++tk) {
+    const int t = t0 + tk;
+    if (t >= a.T) break;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const float* row = a.dxr + (size_t)a.inv[t * K + j] * D + c0;
+      const float4 r0 = *reinterpret_cast<const float4*>(row);
+      const float4 r1 = *reinterpret_cast<const float4*>(row + 4);
+      acc[tk][0] += r0.x; acc[tk][1] += r0.y; acc[tk][2] += r0.z; acc[tk][3] += r0.w;
+      acc[tk][4] += r1.x; acc[tk][5] += r1.y; acc[tk][6] += r1.z; acc[tk][7] += r1.w;
+    }
+    float4* o = reinterpret_cast<float4*>(a.dx + (size_t)t * D + c0);
+    o[0] = make_float4(acc[tk][0], acc[tk][1], acc[tk][2], acc[tk][3]);
+    o[1] = make_float4(acc[tk][4], acc[tk][5], acc[tk][6], acc[tk][7]);
+  }
+}
+
+}  // namespace
+
+int bwd_router_splits(int T) { return (T + WR_SPLIT_TOKENS - 1) / WR_SPLIT_TOKENS; }
+
+hipError_t launch_bwd_prepare(const BwdSmallArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(bwd_prepare_kernel, dim3(1 + K * a.T), dim3(256), 0, stream, a, bwd_tile_rows());
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_router(const BwdSmallArgs& a, hipStream_t stream) {
+  if (a.T == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_router_kernel, dim3((a.T + 3) / 4), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_finish(const BwdSmallArgs& a, hipStream_t stream) {
+  const int ns = bwd_router_splits(a.T);
+  if (ns > 0) hipLaunchKernelGGL(bwd_wrouter_partial_kernel, dim3(D / 64, ns), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_wrouter_reduce_kernel, dim3(E * D / 256), dim3(256), 0, stream, a, ns);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.T == 0) return e;
+  hipLaunchKernelGGL(bwd_dx_kernel, dim3((a.T + DX_TOK - 1) / DX_TOK), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace olmoe

@@ -13,6 +13,9 @@ constexpr int F = OLMOE_F;  // expert width
 constexpr int E = OLMOE_E;  // experts
 constexpr int K = OLMOE_K;  // experts per token
 constexpr int ROUTE_BLOCK = 16;  // tokens per routing block (one wavefront's share in the router)
+// loss weights: load balancing ("OLMoE Guide", item 2) and router z-loss (item 3)
+constexpr double LB_ALPHA = 0.01;
+constexpr double Z_BETA = 0.001;
 
 typedef uint16_t bf16_t;  // storage type of bfloat16 values
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -62,8 +62,10 @@ __device__ __forceinline__ void vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int BM_, int BN_, int WM_, int WN_, bool GATEUP_, int STAGES_, int BK_ = 64, int ROT_ = 1, bool NTW_ = false>
+template <int BM_, int BN_, int WM_, int WN_, bool GATEUP_, int STAGES_, int BK_ = 64, int ROT_ = 1, bool NTW_ = false,
+          bool SAVE_GU_ = false>
 struct Cfg {
+  static constexpr bool SAVE_GU = SAVE_GU_;   // gate/up: also store the fp32 pre-activations G and U
   static constexpr int ROT = ROT_;   // rotate each work unit's starting k-step
   static constexpr bool NTW = NTW_;  // weight loads marked non-temporal (streamed once)
   static constexpr int BM = BM_;   // rows (tokens) per tile
@@ -109,7 +111,7 @@ template <class C>
 __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W0, const bf16_t* __restrict__ W1,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ tile_count, const int2* __restrict__ tiles,
-    int n_blocks, bf16_t* __restrict__ Cout) {
+    int n_blocks, bf16_t* __restrict__ Cout, float* __restrict__ gu) {
   constexpr int BK = C::BK;
   __shared__ __align__(16) bf16_t smem[C::STAGES][C::ROWS * BK];
 
@@ -274,6 +276,10 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
           if constexpr (C::GATEUP) o = silu(acc[0][i][j][v]) * acc[1][i][j][v];
           else o = acc[0][i][j][v];
           Cout[(size_t)(row0 + r) * C::ND + c] = f32_to_f16_sat(o);
+          if constexpr (C::SAVE_GU) {   // [rows, 2F]: G in columns 0..F-1, U in F..2F-1
+            gu[(size_t)(row0 + r) * (2 * F) + c] = acc[0][i][j][v];
+            gu[(size_t)(row0 + r) * (2 * F) + F + c] = acc[1][i][j][v];
+          }
         }
       }
 }
@@ -294,15 +300,20 @@ using DnLarge = Cfg<256, 256, 4, 2, false, 2, 64, 0>;
 
 template <class C>
 hipError_t launch_cfg(const bf16_t* A, const bf16_t* W0, const bf16_t* W1, const GemmArgs& a,
-                      const int32_t* tile_prefix, const int2* tiles, bf16_t* out, hipStream_t stream) {
+                      const int32_t* tile_prefix, const int2* tiles, bf16_t* out, hipStream_t stream,
+                      float* gu = nullptr) {
   const int max_tiles = max_row_tiles(a.T, C::BM);
   if (max_tiles == 0) return hipSuccess;
   const int n_blocks = C::ND / C::BN;
   const int grid = (max_tiles * n_blocks + 7) / 8 * 8;
   hipLaunchKernelGGL(grouped_gemm_kernel<C>, dim3(grid), dim3(C::NT), 0, stream, A, W0, W1, a.perm,
-                     tile_prefix + E, tiles, n_blocks, out);
+                     tile_prefix + E, tiles, n_blocks, out, gu);
   return hipGetLastError();
 }
+
+// the gate/up config C with the pre-activations saved (the backward pass recomputes them)
+template <class C>
+using SavingGU = Cfg<C::BM, C::BN, C::WM, C::WN, true, C::STAGES, C::BK, C::ROT, C::NTW, true>;
 
 }  // namespace
 
@@ -337,6 +348,14 @@ GemmPlan plan_gemm(int T) {
 }
 
 hipError_t launch_gateup(const GemmArgs& a, const GemmPlan& p, hipStream_t stream) {
+  if (a.gu) {
+    switch (p.variant) {
+      case 0: return launch_cfg<SavingGU<GuTiny>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
+      case 1: return launch_cfg<SavingGU<GuSmall>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
+      case 2: return launch_cfg<SavingGU<GuMedium>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
+      default: return launch_cfg<SavingGU<GuLarge>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
+    }
+  }
   switch (p.variant) {
     case 0: return launch_cfg<GuTiny>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
     case 1: return launch_cfg<GuSmall>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);

@@ -1,0 +1,377 @@
+// Grouped GEMMs of the backward pass of the OLMoE MoE layer on MFMA (gfx950).
+//
+// The expert network is (SiLU(X W_gate^T) * (X W_up^T)) W_down^T ("OLMoE Guide:
+// 64-Expert Fine-Grained Open MoE Architecture", item 1 and its SwiGLUExpert
+// module); its gradients contract over the other index of each product:
+//
+//   dgrad (rows of one expert x output columns, K fixed):
+//     dH~ = dOut_rows W_down[e]            A = upstream rows (gathered), B = W_down[e] as [d][f]
+//     dX  = dG W_gate[e] + dU W_up[e]      A = [dG | dU] rows, B = W_gate[e] / W_up[e] as [f][d]
+//   wgrad (one expert's weight tile, K = the expert's rows):
+//     dW_down[e]       = dOut_rows^T (w H)
+//     dW_gate/up[e]    = [dG | dU]^T X_rows
+//
+// The weights are read as stored, so the dgrad B operand and both wgrad operands
+// have the reduction index as their outer (row) index.  Such tiles are staged
+// in LDS as rows of k (LDS-DMA, 16-byte chunks XOR-swizzled by k & 3), and the
+// MFMA fragments are read with gfx950's transposing LDS read: within a group of
+// 16 lanes, lane p receives element p % 4 of the 8-byte pieces addressed by
+// lanes p/4, p/4 + 4, p/4 + 8 and p/4 + 12, so pointing lane j at
+// (k0 + j/4, n0 + 4 (j%4)) hands lane p column n0 + p at k0 .. k0+3.  Two such
+// reads give the 8 consecutive k of a 32x32x16 operand.  Row-major (K-inner)
+// A tiles use the forward kernel's layout and 16-byte reads.
+//
+// Pipelining, XCD remap and the per-workgroup choice of k-loop copy follow the
+// forward grouped GEMM.
+#include <type_traits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+#define GPTR(p) ((const __attribute__((address_space(1))) void*)(p))
+#define LPTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+namespace olmoe {
+
+namespace {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+template <int N>
+__device__ __forceinline__ void vm_barrier_b() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+template <int R, int IPS>
+__device__ __forceinline__ void wait_stage_b(int remaining) {
+  if constexpr (R == 0) {
+    vm_barrier_b<0>();
+  } else {
+    if (remaining >= R) vm_barrier_b<R * IPS>();
+    else wait_stage_b<R - 1, IPS>(remaining);
+  }
+}
+
+// element offset of (k, col) in a K-outer tile of BW columns; col % 4 == 0 inside a chunk
+template <int BW>
+__device__ __forceinline__ int kout_off(int k, int col) {
+  return k * BW + ((((col >> 3) ^ ((k & 3) << 1))) << 3) + (col & 7);
+}
+// element offset of chunk ch of row `row` in a K-inner tile of 64-element rows
+__device__ __forceinline__ int kin_off(int row, int ch) { return row * 64 + ((ch ^ (row & 7)) << 3); }
+
+// 32x32x16 operand of columns col0 .. col0+31 at k-step kk from a K-outer tile
+template <int BW>
+__device__ __forceinline__ bf16x8 frag_kout(const bf16_t* tile, int kk, int col0, int lane) {
+  const int krow = kk * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);
+  const int col = col0 + ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  typedef __attribute__((address_space(3))) v4i16 lds_v4;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(tile + kout_off<BW>(krow, col)));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(tile + kout_off<BW>(krow + 4, col)));
+  const u32x4 v = {__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                   __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ float sigmoidf(float g) { return 1.0f / (1.0f + __expf(-g)); }
+
+constexpr int BK = 64;   // reduction rows per stage
+
+// ----------------------------------------------------------------------------- dgrad
+
+enum { EPI_DH = 0, EPI_F32 = 1 };
+
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int EPI_>
+struct DCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_, EPI = EPI_;
+  static constexpr int NW = WM * WN, NT = NW * 64;
+  static constexpr int KD = 2 * F;                     // both dgrad products reduce over 2048
+  static constexpr int ND = EPI == EPI_DH ? F : D;     // output columns
+  static constexpr int KT = KD / BK;
+  static constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
+  static constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN;
+  static constexpr int IPA = A_ELEMS / 8 / NT;         // 16-byte loads per thread per stage
+  static constexpr int IPB = B_ELEMS / 8 / NT;
+  static constexpr int IPS = IPA + IPB;
+  static constexpr int CPB = BN / 8;                   // chunks per B row
+  static constexpr int RPB = 64 / CPB;                 // B rows per wave load
+  static_assert(FM >= 1 && FN >= 1 && IPA * NT * 8 == A_ELEMS && IPB * NT * 8 == B_ELEMS, "tiling");
+  static_assert(CPB >= 8 && BM % (8 * NW) == 0 && BK % (RPB * NW) == 0, "stage loading");
+  static_assert(STAGES >= 2 && IPS * (STAGES - 2) <= 63 && ND % BN == 0, "pipeline");
+};
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void dgrad_kernel(BwdDgradArgs a) {
+  __shared__ __align__(16) bf16_t smem[C::STAGES][C::A_ELEMS + C::B_ELEMS];
+
+  const int n_blocks = C::ND / C::BN;
+  const int nunits = *a.tile_count * n_blocks;
+  const int nper = (nunits + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  const int logical = (blockIdx.x & 7) * nper + slot;
+  if (slot >= nper || logical >= nunits) return;
+  const int tile = logical / n_blocks;
+  const int nt = logical - tile * n_blocks;
+  const int2 ti = a.tiles[tile];
+  const int e = ti.y & 255;
+  const int row0 = ti.x;
+  const int valid = ti.y >> 8;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv / C::WN, wn = wv % C::WN;
+  int nf = 0;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) nf += (i * C::WM + wm) * 32 < valid;
+
+  // A (K-inner rows): load j fills rows (j*NW + wv)*8 + lane/8, slot lane%8 <- chunk slot ^ (row & 7)
+  const bf16_t* ga[C::IPA];
+  const int dummy = a.a_rows ? a.a_rows[row0] : row0;
+#pragma unroll
+  for (int j = 0; j < C::IPA; ++j) {
+    const int r = (j * C::NW + wv) * 8 + (lane >> 3);
+    const int ch = (lane & 7) ^ (r & 7);
+    const int src = r < valid ? (a.a_rows ? a.a_rows[row0 + r] : row0 + r) : dummy;
+    ga[j] = a.a + (size_t)src * C::KD + ch * 8;
+  }
+  // B (K-outer weight rows): load j fills k-rows (j*NW + wv)*RPB + lane/CPB, slot lane%CPB
+  int gb[C::IPB];   // element offset inside a k-stage of the weight matrix
+#pragma unroll
+  for (int j = 0; j < C::IPB; ++j) {
+    const int k = (j * C::NW + wv) * C::RPB + lane / C::CPB;
+    const int ch = (lane % C::CPB) ^ ((k & 3) << 1);
+    gb[j] = k * a.ldb + nt * C::BN + ch * 8;
+  }
+  auto issue = [&](int kt, int sl, int j0, int j1) {
+    const int kg = kt * BK;
+    const bf16_t* bbase = (kg < a.kb_split ? a.b0 + (size_t)kg * a.ldb : a.b1 + (size_t)(kg - a.kb_split) * a.ldb) +
+                          (size_t)e * a.b_stride;
+#pragma unroll
+    for (int j = 0; j < C::IPS; ++j) {
+      if (j < j0 || j >= j1) continue;
+      if (j < C::IPA) {
+        __builtin_amdgcn_global_load_lds(GPTR(ga[j] + kg), LPTR(&smem[sl][(j * C::NW + wv) * 8 * 64]), 16, 0, 0);
+      } else {
+        const int jb = j - C::IPA;
+        __builtin_amdgcn_global_load_lds(GPTR(bbase + gb[jb]),
+                                         LPTR(&smem[sl][C::A_ELEMS + (jb * C::NW + wv) * C::RPB * C::BN]), 16, 0, 0);
+      }
+    }
+  };
+
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+#pragma unroll
+  for (int s = 0; s < C::STAGES - 1; ++s) issue(s, s, 0, C::IPS);
+  constexpr int NKK = BK / 16;
+  auto kloop = [&](auto nf_tag) __attribute__((always_inline)) {
+    constexpr int NF = decltype(nf_tag)::value;
+    for (int kt = 0; kt < C::KT; ++kt) {
+      wait_stage_b<C::STAGES - 2, C::IPS>(min(C::STAGES - 2, C::KT - 1 - kt));
+      const bool more = kt + C::STAGES - 1 < C::KT;
+      const int next_slot = (kt + C::STAGES - 1) % C::STAGES;
+      const bf16_t* As = smem[kt % C::STAGES];
+      const bf16_t* Bs = As + C::A_ELEMS;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        if (more) issue(kt + C::STAGES - 1, next_slot, kk * C::IPS / NKK, (kk + 1) * C::IPS / NKK);
+        if constexpr (NF > 0) {
+          bf16x8 af[NF], bfr[C::FN];
+          const int kc = kk * 2 + (lane >> 5);
+#pragma unroll
+          for (int i = 0; i < NF; ++i)
+            af[i] = *reinterpret_cast<const bf16x8*>(&As[kin_off((i * C::WM + wm) * 32 + (lane & 31), kc)]);
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) bfr[j] = frag_kout<C::BN>(Bs, kk, wn * (C::BN / C::WN) + j * 32, lane);
+#pragma unroll
+          for (int i = 0; i < NF; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  };
+  if (nf >= C::FM) kloop(std::integral_constant<int, C::FM>{});
+  else if (C::FM > 1 && nf == 1) kloop(std::integral_constant<int, (C::FM > 1 ? 1 : 0)>{});
+  else if (C::FM > 2 && nf == 2) kloop(std::integral_constant<int, (C::FM > 2 ? 2 : 0)>{});
+  else if (C::FM > 3 && nf == 3) kloop(std::integral_constant<int, (C::FM > 3 ? 3 : 0)>{});
+  else kloop(std::integral_constant<int, 0>{});
+
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = (i * C::WM + wm) * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        const int c = nt * C::BN + wn * (C::BN / C::WN) + j * 32 + (lane & 31);
+        if (r >= valid) continue;
+        const size_t row = (size_t)(row0 + r);
+        if constexpr (C::EPI == EPI_DH) {
+          // dH = w dH~; H = SiLU(G) U, so dG = dH U SiLU'(G), dU = dH SiLU(G)
+          const float w = a.row_w[row];
+          const float g = a.gu[row * (2 * F) + c], u = a.gu[row * (2 * F) + F + c];
+          const float sg = sigmoidf(g);
+          const float s = g * sg;
+          const float dh = w * acc[i][j][v];
+          a.dgu[row * (2 * F) + c] = f32_to_bf16(dh * u * (sg * (1.0f + g * (1.0f - sg))));
+          a.dgu[row * (2 * F) + F + c] = f32_to_bf16(dh * s);
+          a.hw[row * F + c] = f32_to_bf16(w * s * u);
+        } else {
+          a.out_f32[row * D + c] = acc[i][j][v];
+        }
+      }
+}
+
+// ----------------------------------------------------------------------------- wgrad
+
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
+struct WCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
+  static constexpr int NW = WM * WN, NT = NW * 64;
+  static constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
+  static constexpr int A_ELEMS = BK * BM, B_ELEMS = BK * BN;
+  static constexpr int IPA = A_ELEMS / 8 / NT, IPB = B_ELEMS / 8 / NT, IPS = IPA + IPB;
+  static constexpr int CPA = BM / 8, RPA = 64 / CPA, CPB = BN / 8, RPB = 64 / CPB;
+  static_assert(FM >= 1 && FN >= 1 && IPA * NT * 8 == A_ELEMS && IPB * NT * 8 == B_ELEMS, "tiling");
+  static_assert(CPA >= 8 && CPB >= 8 && BK % (RPA * NW) == 0 && BK % (RPB * NW) == 0, "stage loading");
+  static_assert(STAGES >= 2 && IPS * (STAGES - 2) <= 63, "pipeline");
+};
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void wgrad_kernel(BwdWgradArgs a) {
+  __shared__ __align__(16) bf16_t smem[C::STAGES][C::A_ELEMS + C::B_ELEMS];
+
+  const int mtiles = a.m_total / C::BM, ntiles = a.n_total / C::BN;
+  const int nunits = E * mtiles * ntiles;
+  const int nper = (nunits + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  const int logical = (blockIdx.x & 7) * nper + slot;
+  if (slot >= nper || logical >= nunits) return;
+  const int e = logical / (mtiles * ntiles);
+  const int rem = logical - e * mtiles * ntiles;
+  const int mt = rem / ntiles, nt = rem - mt * ntiles;
+  const int r0 = a.offsets[e];
+  const int rows = a.offsets[e + 1] - r0;
+  const int KT = (rows + BK - 1) / BK;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv / C::WN, wn = wv % C::WN;
+
+  // both operands K-outer: load j fills k-rows (j*NW + wv)*RP + lane/CP, slot lane%CP
+  int ka[C::IPA], oa[C::IPA], kb[C::IPB], ob[C::IPB];
+#pragma unroll
+  for (int j = 0; j < C::IPA; ++j) {
+    ka[j] = (j * C::NW + wv) * C::RPA + lane / C::CPA;
+    oa[j] = mt * C::BM + (((lane % C::CPA) ^ ((ka[j] & 3) << 1)) << 3);
+  }
+#pragma unroll
+  for (int j = 0; j < C::IPB; ++j) {
+    kb[j] = (j * C::NW + wv) * C::RPB + lane / C::CPB;
+    ob[j] = nt * C::BN + (((lane % C::CPB) ^ ((kb[j] & 3) << 1)) << 3);
+  }
+  auto issue = [&](int kt, int sl, int j0, int j1) {
+#pragma unroll
+    for (int j = 0; j < C::IPS; ++j) {
+      if (j < j0 || j >= j1) continue;
+      if (j < C::IPA) {
+        const int k = kt * BK + ka[j];   // rows past the expert's count read zeros
+        const bf16_t* src = k < rows ? a.a + (size_t)(r0 + k) * a.lda + oa[j] : a.zero + (oa[j] - mt * C::BM);
+        __builtin_amdgcn_global_load_lds(GPTR(src), LPTR(&smem[sl][(j * C::NW + wv) * C::RPA * C::BM]), 16, 0, 0);
+      } else {
+        const int jb = j - C::IPA;
+        const int k = kt * BK + kb[jb];
+        const bf16_t* src = k < rows ? a.b + (size_t)(r0 + k) * a.ldb + ob[jb] : a.zero + (ob[jb] - nt * C::BN);
+        __builtin_amdgcn_global_load_lds(GPTR(src),
+                                         LPTR(&smem[sl][C::A_ELEMS + (jb * C::NW + wv) * C::RPB * C::BN]), 16, 0, 0);
+      }
+    }
+  };
+
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+#pragma unroll
+  for (int s = 0; s < C::STAGES - 1; ++s)
+    if (s < KT) issue(s, s, 0, C::IPS);
+  constexpr int NKK = BK / 16;
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_stage_b<C::STAGES - 2, C::IPS>(min(C::STAGES - 2, KT - 1 - kt));
+    const bool more = kt + C::STAGES - 1 < KT;
+    const int next_slot = (kt + C::STAGES - 1) % C::STAGES;
+    const bf16_t* As = smem[kt % C::STAGES];
+    const bf16_t* Bs = As + C::A_ELEMS;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      if (more) issue(kt + C::STAGES - 1, next_slot, kk * C::IPS / NKK, (kk + 1) * C::IPS / NKK);
+      bf16x8 af[C::FM], bfr[C::FN];
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) af[i] = frag_kout<C::BM>(As, kk, wm * (C::BM / C::WM) + i * 32, lane);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) bfr[j] = frag_kout<C::BN>(Bs, kk, wn * (C::BN / C::WN) + j * 32, lane);
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // output row m (of m_total) goes to out0 below m_split, out1 above
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = mt * C::BM + wm * (C::BM / C::WM) + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        const int n = nt * C::BN + wn * (C::BN / C::WN) + j * 32 + (lane & 31);
+        float* o = m < a.m_split ? a.out0 + (size_t)e * a.out_stride + (size_t)m * a.n_total
+                                 : a.out1 + (size_t)e * a.out_stride + (size_t)(m - a.m_split) * a.n_total;
+        o[n] = acc[i][j][v];
+      }
+}
+
+using DgDH = DCfg<128, 128, 2, 2, 3, EPI_DH>;
+using DgDX = DCfg<128, 128, 2, 2, 3, EPI_F32>;
+using WgCfg = WCfg<128, 128, 2, 2, 3>;
+
+}  // namespace
+
+int bwd_tile_rows() { return DgDH::BM; }
+
+hipError_t launch_dgrad(const BwdDgradArgs& a, int T, bool dh, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int max_tiles = max_row_tiles(T, DgDH::BM);
+  if (dh) {
+    const int grid = (max_tiles * (DgDH::ND / DgDH::BN) + 7) / 8 * 8;
+    hipLaunchKernelGGL(dgrad_kernel<DgDH>, dim3(grid), dim3(DgDH::NT), 0, stream, a);
+  } else {
+    const int grid = (max_tiles * (DgDX::ND / DgDX::BN) + 7) / 8 * 8;
+    hipLaunchKernelGGL(dgrad_kernel<DgDX>, dim3(grid), dim3(DgDX::NT), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad(const BwdWgradArgs& a, hipStream_t stream) {
+  const int units = E * (a.m_total / WgCfg::BM) * (a.n_total / WgCfg::BN);
+  const int grid = (units + 7) / 8 * 8;
+  hipLaunchKernelGGL(wgrad_kernel<WgCfg>, dim3(grid), dim3(WgCfg::NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace olmoe

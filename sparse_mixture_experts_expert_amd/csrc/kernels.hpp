@@ -29,6 +29,8 @@ struct SelectArgs {
   float* blk_lse2;        // [nblk]
   uint64_t keep;          // bit e set: expert e may be chosen (at least 8 bits set)
   int renormalize;        // nonzero: route_probs divided by their sum over the 8 slots
+  float* p_all = nullptr; // [T,64] all 64 probabilities, or null (backward pass)
+  float* lse = nullptr;   // [T] log-sum-exp of the logits, or null (backward pass)
 };
 // softmax + top-8 per routing block (one launch, one workgroup per block)
 hipError_t launch_router_select(const SelectArgs& a, hipStream_t stream);
@@ -61,6 +63,8 @@ struct PermuteArgs {
   const int32_t* blk_base;
   int32_t* perm;            // [8T]
   int32_t* inv;             // [T,8]
+  const float* probs = nullptr;   // [T,8] routing weights, read when row_w is set
+  float* row_w = nullptr;         // [8T] routing weight of each row, or null (backward pass)
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
 // scan + permutation in one workgroup, for T <= SMALL_TOKENS
@@ -90,6 +94,7 @@ struct GemmArgs {
   const int2* tiles_dn;
   uint16_t* h;              // fp16 [8T,1024] SwiGLU activations, expert-contiguous rows
   uint16_t* y;              // fp16 [8T,2048] expert outputs, expert-contiguous rows
+  float* gu = nullptr;      // gate/up: also store fp32 G and U [8T, 2048] (backward recompute), or null
 };
 hipError_t launch_gateup(const GemmArgs& a, const GemmPlan& p, hipStream_t stream);
 hipError_t launch_down(const GemmArgs& a, const GemmPlan& p, hipStream_t stream);
@@ -105,6 +110,74 @@ struct CombineArgs {
   float eps;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- backward pass
+
+// dgrad: rows of one expert (tile list) x output columns, K = 2048
+struct BwdDgradArgs {
+  const uint16_t* a;          // bf16 rows of 2048 (K-inner)
+  const int32_t* a_rows;      // row -> source row of a (gather), or null (row itself)
+  const uint16_t* b0;         // weights read as [k][n]: rows k < kb_split from b0, the rest from b1
+  const uint16_t* b1;
+  int ldb;                    // elements per weight row
+  long b_stride;              // elements per expert
+  int kb_split;
+  const int32_t* tile_count;  // row tiles (first row, expert | rows << 8)
+  const int2* tiles;
+  // epilogue: dH~ -> dG, dU (bf16 [rows, 2048]) and w*H (bf16 [rows, 1024]), or plain fp32 rows
+  const float* row_w;
+  const float* gu;            // fp32 [rows, 2048]: G | U of the forward
+  uint16_t* dgu;
+  uint16_t* hw;
+  float* out_f32;             // fp32 [rows, 2048]
+};
+int bwd_tile_rows();   // row tile height of the dgrad kernels
+hipError_t launch_dgrad(const BwdDgradArgs& a, int T, bool dh, hipStream_t stream);
+
+// wgrad: per expert, out[m][n] = sum over the expert's rows r of a[r][m] * b[r][n]
+struct BwdWgradArgs {
+  const uint16_t* a;          // bf16 [rows, lda], expert-contiguous
+  int lda;
+  const uint16_t* b;          // bf16 [rows, ldb]
+  int ldb;
+  const int32_t* offsets;     // [65]
+  const uint16_t* zero;       // at least 256 zero bytes (rows past an expert's count)
+  int m_total, n_total;       // output rows / columns per expert
+  float* out0;                // rows m < m_split
+  float* out1;                // rows m >= m_split (at m - m_split)
+  int m_split;
+  long out_stride;            // elements per expert in out0 / out1
+};
+hipError_t launch_wgrad(const BwdWgradArgs& a, hipStream_t stream);
+
+struct BwdSmallArgs {
+  int T;
+  const uint16_t* x;          // bf16 [T,2048]
+  const uint16_t* dout;       // bf16 [T,2048]
+  const float* w_router;      // fp32 [64,2048]
+  const int32_t* ids;         // [T,8]
+  const float* p_all;         // [T,64]
+  const float* lse;           // [T]
+  const int32_t* offsets;     // [65]
+  const int32_t* perm;        // [8T]
+  const int32_t* inv;         // [T,8]
+  const uint16_t* y;          // fp16 [8T,2048] expert outputs
+  float g_aux, g_z;
+  float* dlogits;             // fp32 [T,64]
+  uint16_t* xg;               // bf16 [8T,2048] x rows in expert order
+  uint16_t* dg;               // bf16 [8T,2048] dout rows in expert order
+  const float* dxr;           // fp32 [8T,2048] per-row input gradients
+  float* dx;                  // fp32 [T,2048]
+  float* dwr_part;            // fp32 [nsplit,64,2048]
+  float* dw_router;           // fp32 [64,2048]
+  uint16_t* zero;             // 4 KiB
+  int32_t* tp_bwd;            // [65] row-tile prefix of the dgrad tile list
+  int2* tiles_bwd;
+};
+int bwd_router_splits(int T);
+hipError_t launch_bwd_prepare(const BwdSmallArgs& a, hipStream_t stream);   // zero row, tile list, gathers
+hipError_t launch_bwd_router(const BwdSmallArgs& a, hipStream_t stream);    // dw and dlogits
+hipError_t launch_bwd_finish(const BwdSmallArgs& a, hipStream_t stream);    // dW_router and dx
 
 hipError_t launch_rmsnorm(const float* h, float eps, int T, uint16_t* x_out, hipStream_t stream);
 hipError_t launch_residual_add(float* h, const uint16_t* y, int T, hipStream_t stream);

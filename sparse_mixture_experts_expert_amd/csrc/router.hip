@@ -202,7 +202,7 @@ template <int NS>
 __global__ __launch_bounds__(256) void router_select_kernel(SelectArgs a) {
   __shared__ SelectLds L;
   select_block<NS>(a.partial, a.T, blockIdx.x, L, a.ids, a.probs, a.lrank, a.blk_counts, a.blk_psum,
-                   a.blk_lse2, a.keep, a.renormalize);
+                   a.blk_lse2, a.keep, a.renormalize, a.p_all, a.lse);
 }
 
 }  // namespace

@@ -79,7 +79,8 @@ __device__ __forceinline__ void select_block(const float2* __restrict__ partial,
                                              int32_t* __restrict__ blk_counts,
                                              float* __restrict__ blk_psum,
                                              float* __restrict__ blk_lse2, uint64_t keep,
-                                             int renormalize) {
+                                             int renormalize, float* __restrict__ p_all = nullptr,
+                                             float* __restrict__ lse_out = nullptr) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -156,6 +157,8 @@ __device__ __forceinline__ void select_block(const float2* __restrict__ partial,
     for (int i = 0; i < 4; ++i)
       if (my_slot[i] >= 0) probs[t * K + my_slot[i]] = renormalize ? p[i] * wsc : p[i];
   }
+  if (valid && p_all) *reinterpret_cast<f32x4*>(p_all + (size_t)t * E + j * 4) = f32x4{p[0], p[1], p[2], p[3]};
+  if (valid && lse_out && j == 0) lse_out[t] = lse;
   L.chosen[rt][j] = valid ? static_cast<uint8_t>(taken) : 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) L.p[rt][j * 4 + i] = valid ? p[i] : 0.f;
@@ -287,8 +290,8 @@ __device__ __forceinline__ void scan_block(const ScanArgs& a, ScanLds& L) {
     if (e == 0) {
       double z = 0.0;
       for (int q = 0; q < 16; ++q) z += L.sl2[q];
-      if (a.aux_loss) a.aux_loss[0] = static_cast<float>(0.01 * E * fp);
-      if (a.z_loss) a.z_loss[0] = a.T > 0 ? static_cast<float>(0.001 * z / a.T) : 0.f;
+      if (a.aux_loss) a.aux_loss[0] = static_cast<float>(LB_ALPHA * E * fp);
+      if (a.z_loss) a.z_loss[0] = a.T > 0 ? static_cast<float>(Z_BETA * z / a.T) : 0.f;
     }
   }
   __syncthreads();
@@ -312,6 +315,7 @@ __device__ __forceinline__ void permute_range(const PermuteArgs& a, int i0, int 
     const int pos = a.blk_base[(t / ROUTE_BLOCK) * E + e] + a.lrank[i];
     a.perm[pos] = t;
     a.inv[i] = pos;
+    if (a.row_w) a.row_w[pos] = a.probs[i];
   }
 }
 

@@ -124,6 +124,29 @@ def test_residual_entry_point_checks_arguments_first(L):
     assert "x_next" in L.olmoe_last_error().decode() or "workspace" in L.olmoe_last_error().decode()
 
 
+def test_backward_checks_arguments_first(L):
+    # every call here fails validation, so nothing reaches a device (fake pointers)
+    vp = ctypes.c_void_p
+    T = 16
+    wsb = binding.backward_workspace_bytes(T)
+    assert wsb > binding.workspace_bytes(T) + T * 8 * (2048 * 4 + 2048 * 2 * 3 + 1024 * 2 + 2048 * 4)
+    assert binding.backward_workspace_bytes(-1) == 0
+
+    def bwd(dx=5 << 20, dwr=6 << 20, dwg=1 << 34, dwu=2 << 34, dwd=3 << 34, ws=8 << 36, wsb=wsb, g=1.0, x=1 << 20):
+        return L.olmoe_moe_backward(vp(x), vp(2 << 20), vp(1 << 32), vp(2 << 32), vp(3 << 32), T, vp(4 << 20),
+                                    ctypes.c_float(g), ctypes.c_float(0.5), vp(dx), vp(dwr), vp(dwg), vp(dwu),
+                                    vp(dwd), vp(ws), wsb, None)
+    assert bwd(dwg=0) == binding.EINVAL                        # weight gradient NULL
+    assert bwd(dx=0) == binding.EINVAL                         # dx NULL with T > 0
+    assert bwd(g=float("nan")) == binding.EINVAL
+    assert bwd(dx=(5 << 20) + 8) == binding.EINVAL             # misaligned
+    assert bwd(wsb=1000) == binding.EWORKSPACE
+    assert bwd(dx=(1 << 20) + 4096) == binding.EINVAL          # dx over x
+    assert bwd(dwu=(1 << 34) + 4096) == binding.EINVAL         # two outputs overlap
+    assert bwd(dwd=(8 << 36) + 256) == binding.EINVAL          # output in the workspace
+    assert bwd(dwr=(1 << 32) + 64) == binding.EINVAL           # dW_router over W_gate
+
+
 def test_glue_entry_points_reject_bad_arguments(L):
     vp = ctypes.c_void_p
     assert L.olmoe_rmsnorm_bf16(vp(1 << 20), ctypes.c_float(0.0), 4, vp(1 << 30), None) == binding.EINVAL

@@ -1,0 +1,114 @@
+"""GPU parity of the layer's backward pass (olmoe_moe_backward, through the C ABI)
+against the float64 oracle's chain rule (oracle.moe_layer_backward_ref, itself pinned
+against autograd and finite differences).  Every gradient tensor is compared whole."""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_mixture_experts_expert_amd import binding, inputs
+from tests import parity
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+GRAD_REL_L2 = 1e-2        # the output bar of the forward, applied to every gradient tensor
+GRAD_MAX_ABS_RMS = 2e-2   # dW_router (fp32 throughout)
+# dx and the expert weight gradients are sums of products of one bf16-rounded operand (dG,
+# dU or w*H, rounded to nearest even: relative error <= 2^-9) with an exact one, accumulated
+# in fp32; each element's error is therefore bounded by 2^-9 times the same sum over |terms|.
+# With few rows an expert's gradient is a near rank-one outer product whose largest entries
+# are far above the tensor's RMS, and the largest error of dx grows with the number of
+# elements, so an RMS-relative bar cannot hold at every size; the bound below (four times
+# the rounding bound, plus a floor far under the RMS) can.
+GRAD_TERM_BOUND = 2.0 ** -7
+
+
+def _log(msg):
+    print(f"[gpu-backward] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def weights():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm device")
+    binding.lib()
+    w = inputs.device_weights(seed=0, workload="parity")
+    host = {k: (v.cpu().numpy() if v.dtype == torch.float32 else parity.bf16_tensor_to_bits(v))
+            for k, v in w.items()}
+    return w, host
+
+
+def check_grad(got, ref, name, mag=None):
+    """rel L2 over the tensor, then max |error| / RMS (mag None) or |error| against the
+    per-element rounding bound GRAD_TERM_BOUND * mag; returns (rel L2, worst ratio)."""
+    got = np.asarray(got, np.float64)
+    nrm = np.linalg.norm(ref)
+    if nrm == 0:
+        assert not np.any(got), f"{name}: expected zeros"
+        return 0.0, 0.0
+    rel = np.linalg.norm(got - ref) / nrm
+    rms = nrm / np.sqrt(ref.size)
+    assert rel <= GRAD_REL_L2, f"{name}: rel L2 {rel:.3e}"
+    err = np.abs(got - ref)
+    if mag is None:
+        mx = err.max() / rms
+        assert mx <= GRAD_MAX_ABS_RMS, f"{name}: max abs / rms {mx:.3e}"
+        return rel, mx
+    worst = (err / (GRAD_TERM_BOUND * mag + 2.0 ** -20 * rms)).max()
+    assert worst <= 1.0, f"{name}: error {worst:.2f} x the rounding bound"
+    assert not np.any(got[mag == 0]), f"{name}: nonzero gradient where no row contributes"
+    return rel, worst
+
+
+def run_backward(w, hw, T, seed, g_aux, g_z):
+    x = inputs.device_x(T, seed=seed, workload="parity")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 100)
+    dout = torch.randn((T, 2048), generator=g, device="cuda").to(torch.bfloat16)
+    fwd = binding.moe_forward(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"])
+    b = binding.moe_backward(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], dout, g_aux=g_aux, g_z=g_z)
+    torch.cuda.synchronize()
+    xb = parity.bf16_tensor_to_bits(x)
+    ids = fwd["route_ids"].cpu().numpy()
+    ref_fwd = oracle.moe_layer_ref(xb, hw["w_router"], hw["w_gate"], hw["w_up"], hw["w_down"], 8)
+    ntie = parity.check_routing(ids, fwd["route_probs"].cpu().numpy(), ref_fwd, f"backward T={T}")
+    forced = ids if ntie or not np.array_equal(ids, ref_fwd["ids"]) else None
+    ref = oracle.moe_layer_backward_ref(xb, hw["w_router"], hw["w_gate"], hw["w_up"], hw["w_down"],
+                                        parity.bf16_tensor_to_bits(dout), g_aux, g_z, 8, forced_ids=forced,
+                                        magnitudes=True)
+    out = {}
+    for name, mag in (("dx", "mag_dx"), ("dw_router", None), ("dw_gate", "mag_gate"), ("dw_up", "mag_up"),
+                      ("dw_down", "mag_down")):
+        out[name] = check_grad(b[name].cpu().numpy(), ref[name], f"T={T} {name}", ref[mag] if mag else None)
+    _log(f"T={T} g_aux={g_aux} g_z={g_z} ties={ntie} " +
+         " ".join(f"{n}=({r:.1e},{m:.1e})" for n, (r, m) in out.items()))
+    return b, ref
+
+
+@pytest.mark.parametrize("T,g_aux,g_z", [(1, 1.0, 1.0), (33, 1.0, 1.0), (200, 0.0, 0.0), (200, 5.0, -3.0),
+                                         (700, 1.0, 1.0), (2100, 1.0, 1.0), (4096, 1.0, 1.0)])
+def test_backward_matches_oracle(weights, T, g_aux, g_z):
+    w, hw = weights
+    _log(f"backward T={T}")
+    run_backward(w, hw, T, seed=20 + T, g_aux=g_aux, g_z=g_z)
+
+
+def test_backward_zero_tokens_gives_zero_weight_gradients(weights):
+    w, _ = weights
+    x = torch.empty((0, 2048), dtype=torch.bfloat16, device="cuda")
+    b = binding.moe_backward(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], x.clone())
+    torch.cuda.synchronize()
+    for k in ("dw_router", "dw_gate", "dw_up", "dw_down"):
+        assert not torch.any(b[k]).item(), k
+
+
+def test_backward_bitwise_reproducible(weights):
+    w, _ = weights
+    T = 300
+    x = inputs.device_x(T, seed=31, workload="parity")
+    dout = inputs.device_x(T, seed=32, workload="parity")
+    a = binding.moe_backward(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], dout)
+    b = binding.moe_backward(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], dout)
+    torch.cuda.synchronize()
+    for k in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down"):
+        assert torch.equal(a[k], b[k]), k
