@@ -83,6 +83,11 @@ def traffic_from_profiles(workload, stage):
 N_WEIGHT_SETS = 4   # single-layer steps cycle through distinct weight sets (3.2 GB, far above the 256 MB MALL)
 
 
+def wl_layers_of(workload):
+    from sparse_mixture_experts_expert_amd import inputs
+    return inputs.WORKLOADS[workload].layers
+
+
 def measure(workload, steps, warmup, seed=0, tokens=None):
     import torch
     from sparse_mixture_experts_expert_amd import binding, inputs
@@ -188,6 +193,52 @@ def measure(workload, steps, warmup, seed=0, tokens=None):
     if wl.layers == 1:
         res["host_inputs"] = d
     return res
+
+
+# backward: the gradient GEMMs are twice the forward's expert GEMMs (dgrad + wgrad), plus the
+# router's two small products; the forward recomputed inside is not counted
+BWD_FLOP_PER_TOKEN = 2 * K * 3 * 2 * D * F + 2 * 2 * D * E
+
+
+def measure_backward(workload, steps, warmup, seed=0):
+    """Wall-clock time of olmoe_moe_backward (forward recompute + gradients) per call."""
+    import torch
+    from sparse_mixture_experts_expert_amd import binding, inputs
+
+    wl = inputs.WORKLOADS[workload]
+    T = wl.tokens
+    d = inputs.device_workload(workload, seed=seed)
+    sets = [d] + [inputs.device_weights(seed, workload, layer=r, skew=wl.skew) for r in range(1, N_WEIGHT_SETS)]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 7)
+    dout = torch.randn((T, D), generator=g, device="cuda").to(torch.bfloat16)
+    f32 = torch.float32
+    outs = dict(dx=torch.empty((T, D), dtype=f32, device="cuda"),
+                dw_router=torch.empty((E, D), dtype=f32, device="cuda"),
+                dw_gate=torch.empty((E, F, D), dtype=f32, device="cuda"),
+                dw_up=torch.empty((E, F, D), dtype=f32, device="cuda"),
+                dw_down=torch.empty((E, D, F), dtype=f32, device="cuda"))
+    ws = torch.empty(binding.backward_workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    it = [0]
+
+    def step():
+        w = sets[it[0] % N_WEIGHT_SETS]
+        it[0] += 1
+        binding.moe_backward(d["x"], w["w_router"], w["w_gate"], w["w_up"], w["w_down"], dout, g_aux=1.0,
+                             g_z=1.0, workspace=ws, **outs)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    return {"workload": workload, "tokens": T, "ms_per_step": round(sec * 1e3, 5),
+            "tokens_per_s": round(T / sec, 1),
+            "tflops": round(BWD_FLOP_PER_TOKEN * T / sec / 1e12, 2),
+            "mfma_frac": round(BWD_FLOP_PER_TOKEN * T / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "note": "gradients of x and all weights; the forward recompute inside is timed, not counted"}
 
 
 def cpu_baseline(d, workload, budget_s=20.0):
@@ -358,6 +409,7 @@ def main():
     ap.add_argument("--tokens", type=int, default=None, help="override the workload's token count")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--copy-probe", action="store_true", help="run the counter-calibration copy and exit")
     ap.add_argument("--traffic-summary", action="store_true", help="summarise --pmc runs into profiles/")
     ap.add_argument("--stats-summary", metavar="DIR", dest="stats_dir", help="summarise a --stats run")
@@ -428,6 +480,10 @@ def main():
                              "tflops": round(s["tflops"], 2), "layer_mfma_frac": round(s["layer_mfma_frac"], 4),
                              "stage_ms": s["stage_ms"], "roofline": s["roofline"]}
         d = None
+    if not args.no_backward and wl_layers_of(args.workload) == 1:
+        wls = [args.workload] + ([] if args.no_secondary or args.workload == "prefill-4096" else ["prefill-4096"])
+        torch.cuda.empty_cache()
+        line["backward"] = [measure_backward(w, max(5, args.steps // 5), 2, args.seed) for w in wls]
     if not args.no_cpu:
         if d is None:
             from sparse_mixture_experts_expert_amd import inputs

@@ -18,7 +18,7 @@ namespace olmoe {
 
 namespace {
 
-constexpr int WR_SPLIT_TOKENS = 256;   // tokens per partial sum of dW_router
+constexpr int WR_SPLIT_TOKENS = 32;    // tokens per partial sum of dW_router
 
 // workgroup 0: zero row and the dgrad row-tile list; the others: x and dout rows in
 // expert order (one row per workgroup)
@@ -101,11 +101,29 @@ __global__ __launch_bounds__(256) void bwd_wrouter_partial_kernel(BwdSmallArgs a
   float acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  for (int t = t0; t < t1; ++t) {
-    const float xv = bf16_to_f32(a.x[(size_t)t * D + col]);
-    const float* dl = a.dlogits + (size_t)t * E + e0;
+  if (t1 - t0 == WR_SPLIT_TOKENS) {   // full split: every load issued before the FMAs
+    float xv[WR_SPLIT_TOKENS];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = fmaf(dl[i], xv, acc[i]);
+    for (int q = 0; q < WR_SPLIT_TOKENS; ++q) xv[q] = bf16_to_f32(a.x[(size_t)(t0 + q) * D + col]);
+#pragma unroll 4
+    for (int q = 0; q < WR_SPLIT_TOKENS; ++q) {
+      const float4* dl = reinterpret_cast<const float4*>(a.dlogits + (size_t)(t0 + q) * E + e0);
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 d4 = dl[i4];
+        acc[4 * i4] = fmaf(d4.x, xv[q], acc[4 * i4]);
+        acc[4 * i4 + 1] = fmaf(d4.y, xv[q], acc[4 * i4 + 1]);
+        acc[4 * i4 + 2] = fmaf(d4.z, xv[q], acc[4 * i4 + 2]);
+        acc[4 * i4 + 3] = fmaf(d4.w, xv[q], acc[4 * i4 + 3]);
+      }
+    }
+  } else {
+    for (int t = t0; t < t1; ++t) {
+      const float xv = bf16_to_f32(a.x[(size_t)t * D + col]);
+      const float* dl = a.dlogits + (size_t)t * E + e0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = fmaf(dl[i], xv, acc[i]);
+    }
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) a.dwr_part[((size_t)blockIdx.y * E + e0 + i) * D + col] = acc[i];
@@ -118,8 +136,8 @@ __global__ __launch_bounds__(256) void bwd_wrouter_reduce_kernel(BwdSmallArgs a,
   a.dw_router[i] = s;
 }
 
-// dx for 16 tokens per workgroup, 8 columns per thread: dl W_router, then the token's 8
-// per-row input gradients in slot order
+// dx for DX_TOK tokens and 256 columns per workgroup, one column per thread: dl W_router, then
+// the token's 8 per-row input gradients in slot order
 constexpr int DX_TOK = 16;
 __global__ __launch_bounds__(256) void bwd_dx_kernel(BwdSmallArgs a) {
   __shared__ float sdl[DX_TOK][E];
@@ -129,39 +147,28 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(BwdSmallArgs a) {
     const int tk = i / E;
     sdl[tk][i % E] = t0 + tk < a.T ? a.dlogits[(size_t)(t0 + tk) * E + i % E] : 0.f;
   }
+  const int col = blockIdx.y * 256 + tid;
+  float wr[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) wr[e] = a.w_router[(size_t)e * D + col];
   __syncthreads();
-  const int c0 = tid * 8;
-  float acc[DX_TOK][8];
+  float acc[DX_TOK];
 #pragma unroll
-  for (int tk = 0; tk < DX_TOK; ++tk)
+  for (int tk = 0; tk < DX_TOK; ++tk) acc[tk] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[tk][i] = 0.f;
-  for (int e = 0; e < E; ++e) {
-    const float4 w0 = *reinterpret_cast<const float4*>(a.w_router + (size_t)e * D + c0);
-    const float4 w1 = *reinterpret_cast<const float4*>(a.w_router + (size_t)e * D + c0 + 4);
-    const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  for (int e = 0; e < E; ++e)
 #pragma unroll
-    for (int tk = 0; tk < DX_TOK; ++tk) {
-      const float d = sdl[tk][e];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[tk][i] = fmaf(d, w[i], acc[tk][i]);
-    }
-  }
+    for (int tk = 0; tk < DX_TOK; ++tk) acc[tk] = fmaf(sdl[tk][e], wr[e], acc[tk]);
 #pragma unroll
   for (int tk = 0; tk < DX_TOK; ++tk) {
     const int t = t0 + tk;
     if (t >= a.T) break;
+    float r[K];
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const float* row = a.dxr + (size_t)a.inv[t * K + j] * D + c0;
-      const float4 r0 = *reinterpret_cast<const float4*>(row);
-      const float4 r1 = *reinterpret_cast<const float4*>(row + 4);
-      acc[tk][0] += r0.x; acc[tk][1] += r0.y; acc[tk][2] += r0.z; acc[tk][3] += r0.w;
-      acc[tk][4] += r1.x; acc[tk][5] += r1.y; acc[tk][6] += r1.z; acc[tk][7] += r1.w;
-    }
-    float4* o = reinterpret_cast<float4*>(a.dx + (size_t)t * D + c0);
-    o[0] = make_float4(acc[tk][0], acc[tk][1], acc[tk][2], acc[tk][3]);
-    o[1] = make_float4(acc[tk][4], acc[tk][5], acc[tk][6], acc[tk][7]);
+    for (int j = 0; j < K; ++j) r[j] = a.dxr[(size_t)a.inv[t * K + j] * D + col];
+#pragma unroll
+    for (int j = 0; j < K; ++j) acc[tk] += r[j];
+    a.dx[(size_t)t * D + col] = acc[tk];
   }
 }
 
@@ -188,7 +195,7 @@ hipError_t launch_bwd_finish(const BwdSmallArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(bwd_wrouter_reduce_kernel, dim3(E * D / 256), dim3(256), 0, stream, a, ns);
   e = hipGetLastError();
   if (e != hipSuccess || a.T == 0) return e;
-  hipLaunchKernelGGL(bwd_dx_kernel, dim3((a.T + DX_TOK - 1) / DX_TOK), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(bwd_dx_kernel, dim3((a.T + DX_TOK - 1) / DX_TOK, D / 256), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

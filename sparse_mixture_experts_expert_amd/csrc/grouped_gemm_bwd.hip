@@ -35,8 +35,6 @@ namespace olmoe {
 
 namespace {
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-
 template <int N>
 __device__ __forceinline__ void vm_barrier_b() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
@@ -59,17 +57,55 @@ __device__ __forceinline__ int kout_off(int k, int col) {
 // element offset of chunk ch of row `row` in a K-inner tile of 64-element rows
 __device__ __forceinline__ int kin_off(int row, int ch) { return row * 64 + ((ch ^ (row & 7)) << 3); }
 
-// 32x32x16 operand of columns col0 .. col0+31 at k-step kk from a K-outer tile
+// LDS byte address (offset in the LDS aperture) of element e of a K-outer tile
+__device__ __forceinline__ uint32_t lds_addr(const bf16_t* tile, int e) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const bf16_t*)(tile + e)));
+}
+
+// addresses of the two transposing reads that give the 32x32x16 operand of columns
+// col0 .. col0+31 at k-step kk of a K-outer tile: 8 consecutive k of column col0 + lane%32
 template <int BW>
-__device__ __forceinline__ bf16x8 frag_kout(const bf16_t* tile, int kk, int col0, int lane) {
+__device__ __forceinline__ void frag_kout_addr(const bf16_t* tile, int kk, int col0, int lane, uint32_t& a_lo,
+                                               uint32_t& a_hi) {
   const int krow = kk * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);
   const int col = col0 + ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
-  typedef __attribute__((address_space(3))) v4i16 lds_v4;
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(tile + kout_off<BW>(krow, col)));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(tile + kout_off<BW>(krow + 4, col)));
-  const u32x4 v = {__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
-                   __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y};
+  a_lo = lds_addr(tile, kout_off<BW>(krow, col));
+  a_hi = lds_addr(tile, kout_off<BW>(krow + 4, col));
+}
+
+__device__ __forceinline__ bf16x8 frag_of(uint2 lo, uint2 hi) {
+  const u32x4 v = {lo.x, lo.y, hi.x, hi.y};
   return __builtin_bit_cast(bf16x8, v);
+}
+
+// Four transposing LDS reads, waited for inside the same block.  Written as assembly
+// because the compiler, unable to tell these reads from the LDS-DMA writes still in flight
+// (to other ring slots), would otherwise drain every outstanding load before each of them;
+// the stage being read was already waited for at the top of its k-step.
+__device__ __forceinline__ void tr_read4(uint2& r0, uint2& r1, uint2& r2, uint2& r3, uint32_t a0, uint32_t a1,
+                                         uint32_t a2, uint32_t a3) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
+
+// two 32x32x16 operands (columns col0 and col1) of a K-outer tile
+template <int BW>
+__device__ __forceinline__ void frag_kout2(const bf16_t* tile, int kk, int col0, int col1, int lane, bf16x8& f0,
+                                           bf16x8& f1) {
+  uint32_t a0, a1, a2, a3;
+  frag_kout_addr<BW>(tile, kk, col0, lane, a0, a1);
+  frag_kout_addr<BW>(tile, kk, col1, lane, a2, a3);
+  uint2 r0, r1, r2, r3;
+  tr_read4(r0, r1, r2, r3, a0, a1, a2, a3);
+  f0 = frag_of(r0, r1);
+  f1 = frag_of(r2, r3);
 }
 
 __device__ __forceinline__ float sigmoidf(float g) { return 1.0f / (1.0f + __expf(-g)); }
@@ -187,8 +223,8 @@ __global__ __launch_bounds__(C::NT) void dgrad_kernel(BwdDgradArgs a) {
 #pragma unroll
           for (int i = 0; i < NF; ++i)
             af[i] = *reinterpret_cast<const bf16x8*>(&As[kin_off((i * C::WM + wm) * 32 + (lane & 31), kc)]);
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j) bfr[j] = frag_kout<C::BN>(Bs, kk, wn * (C::BN / C::WN) + j * 32, lane);
+          static_assert(C::FN == 2, "B operands are read in pairs");
+          frag_kout2<C::BN>(Bs, kk, wn * (C::BN / C::WN), wn * (C::BN / C::WN) + 32, lane, bfr[0], bfr[1]);
 #pragma unroll
           for (int i = 0; i < NF; ++i)
 #pragma unroll
@@ -207,27 +243,41 @@ __global__ __launch_bounds__(C::NT) void dgrad_kernel(BwdDgradArgs a) {
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
+    for (int j = 0; j < C::FN; ++j) {
+      const int c = nt * C::BN + wn * (C::BN / C::WN) + j * 32 + (lane & 31);
+      const int rb = (i * C::WM + wm) * 32 + (lane >> 5) * 4;   // + (v/4)*8 + v%4
+      if constexpr (C::EPI == EPI_DH) {
+        // dH = w dH~; H = SiLU(G) U, so dG = dH U SiLU'(G), dU = dH SiLU(G).  The fragment's
+        // G, U and w are loaded together before any store (the stores could alias them).
+        float g[16], u[16], w[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = (i * C::WM + wm) * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-        const int c = nt * C::BN + wn * (C::BN / C::WN) + j * 32 + (lane & 31);
-        if (r >= valid) continue;
-        const size_t row = (size_t)(row0 + r);
-        if constexpr (C::EPI == EPI_DH) {
-          // dH = w dH~; H = SiLU(G) U, so dG = dH U SiLU'(G), dU = dH SiLU(G)
-          const float w = a.row_w[row];
-          const float g = a.gu[row * (2 * F) + c], u = a.gu[row * (2 * F) + F + c];
-          const float sg = sigmoidf(g);
-          const float s = g * sg;
-          const float dh = w * acc[i][j][v];
-          a.dgu[row * (2 * F) + c] = f32_to_bf16(dh * u * (sg * (1.0f + g * (1.0f - sg))));
-          a.dgu[row * (2 * F) + F + c] = f32_to_bf16(dh * s);
-          a.hw[row * F + c] = f32_to_bf16(w * s * u);
-        } else {
-          a.out_f32[row * D + c] = acc[i][j][v];
+        for (int v = 0; v < 16; ++v) {
+          const int r = rb + (v >> 2) * 8 + (v & 3);
+          const size_t row = (size_t)(row0 + (r < valid ? r : 0));
+          g[v] = a.gu[row * (2 * F) + c];
+          u[v] = a.gu[row * (2 * F) + F + c];
+          w[v] = a.row_w[row];
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = rb + (v >> 2) * 8 + (v & 3);
+          if (r >= valid) continue;
+          const size_t row = (size_t)(row0 + r);
+          const float sg = sigmoidf(g[v]);
+          const float sl = g[v] * sg;
+          const float dh = w[v] * acc[i][j][v];
+          a.dgu[row * (2 * F) + c] = f32_to_bf16(dh * u[v] * (sg * (1.0f + g[v] * (1.0f - sg))));
+          a.dgu[row * (2 * F) + F + c] = f32_to_bf16(dh * sl);
+          a.hw[row * F + c] = f32_to_bf16(w[v] * sl * u[v]);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = rb + (v >> 2) * 8 + (v & 3);
+          if (r < valid) a.out_f32[(size_t)(row0 + r) * D + c] = acc[i][j][v];
         }
       }
+    }
 }
 
 // ----------------------------------------------------------------------------- wgrad
@@ -319,10 +369,9 @@ __global__ __launch_bounds__(C::NT) void wgrad_kernel(BwdWgradArgs a) {
     for (int kk = 0; kk < NKK; ++kk) {
       if (more) issue(kt + C::STAGES - 1, next_slot, kk * C::IPS / NKK, (kk + 1) * C::IPS / NKK);
       bf16x8 af[C::FM], bfr[C::FN];
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) af[i] = frag_kout<C::BM>(As, kk, wm * (C::BM / C::WM) + i * 32, lane);
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) bfr[j] = frag_kout<C::BN>(Bs, kk, wn * (C::BN / C::WN) + j * 32, lane);
+      static_assert(C::FM == 2 && C::FN == 2, "operands are read in pairs");
+      frag_kout2<C::BM>(As, kk, wm * (C::BM / C::WM), wm * (C::BM / C::WM) + 32, lane, af[0], af[1]);
+      frag_kout2<C::BN>(Bs, kk, wn * (C::BN / C::WN), wn * (C::BN / C::WN) + 32, lane, bfr[0], bfr[1]);
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
