@@ -294,6 +294,9 @@ def copy_probe():
 
 def _stage_of(kernel_name):
     n = kernel_name
+    for key in ("dgrad_kernel", "wgrad_kernel", "bwd_"):
+        if key in n:
+            return "backward"
     if "grouped_gemm_kernel" in n:
         cfg = n[n.index("Cfg<") + 4:n.index(">")].split(",")
         return "gateup" if cfg[4].strip() == "true" else "down"
@@ -388,8 +391,12 @@ def stats_summary(args):
         if st is None:
             continue    # input generation and copies made by the harness around the layer
         short = n.replace("olmoe::(anonymous namespace)::", "").replace("void ", "")
-        short = short.split("(")[0] if "Cfg" not in short else short[:short.index(">") + 1].replace(
-            "grouped_gemm_kernel<", "grouped_gemm_kernel ")
+        if "Cfg" in short:
+            short = short[:short.index(">") + 1]
+            for k in ("grouped_gemm_kernel", "dgrad_kernel", "wgrad_kernel"):
+                short = short.replace(k + "<", k + " ")
+        else:
+            short = short.split("(")[0]
         lines.append(f"| {short} | {st} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     lines += ["", f"kernel sources hash: {kernel_source_hash()}", "",
