@@ -202,6 +202,47 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
     if (s < C::KT) issue(s, s, 0, C::IPS);
 
   constexpr int NKK = BK / 16;   // MFMA k-steps per stage
+  using V = typename C::V;
+  // fragments of MFMA k-step kk of a stage: A rows of this wave's NF fragments, B of its columns
+  auto load_frags = [&](auto nf_tag, const bf16_t* As, const bf16_t* Bs, int kk, V* af, V (*bfr)[C::FN])
+      __attribute__((always_inline)) {
+    constexpr int NF = decltype(nf_tag)::value;
+    const int kc = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const int r = (i * C::WM + wm) * 32 + (lane & 31);
+      af[i] = *reinterpret_cast<const V*>(&As[swz<BK>(r, kc)]);
+    }
+#pragma unroll
+    for (int g = 0; g < C::G; ++g)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        const int r = g * C::BN + wn * (C::BN / C::WN) + j * 32 + (lane & 31);
+        u32x4 v = *reinterpret_cast<const u32x4*>(&Bs[swz<BK>(r, kc)]);
+        if constexpr (!C::GATEUP) {   // bf16 -> fp16 (exact in fp16's normal range)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v[q] << 16), __uint_as_float(v[q] & 0xFFFF0000u));
+            v[q] = __builtin_bit_cast(uint32_t, h);
+          }
+        }
+        bfr[g][j] = __builtin_bit_cast(V, v);
+      }
+  };
+  auto mfmas = [&](auto nf_tag, const V* af, const V (*bfr)[C::FN]) __attribute__((always_inline)) {
+    constexpr int NF = decltype(nf_tag)::value;
+#pragma unroll
+    for (int g = 0; g < C::G; ++g)
+#pragma unroll
+      for (int i = 0; i < NF; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+          if constexpr (C::GATEUP)
+            acc[g][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[g][j], acc[g][i][j], 0, 0, 0);
+          else
+            acc[g][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bfr[g][j], acc[g][i][j], 0, 0, 0);
+        }
+  };
   auto kloop = [&](auto nf_tag) __attribute__((always_inline)) {
     constexpr int NF = decltype(nf_tag)::value;
     for (int kt = 0; kt < C::KT; ++kt) {
@@ -216,41 +257,9 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
         // stalls the wave on the memory queue before its MFMAs can start
         if (more) issue(kt + C::STAGES - 1, next_slot, kk * C::IPS / NKK, (kk + 1) * C::IPS / NKK);
         if constexpr (NF > 0) {
-          const int kc = kk * 2 + (lane >> 5);
-          using V = typename C::V;
           V af[NF], bfr[C::G][C::FN];
-#pragma unroll
-          for (int i = 0; i < NF; ++i) {
-            const int r = (i * C::WM + wm) * 32 + (lane & 31);
-            af[i] = *reinterpret_cast<const V*>(&As[swz<BK>(r, kc)]);
-          }
-#pragma unroll
-          for (int g = 0; g < C::G; ++g)
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j) {
-              const int r = g * C::BN + wn * (C::BN / C::WN) + j * 32 + (lane & 31);
-              u32x4 v = *reinterpret_cast<const u32x4*>(&Bs[swz<BK>(r, kc)]);
-              if constexpr (!C::GATEUP) {   // bf16 -> fp16 (exact in fp16's normal range)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                  const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v[q] << 16),
-                                                            __uint_as_float(v[q] & 0xFFFF0000u));
-                  v[q] = __builtin_bit_cast(uint32_t, h);
-                }
-              }
-              bfr[g][j] = __builtin_bit_cast(V, v);
-            }
-#pragma unroll
-          for (int g = 0; g < C::G; ++g)
-#pragma unroll
-            for (int i = 0; i < NF; ++i)
-#pragma unroll
-              for (int j = 0; j < C::FN; ++j) {
-                if constexpr (C::GATEUP)
-                  acc[g][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[g][j], acc[g][i][j], 0, 0, 0);
-                else
-                  acc[g][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bfr[g][j], acc[g][i][j], 0, 0, 0);
-              }
+          load_frags(nf_tag, As, Bs, kk, af, bfr);
+          mfmas(nf_tag, af, bfr);
         }
       }
     }
