@@ -48,10 +48,13 @@ namespace olmoe {
 
 namespace {
 
-// element offset of 16-byte chunk `ch` of tile row `row` (rows of BK elements);
-// the low 3 bits of the chunk index are XORed with the row
+// XOR key of the 16-byte chunks of tile row `row`: with 8 chunks per row (BK = 64) the low 3
+// bits of the row; with 4 (BK = 32) rows 4 apart, so 16 consecutive rows cover 256 bytes once
 template <int BK>
-__device__ __forceinline__ int swz(int row, int ch) { return row * BK + ((ch ^ (row & 7)) << 3); }
+__device__ __forceinline__ int swz_key(int row) { return BK >= 64 ? (row & 7) : ((row >> 2) & 3); }
+// element offset of 16-byte chunk `ch` of tile row `row` (rows of BK elements)
+template <int BK>
+__device__ __forceinline__ int swz(int row, int ch) { return row * BK + ((ch ^ swz_key<BK>(row)) << 3); }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
@@ -91,7 +94,7 @@ struct Cfg {
   static constexpr int JA = BM / (RPL * NW);      // loads j < JA fill A rows, the rest B rows
   static_assert(BM % (RPL * NW) == 0, "each load fills A rows only or B rows only");
   static_assert(FM >= 1 && FN >= 1, "tile too small for the wave grid");
-  static_assert(CPR >= 8 && CPR <= 64 && IPS * NT == ROWS * CPR && ROWS % (RPL * NW) == 0, "stage loading");
+  static_assert((CPR == 4 || CPR == 8) && IPS * NT == ROWS * CPR && ROWS % (RPL * NW) == 0, "stage loading");
   static_assert(STAGES >= 2 && IPS * (STAGES - 2) <= 63, "vmcnt range");
   static_assert(ND % BN == 0 && KD % BK == 0, "tiles");
 };
@@ -144,13 +147,13 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
   for (int i = 0; i < C::FM; ++i) nf += (i * C::WM + wm) * 32 < valid;
 
   // LDS-DMA sources: load j of wavefront wv fills stage rows (j*NW + wv)*RPL .. +RPL;
-  // lane -> row + lane/CPR, slot lane%CPR, which holds chunk slot ^ (row & 7)
+  // lane -> row + lane/CPR, slot lane%CPR, which holds chunk slot ^ swz_key(row)
   const bf16_t* gp[C::IPS];
   const int dummy = C::GATEUP ? perm[row0] : row0;   // any valid row for the tile's unused rows
 #pragma unroll
   for (int j = 0; j < C::IPS; ++j) {
     const int r = (j * C::NW + wv) * C::RPL + lane / C::CPR;
-    const int ch = (lane % C::CPR) ^ (r & 7);
+    const int ch = (lane % C::CPR) ^ swz_key<C::BK>(r);
     const bf16_t* p;
     if (r < C::BM) {
       const int src = r < valid ? (C::GATEUP ? perm[row0 + r] : row0 + r) : dummy;
@@ -297,15 +300,18 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
 // few hundred tokens the layer is bound by streaming the weights once; marking the weight loads
 // non-temporal keeps them from displacing the activation rows that every column tile re-reads.
 // 8 waves (2 per SIMD) keep more loads in flight per CU at small batches and give more MFMA
-// work per byte staged on the 256-row tiles of large batches.
+// work per byte staged on the 256-row tiles of large batches.  The large gate/up tiles run
+// three 32-k stages: the deeper prefetch beats the longer rows of two 64-k stages (328 against
+// 390 us at 4096 tokens on random data); the down GEMM prefers 64-k stages.
 using GuTiny = Cfg<32, 64, 1, 2, true, 4, 64, 1, true>;
 using DnTiny = Cfg<32, 64, 1, 2, false, 4>;
 using GuSmall = Cfg<64, 128, 2, 4, true, 2, 64, 1, true>;
 using DnSmall = Cfg<64, 256, 2, 4, false, 2, 64, 1, true>;
-using GuMedium = Cfg<128, 128, 2, 2, true, 3, 64, 0>;
-using DnMedium = Cfg<128, 128, 2, 2, false, 2>;
-using GuLarge = Cfg<256, 128, 4, 2, true, 2, 64, 0>;
+using GuLarge = Cfg<256, 128, 4, 2, true, 3, 32, 0>;
 using DnLarge = Cfg<256, 256, 4, 2, false, 2, 64, 0>;
+// 64-row tiles stream an expert's weights once per tile, so they lose to the 256-row tiles as
+// soon as experts commonly hold more than 64 rows (measured crossover between 384 and 512 tokens)
+constexpr int SMALL_PLAN_TOKENS = 448;
 
 template <class C>
 hipError_t launch_cfg(const bf16_t* A, const bf16_t* W0, const bf16_t* W1, const GemmArgs& a,
@@ -340,16 +346,12 @@ GemmPlan plan_gemm(int T) {
     p.variant = 0;
     p.bm_gu = GuTiny::BM;
     p.bm_dn = DnTiny::BM;
-  } else if (T <= 640) {
+  } else if (T <= SMALL_PLAN_TOKENS) {
     p.variant = 1;
     p.bm_gu = GuSmall::BM;
     p.bm_dn = DnSmall::BM;
-  } else if (T <= LARGE_TOKENS) {
-    p.variant = 2;
-    p.bm_gu = GuMedium::BM;
-    p.bm_dn = DnMedium::BM;
   } else {
-    p.variant = 3;
+    p.variant = 2;
     p.bm_gu = GuLarge::BM;
     p.bm_dn = DnLarge::BM;
   }
@@ -361,14 +363,12 @@ hipError_t launch_gateup(const GemmArgs& a, const GemmPlan& p, hipStream_t strea
     switch (p.variant) {
       case 0: return launch_cfg<SavingGU<GuTiny>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
       case 1: return launch_cfg<SavingGU<GuSmall>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
-      case 2: return launch_cfg<SavingGU<GuMedium>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
       default: return launch_cfg<SavingGU<GuLarge>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
     }
   }
   switch (p.variant) {
     case 0: return launch_cfg<GuTiny>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
     case 1: return launch_cfg<GuSmall>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
-    case 2: return launch_cfg<GuMedium>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
     default: return launch_cfg<GuLarge>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
   }
 }
@@ -377,7 +377,6 @@ hipError_t launch_down(const GemmArgs& a, const GemmPlan& p, hipStream_t stream)
   switch (p.variant) {
     case 0: return launch_cfg<DnTiny>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
     case 1: return launch_cfg<DnSmall>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
-    case 2: return launch_cfg<DnMedium>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
     default: return launch_cfg<DnLarge>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
   }
 }

@@ -78,7 +78,6 @@ struct GemmPlan {
 GemmPlan plan_gemm(int T);
 int max_row_tiles(int T, int bm);
 constexpr int MIN_TILE_ROWS = 32;   // smallest row tile of any plan (sizes the tile lists)
-constexpr int LARGE_TOKENS = 2048;  // above this the grouped GEMMs use 256-row tiles
 
 struct GemmArgs {
   int T;
