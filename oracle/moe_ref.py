@@ -36,6 +36,13 @@ Readings taken where the pages are silent or disagree:
     -inf before the softmax ([X] section 5), so their probability, count and
     share of the load-balancing term are 0 and lse runs over the kept experts;
     at least k experts must be kept;
+  * expert choice ([P] 4.1.4 names it, without its rules): the plainest reading
+    consistent with the layer is taken. The same router and 64-way softmax;
+    capacity C = ceil(k*T/E) tokens per expert (token choice's k*T pairs shared
+    equally); each expert takes its C most probable tokens, equal
+    probabilities to the lower token id; a token sums p[t,e] * Expert_e over
+    the experts that took it (zero to E of them); z-loss as for token choice,
+    load-balancing term with f_e = C / (k*T);
   * RMSNorm of the stack uses weight 1 and eps 1e-5 and its output is rounded
     to bf16 (round to nearest even), the type the layer takes.
 
@@ -230,6 +237,64 @@ def moe_layer_ref(x, w_router, w_gate, w_up, w_down, k=8, forced_ids=None,
     if keep_y:
         r["y"] = y
     return r
+
+
+# --------------------------------------------------------------- expert choice
+
+
+def expert_capacity(T, k=8, E=64):
+    """Tokens per expert under expert choice: the pair budget of token choice, k*T, shared
+    equally by the E experts and rounded up, ceil(k*T/E)."""
+    return -(-k * T // E)
+
+
+def expert_choice_select(p, C):
+    """Each expert takes the C tokens with the largest probability p[:, e]; equal
+    probabilities go to the lower token id. Returns chosen [E,C] (ascending token ids) and the
+    gap between the C-th and (C+1)-th sorted probability of each expert (inf when C >= T)."""
+    T, E = p.shape
+    chosen = np.zeros((E, C), dtype=np.int64)
+    gap = np.full(E, np.inf)
+    tok = np.arange(T)
+    for e in range(E):
+        order = np.lexsort((tok, -p[:, e]))                 # primary key: -p
+        chosen[e] = np.sort(order[:C])
+        if C < T:
+            gap[e] = p[order[C - 1], e] - p[order[C], e] if C > 0 else np.inf
+    return chosen, gap
+
+
+def expert_choice_layer_ref(x, w_router, w_gate, w_up, w_down, k=8, forced_chosen=None):
+    """The layer with expert-choice routing ([P] 4.1.4 names it as the alternative to token
+    choice; the steps here are the plainest reading, as in the module docstring of the GPU
+    path): the same router and 64-way softmax ([G] item 1), then every expert takes its
+    C = ceil(k*T/E) most probable tokens, and each token sums p[t,e] * Expert_e(x_t) over the
+    experts that took it. Losses: z as for token choice; the load-balancing term with f_e the
+    expert's share of the k*T pairs. forced_chosen [E,C] replaces the selection (near ties).
+
+    Returns dict(out, chosen [E,C], weights [E,C], token_counts [T], p_all, lse, gap, aux, z)."""
+    x64 = to_f64(x)
+    T, D = x64.shape
+    E = np.asarray(w_router).shape[0]
+    C = expert_capacity(T, k, E)
+    logits = router_logits(x64, w_router) if T else np.zeros((0, E))
+    lse, p = softmax_all(logits) if T else (np.zeros(0), np.zeros((0, E)))
+    if forced_chosen is None:
+        chosen, gap = expert_choice_select(p, C) if T else (np.zeros((E, 0), np.int64), np.full(E, np.inf))
+    else:
+        chosen = np.asarray(forced_chosen, dtype=np.int64).reshape(E, C)
+        gap = np.full(E, np.nan)
+    weights = np.take_along_axis(p.T, chosen, axis=1) if T else np.zeros((E, 0))
+    out = np.zeros((T, D))
+    for e in range(E):
+        if C:
+            y = swiglu_expert(x64[chosen[e]], w_gate[e], w_up[e], w_down[e])
+            np.add.at(out, chosen[e], weights[e][:, None] * y)
+    token_counts = np.bincount(chosen.ravel(), minlength=T) if T else np.zeros(0, np.int64)
+    counts = np.full(E, C)
+    aux, z = losses(p, counts, lse, k) if T else (0.0, 0.0)
+    return dict(out=out, chosen=chosen, weights=weights, token_counts=token_counts, p_all=p, lse=lse,
+                gap=gap, aux=aux, z=z, capacity=C)
 
 
 # -------------------------------------------------------------------- backward

@@ -451,3 +451,67 @@ def test_backward_zero_upstream_is_zero_and_unused_experts_get_none():
     unused = b["fwd"]["counts"] == 0
     assert unused.any()
     assert not np.any(b["dw_gate"][unused]) and not np.any(b["dw_down"][unused])
+
+
+# ---------------------------------------------------------------- expert choice
+
+
+def test_expert_choice_selection_brute_force_and_ties():
+    rng = np.random.default_rng(12)
+    p = rng.random((50, 8))
+    chosen, gap = oracle.expert_choice_select(p, 7)
+    for e in range(8):
+        # brute force: the 7 largest of column e, by a full sort of (value, -token) pairs
+        pairs = sorted(((p[t, e], -t) for t in range(50)), reverse=True)[:7]
+        assert sorted(-t for _, t in pairs) == chosen[e].tolist()
+        srt = np.sort(p[:, e])[::-1]
+        assert gap[e] == srt[6] - srt[7]
+    # equal probabilities: the lower token ids win
+    q = np.zeros((10, 2))
+    q[:, 1] = [0.5, 0.9, 0.5, 0.5, 0.1, 0.9, 0.5, 0.2, 0.5, 0.3]
+    c, _ = oracle.expert_choice_select(q, 4)
+    assert c[0].tolist() == [0, 1, 2, 3]
+    assert c[1].tolist() == [0, 1, 2, 5]
+
+
+def test_expert_choice_layer_against_dense_masked_experts():
+    T, D, F, E, k = 24, 32, 16, 16, 4
+    L = inputs.host_layer(T, dims=(D, F, E), w_std=0.3)
+    r = oracle.expert_choice_layer_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], k)
+    C = r["capacity"]
+    assert C == 6 and r["chosen"].shape == (E, C)
+    assert r["token_counts"].sum() == E * C
+    # dense: every expert on every token, weighted by p where the expert took the token
+    x = oracle.to_f64(L["x"])
+    mask = np.zeros((T, E))
+    for e in range(E):
+        mask[r["chosen"][e], e] = 1.0
+    dense = np.zeros((T, D))
+    for e in range(E):
+        dense += (mask[:, e] * r["p_all"][:, e])[:, None] * oracle.swiglu_expert(x, L["w_gate"][e], L["w_up"][e],
+                                                                                   L["w_down"][e])
+    np.testing.assert_allclose(r["out"], dense, rtol=1e-12, atol=1e-14)
+    # each expert's selection holds its C largest probabilities
+    for e in range(E):
+        rest = np.setdiff1d(np.arange(T), r["chosen"][e])
+        assert r["p_all"][r["chosen"][e], e].min() >= r["p_all"][rest, e].max()
+
+
+def test_expert_choice_closed_forms():
+    T, D, F, E, k = 20, 16, 8, 8, 2
+    L = inputs.host_layer(T, dims=(D, F, E), w_std=0.3)
+    L["w_router"][:] = 0      # every p = 1/E: every expert takes tokens 0 .. C-1
+    r = oracle.expert_choice_layer_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], k)
+    C = oracle.expert_capacity(T, k, E)
+    assert C == 5 and (r["chosen"] == np.arange(C)).all()
+    assert (r["token_counts"][:C] == E).all() and (r["token_counts"][C:] == 0).all()
+    assert not np.any(r["out"][C:])
+    # tokens 0..C-1 get the plain average of all experts
+    x = oracle.to_f64(L["x"])[:C]
+    avg = sum(oracle.swiglu_expert(x, L["w_gate"][e], L["w_up"][e], L["w_down"][e]) for e in range(E)) / E
+    np.testing.assert_allclose(r["out"][:C], avg, rtol=1e-12)
+    assert r["z"] == pytest.approx(0.001 * math.log(E) ** 2, rel=1e-13)
+    assert r["aux"] == pytest.approx(0.01 * E * E * (C / (k * T)) / E, rel=1e-13)
+    # one token: every expert takes it
+    r1 = oracle.expert_choice_layer_ref(L["x"][:1], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], k)
+    assert r1["capacity"] == 1 and r1["token_counts"].tolist() == [E]
