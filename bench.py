@@ -241,6 +241,55 @@ def measure_backward(workload, steps, warmup, seed=0):
             "note": "gradients of x and all weights; the forward recompute inside is timed, not counted"}
 
 
+def measure_expert_choice(workload, steps, warmup, seed=0):
+    """Wall-clock time of one expert-choice layer forward (olmoe_moe_forward_expert_choice) per
+    call, with the per-stage split from a separate event-bracketed pass."""
+    import torch
+    from sparse_mixture_experts_expert_amd import binding, inputs
+
+    wl = inputs.WORKLOADS[workload]
+    T = wl.tokens
+    d = inputs.device_workload(workload, seed=seed)
+    sets = [d] + [inputs.device_weights(seed, workload, layer=r, skew=wl.skew) for r in range(1, N_WEIGHT_SETS)]
+    C = binding.ec_capacity(T)
+    dev = "cuda"
+    outs = dict(out=torch.empty((T, D), dtype=torch.bfloat16, device=dev),
+                choice_tokens=torch.empty((E, C), dtype=torch.int32, device=dev),
+                choice_probs=torch.empty((E, C), dtype=torch.float32, device=dev),
+                token_counts=torch.empty(T, dtype=torch.int32, device=dev),
+                aux_loss=torch.empty(1, dtype=torch.float32, device=dev),
+                z_loss=torch.empty(1, dtype=torch.float32, device=dev),
+                workspace=torch.empty(binding.ec_workspace_bytes(T), dtype=torch.uint8, device=dev))
+    it = [0]
+
+    def step():
+        w = sets[it[0] % N_WEIGHT_SETS]
+        it[0] += 1
+        binding.moe_forward_expert_choice(d["x"], w["w_router"], w["w_gate"], w["w_up"], w["w_down"], **outs)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    binding.timing_enable(True)
+    for _ in range(max(3, steps // 5)):
+        step()
+    torch.cuda.synchronize()
+    stage_sum, calls = binding.timing_read()
+    binding.timing_enable(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    rows = E * C
+    flop = 2 * T * D * E + rows * 3 * 2 * D * F
+    return {"workload": workload, "tokens": T, "capacity": C, "ms_per_step": round(sec * 1e3, 5),
+            "tokens_per_s": round(T / sec, 1), "tflops": round(flop / sec / 1e12, 2),
+            "stage_ms": {k: round(v / calls, 5) for k, v in stage_sum.items()},
+            "untouched_tokens": int((outs["token_counts"] == 0).sum().item()),
+            "max_experts_per_token": int(outs["token_counts"].max().item())}
+
+
 def cpu_baseline(d, workload, budget_s=20.0):
     """The float64 oracle, as it stands, on a bounded sample of the workload."""
     import numpy as np
@@ -417,6 +466,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
+    ap.add_argument("--no-expert-choice", action="store_true", help="skip the expert-choice forward timing")
     ap.add_argument("--copy-probe", action="store_true", help="run the counter-calibration copy and exit")
     ap.add_argument("--traffic-summary", action="store_true", help="summarise --pmc runs into profiles/")
     ap.add_argument("--stats-summary", metavar="DIR", dest="stats_dir", help="summarise a --stats run")
@@ -491,6 +541,10 @@ def main():
         wls = [args.workload] + ([] if args.no_secondary or args.workload == "prefill-4096" else ["prefill-4096"])
         torch.cuda.empty_cache()
         line["backward"] = [measure_backward(w, max(5, args.steps // 5), 2, args.seed) for w in wls]
+    if not args.no_expert_choice and wl_layers_of(args.workload) == 1:
+        wls = [args.workload] + ([] if args.no_secondary or args.workload == "prefill-4096" else ["prefill-4096"])
+        torch.cuda.empty_cache()
+        line["expert_choice"] = [measure_expert_choice(w, args.steps, min(args.warmup, 5), args.seed) for w in wls]
     if not args.no_cpu:
         if d is None:
             from sparse_mixture_experts_expert_amd import inputs

@@ -47,7 +47,7 @@ extern "C" {
 #define OLMOE_API
 #endif
 
-#define OLMOE_ABI_VERSION 3
+#define OLMOE_ABI_VERSION 4
 
 #define OLMOE_D 2048 /* hidden size */
 #define OLMOE_F 1024 /* expert width (SwiGLU intermediate size) */
@@ -172,6 +172,41 @@ OLMOE_API olmoe_status_t olmoe_moe_forward_residual(const void* x, const float* 
                                           int32_t* expert_counts, float* aux_loss, float* z_loss,
                                           uint32_t route_flags, uint64_t keep_mask,
                                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Expert-choice routing: the experts choose their tokens ("OLMoE: Open
+ * Mixture-of-Experts Language Models", section 4.1.4, where it is compared with
+ * token choice; the page gives no formulas, and this is the plainest reading
+ * built from the token-choice layer's steps, "OLMoE Guide", items 1-3):
+ *   p[t,e]  the same 64-way softmax of the router logits (fp32)
+ *   C       = ceil(8T / 64) tokens per expert (the 8T pairs of token choice
+ *             shared equally)
+ *   S_e     the C tokens with the largest p[t,e]; equal probabilities go to
+ *           the lower token id (selection on the fp32 probabilities)
+ *   out[t]  = sum over the experts e with t in S_e of p[t,e] * Expert_e(x_t),
+ *             accumulated in fp32 in ascending e; a token no expert took gets 0
+ *
+ *   x, W_*, out   as olmoe_moe_forward;  0 <= T <= OLMOE_EC_MAX_TOKENS
+ *   choice_tokens int32 [64,C] or NULL  row e: the tokens of S_e, ascending
+ *   choice_probs  fp32 [64,C] or NULL   p[t,e] of those tokens
+ *   token_counts  int32 [T] or NULL     experts that took each token (0..64,
+ *                                       sum 64C)
+ *   aux_loss      fp32 [1] or NULL      0.01 * 64 * sum_e f_e P_e with
+ *                                       f_e = C / (8T), P_e = mean_t p[t,e]
+ *   z_loss        fp32 [1] or NULL      0.001 * mean_t lse_t^2
+ *   workspace     at least olmoe_moe_ec_workspace_bytes(T) bytes, 256-byte
+ *                 aligned; contents on entry are ignored
+ * The expert GEMMs and their precisions are those of olmoe_moe_forward.
+ * T == 0 is valid (the losses are set to 0).
+ * Errors: as olmoe_moe_forward (EINVAL for T > OLMOE_EC_MAX_TOKENS, and for any
+ * output overlapping an input, another output or the workspace). */
+#define OLMOE_EC_MAX_TOKENS ((int64_t)1 << 16) /* the selection holds a column per workgroup in registers */
+OLMOE_API size_t olmoe_moe_ec_workspace_bytes(int64_t T);   /* 0 for T out of range; host only */
+OLMOE_API olmoe_status_t olmoe_moe_forward_expert_choice(const void* x, const float* W_router,
+                                               const void* W_gate, const void* W_up,
+                                               const void* W_down, int64_t T, void* out,
+                                               int32_t* choice_tokens, float* choice_probs,
+                                               int32_t* token_counts, float* aux_loss, float* z_loss,
+                                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* RMSNorm of the residual stream with unit weight, rounded to the layer's
  * input type: x_out[t] = bf16(h[t] / sqrt(mean_k h[t,k]^2 + eps)), computed in

@@ -16,6 +16,7 @@ D, F, E, K = 2048, 1024, 64, 8
 OK, EINVAL, EWORKSPACE, EHIP, ENODEVICE = range(5)
 ROUTE_RENORMALIZE = 1
 KEEP_ALL = (1 << 64) - 1
+EC_MAX_TOKENS = 1 << 16
 STATUS_NAMES = {0: "OLMOE_OK", 1: "OLMOE_EINVAL", 2: "OLMOE_EWORKSPACE", 3: "OLMOE_EHIP", 4: "OLMOE_ENODEVICE"}
 
 _lib = None
@@ -58,6 +59,10 @@ def lib() -> ctypes.CDLL:
     L.olmoe_moe_backward.restype = i32
     L.olmoe_moe_backward.argtypes = [vp, vp, vp, vp, vp, i64, vp, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp,
                                      vp, vp, sz, vp]
+    L.olmoe_moe_ec_workspace_bytes.restype = sz
+    L.olmoe_moe_ec_workspace_bytes.argtypes = [i64]
+    L.olmoe_moe_forward_expert_choice.restype = i32
+    L.olmoe_moe_forward_expert_choice.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.olmoe_rmsnorm_bf16.restype = i32
     L.olmoe_rmsnorm_bf16.argtypes = [vp, ctypes.c_float, i64, vp, vp]
     L.olmoe_residual_add.restype = i32
@@ -205,6 +210,51 @@ def moe_backward(x, w_router, w_gate, w_up, w_down, dout, *, g_aux: float = 1.0,
         _ptr(dw_down), _ptr(workspace), workspace.numel(), _stream(stream)))
     return {"dx": dx, "dw_router": dw_router, "dw_gate": dw_gate, "dw_up": dw_up, "dw_down": dw_down,
             "workspace": workspace}
+
+
+def ec_capacity(T: int) -> int:
+    """Tokens each expert takes under expert choice: ceil(8T / 64)."""
+    return -(-K * int(T) // E)
+
+
+def ec_workspace_bytes(T: int) -> int:
+    return int(lib().olmoe_moe_ec_workspace_bytes(int(T)))
+
+
+def moe_forward_expert_choice(x, w_router, w_gate, w_up, w_down, *, out=None, choice_tokens=None,
+                              choice_probs=None, token_counts=None, aux_loss=None, z_loss=None,
+                              workspace=None, stream=None, want_routing=True):
+    """One MoE layer with expert-choice routing (olmoe_moe_forward_expert_choice): every
+    expert takes its C = ceil(8T/64) most probable tokens.  Tensors as moe_forward; the
+    routing outputs are choice_tokens int32 [64,C] (ascending per expert), choice_probs
+    fp32 [64,C], token_counts int32 [T], aux_loss / z_loss fp32 [1], allocated when missing
+    (only when want_routing).  Returns a dict of the output tensors."""
+    import torch
+    T = x.shape[0]
+    dev = x.device
+    C = ec_capacity(T)
+    _need(x, "x", torch.bfloat16, (T, D))
+    _need(w_router, "w_router", torch.float32, (E, D))
+    _need(w_gate, "w_gate", torch.bfloat16, (E, F, D))
+    _need(w_up, "w_up", torch.bfloat16, (E, F, D))
+    _need(w_down, "w_down", torch.bfloat16, (E, D, F))
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    if want_routing:
+        i32, f32 = torch.int32, torch.float32
+        choice_tokens = choice_tokens if choice_tokens is not None else torch.empty((E, C), dtype=i32, device=dev)
+        choice_probs = choice_probs if choice_probs is not None else torch.empty((E, C), dtype=f32, device=dev)
+        token_counts = token_counts if token_counts is not None else torch.empty(T, dtype=i32, device=dev)
+        aux_loss = aux_loss if aux_loss is not None else torch.empty(1, dtype=f32, device=dev)
+        z_loss = z_loss if z_loss is not None else torch.empty(1, dtype=f32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(ec_workspace_bytes(T), 256), dtype=torch.uint8, device=dev)
+    _check(lib().olmoe_moe_forward_expert_choice(
+        _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), int(T), _ptr(out),
+        _ptr(choice_tokens), _ptr(choice_probs), _ptr(token_counts), _ptr(aux_loss), _ptr(z_loss),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return {"out": out, "choice_tokens": choice_tokens, "choice_probs": choice_probs,
+            "token_counts": token_counts, "aux_loss": aux_loss, "z_loss": z_loss, "workspace": workspace}
 
 
 def dispatch_tables(workspace, T: int):

@@ -109,6 +109,31 @@ BwdLayout make_bwd_layout(int64_t T) {
   return B;
 }
 
+// expert-choice workspace: the forward layout for 8C "tokens" (64C rows, every expert C of
+// them; C = ceil(8T / 64) >= T / 8, so all row buffers and tile lists fit), then its own tables
+struct EcLayout {
+  Layout f;
+  size_t pT, lse, inv_ec, row_w, total;
+};
+EcLayout make_ec_layout(int64_t T) {
+  EcLayout L{};
+  const int64_t C = ec_capacity(static_cast<int>(T));
+  L.f = make_layout(8 * C);
+  size_t off = L.f.total;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~size_t(255);
+    return o;
+  };
+  const size_t t = static_cast<size_t>(T);
+  L.pT = take(t * OLMOE_E * 4);
+  L.lse = take(t * 4);
+  L.inv_ec = take(t * OLMOE_E * 4);
+  L.row_w = take(static_cast<size_t>(C) * OLMOE_E * 4);
+  L.total = off;
+  return L;
+}
+
 bool misaligned(const void* p, size_t a = 16) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -511,6 +536,127 @@ olmoe_status_t olmoe_moe_backward(const void* x, const float* W_router, const vo
   if (he == hipSuccess) he = launch_wgrad(wgu, s);
   if (he == hipSuccess) he = launch_bwd_finish(ba, s);
   if (he != hipSuccess) return fail(OLMOE_EHIP, "weight-gradient launch: %s", hipGetErrorString(he));
+  return ok();
+}
+
+size_t olmoe_moe_ec_workspace_bytes(int64_t T) {
+  if (T < 0 || T > OLMOE_EC_MAX_TOKENS) return 0;
+  return make_ec_layout(T).total;
+}
+
+olmoe_status_t olmoe_moe_forward_expert_choice(const void* x, const float* W_router, const void* W_gate,
+                                               const void* W_up, const void* W_down, int64_t T, void* out,
+                                               int32_t* choice_tokens, float* choice_probs,
+                                               int32_t* token_counts, float* aux_loss, float* z_loss,
+                                               void* workspace, size_t workspace_bytes, void* stream) {
+  // ---- host-side checks; nothing is enqueued unless all pass
+  if (T < 0 || T > OLMOE_EC_MAX_TOKENS)
+    return fail(OLMOE_EINVAL, "T=%lld out of range [0, %lld]", (long long)T, (long long)OLMOE_EC_MAX_TOKENS);
+  if (!W_router || !W_gate || !W_up || !W_down) return fail(OLMOE_EINVAL, "a weight pointer is NULL");
+  if (T > 0 && (!x || !out)) return fail(OLMOE_EINVAL, "x or out is NULL");
+  const void* ptrs[] = {x, W_router, W_gate, W_up, W_down, out, choice_tokens, choice_probs, token_counts};
+  const char* names[] = {"x", "W_router", "W_gate", "W_up", "W_down", "out", "choice_tokens", "choice_probs",
+                         "token_counts"};
+  for (int i = 0; i < 9; ++i)
+    if (ptrs[i] && misaligned(ptrs[i])) return fail(OLMOE_EINVAL, "%s is not 16-byte aligned", names[i]);
+  if ((aux_loss && misaligned(aux_loss, 4)) || (z_loss && misaligned(z_loss, 4)))
+    return fail(OLMOE_EINVAL, "aux_loss / z_loss not 4-byte aligned");
+  const int Ti = static_cast<int>(T);
+  const int C = ec_capacity(Ti);
+  const size_t act = static_cast<size_t>(T) * OLMOE_D * 2;
+  const size_t wexp = static_cast<size_t>(OLMOE_E) * OLMOE_F * OLMOE_D * 2;
+  const size_t wr_bytes = (size_t)OLMOE_E * OLMOE_D * 4;
+  const size_t choice_n = static_cast<size_t>(C) * OLMOE_E * 4;
+  const void* ins[] = {x, W_router, W_gate, W_up, W_down};
+  const size_t in_n[] = {act, wr_bytes, wexp, wexp, wexp};
+  void* outs[] = {out, choice_tokens, choice_probs, token_counts, aux_loss, z_loss};
+  const size_t out_n[] = {act, choice_n, choice_n, static_cast<size_t>(T) * 4, 4, 4};
+  const EcLayout L = make_ec_layout(T);
+  if (!workspace) return fail(OLMOE_EWORKSPACE, "workspace is NULL");
+  if (misaligned(workspace, 256)) return fail(OLMOE_EINVAL, "workspace is not 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(OLMOE_EWORKSPACE, "workspace has %zu bytes, %zu needed for T=%lld", workspace_bytes, L.total,
+                (long long)T);
+  for (int o = 0; o < 6; ++o) {
+    for (int i = 0; i < 5; ++i)
+      if (overlaps(outs[o], out_n[o], ins[i], in_n[i])) return fail(OLMOE_EINVAL, "an output overlaps an input");
+    for (int q = o + 1; q < 6; ++q)
+      if (overlaps(outs[o], out_n[o], outs[q], out_n[q])) return fail(OLMOE_EINVAL, "two outputs overlap");
+    if (overlaps(outs[o], out_n[o], workspace, L.total)) return fail(OLMOE_EINVAL, "an output overlaps the workspace");
+  }
+  olmoe_status_t st = check_device();
+  if (st != OLMOE_OK) return st;
+
+  // ---- launches: router -> softmax (stage "router"), choose + losses ("dispatch"), the grouped
+  // GEMMs on 64 blocks of C rows, combine
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int Teff = 8 * C;   // the GEMMs see 8*Teff = 64C rows, C per expert
+  const GemmPlan plan = plan_gemm(Teff);
+  StageRecorder rec(s);
+  EcArgs ea{};
+  ea.T = Ti;
+  ea.C = C;
+  ea.partial = reinterpret_cast<const float2*>(ws + L.f.partial);
+  ea.pT = reinterpret_cast<float*>(ws + L.pT);
+  ea.lse = reinterpret_cast<float*>(ws + L.lse);
+  ea.inv_ec = reinterpret_cast<int32_t*>(ws + L.inv_ec);
+  ea.perm = reinterpret_cast<int32_t*>(ws + L.f.perm);
+  ea.row_w = reinterpret_cast<float*>(ws + L.row_w);
+  ea.blk_psum = reinterpret_cast<float*>(ws + L.f.blk_psum);   // ceil(8C/16) >= ceil(T/16) blocks
+  ea.blk_lse2 = reinterpret_cast<float*>(ws + L.f.blk_lse2);
+  ea.offsets = reinterpret_cast<int32_t*>(ws + L.f.offsets);
+  ea.tile_prefix_gu = reinterpret_cast<int32_t*>(ws + L.f.tp_gu);
+  ea.tiles_gu = reinterpret_cast<int2*>(ws + L.f.tiles_gu);
+  ea.bm_gu = plan.bm_gu;
+  ea.tile_prefix_dn = reinterpret_cast<int32_t*>(ws + L.f.tp_dn);
+  ea.tiles_dn = reinterpret_cast<int2*>(ws + L.f.tiles_dn);
+  ea.bm_dn = plan.bm_dn;
+  ea.choice_tokens = choice_tokens;
+  ea.choice_probs = choice_probs;
+  ea.y = reinterpret_cast<const uint16_t*>(ws + L.f.y);
+  ea.out = static_cast<uint16_t*>(out);
+  ea.token_counts = token_counts;
+  ea.aux_loss = aux_loss;
+  ea.z_loss = z_loss;
+  hipError_t he = hipSuccess;
+  if (Ti > 0) {
+    RouterArgs ra{static_cast<const uint16_t*>(x), W_router, Ti, reinterpret_cast<float2*>(ws + L.f.partial),
+                  reinterpret_cast<uint16_t*>(ws + L.f.planes)};
+    he = launch_router_partial(ra, s);
+    if (he == hipSuccess) he = launch_ec_softmax(ea, s);
+    if (he != hipSuccess) return fail(OLMOE_EHIP, "router launch: %s", hipGetErrorString(he));
+  }
+  rec.mark();
+  he = launch_ec_choose(ea, s);   // T == 0: only the losses (0)
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "expert-choice selection launch: %s", hipGetErrorString(he));
+  rec.mark();
+  if (Ti == 0) {
+    rec.finish();
+    return ok();
+  }
+  GemmArgs ga{Teff,
+              static_cast<const uint16_t*>(x),
+              static_cast<const uint16_t*>(W_gate),
+              static_cast<const uint16_t*>(W_up),
+              static_cast<const uint16_t*>(W_down),
+              reinterpret_cast<const int32_t*>(ws + L.f.perm),
+              reinterpret_cast<const int32_t*>(ws + L.f.offsets),
+              reinterpret_cast<const int32_t*>(ws + L.f.tp_gu),
+              reinterpret_cast<const int32_t*>(ws + L.f.tp_dn),
+              reinterpret_cast<const int2*>(ws + L.f.tiles_gu),
+              reinterpret_cast<const int2*>(ws + L.f.tiles_dn),
+              reinterpret_cast<uint16_t*>(ws + L.f.h),
+              reinterpret_cast<uint16_t*>(ws + L.f.y)};
+  he = launch_gateup(ga, plan, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "gate/up launch: %s", hipGetErrorString(he));
+  rec.mark();
+  he = launch_down(ga, plan, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "down launch: %s", hipGetErrorString(he));
+  rec.mark();
+  he = launch_ec_combine(ea, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "combine launch: %s", hipGetErrorString(he));
+  rec.mark();
   return ok();
 }
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.hpp"
+
 namespace olmoe {
 
 struct RouterArgs {
@@ -109,6 +111,41 @@ struct CombineArgs {
   float eps;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- expert choice
+
+constexpr int EC_MAX_TOKENS = static_cast<int>(OLMOE_EC_MAX_TOKENS);
+constexpr int ec_capacity(int T) { return (K * T + E - 1) / E; }   // ceil(8T / 64) tokens per expert
+
+struct EcArgs {
+  int T, C;
+  const float2* partial;      // [S,T,64] router partials
+  float* pT;                  // fp32 [64,T] probabilities, one row per expert
+  float* lse;                 // fp32 [T]
+  int32_t* inv_ec;            // [T,64] row holding (t, e), or -1
+  int32_t* perm;              // [64C] token of each row (expert e owns rows e*C .. e*C+C-1)
+  float* row_w;               // [64C] routing weight p[t,e] of each row
+  float* blk_psum;            // [ceil(T/16),64] sum of p[t,e] over each 16-token block (token order)
+  float* blk_lse2;            // [ceil(T/16)] sum of lse^2 over each block
+  int32_t* offsets;           // [65] e*C
+  int32_t* tile_prefix_gu;    // [65]; entry 64 holds the tile count
+  int2* tiles_gu;
+  int bm_gu;
+  int32_t* tile_prefix_dn;
+  int2* tiles_dn;
+  int bm_dn;
+  int32_t* choice_tokens;     // [64,C] or null
+  float* choice_probs;        // [64,C] or null
+  const uint16_t* y;          // fp16 [64C,2048] expert outputs
+  uint16_t* out;              // bf16 [T,2048]
+  int32_t* token_counts;      // [T] or null
+  float* aux_loss;            // [1] or null
+  float* z_loss;              // [1] or null
+};
+hipError_t launch_ec_softmax(const EcArgs& a, hipStream_t stream);   // p (transposed), lse, inv_ec = -1
+// top-C per expert and the tile lists (one workgroup per expert), aux and z (one more)
+hipError_t launch_ec_choose(const EcArgs& a, hipStream_t stream);
+hipError_t launch_ec_combine(const EcArgs& a, hipStream_t stream);   // weighted sum per token
 
 // ---------------------------------------------------------------- backward pass
 

@@ -116,3 +116,50 @@ def check_out(out_gpu, out_ref, label=""):
 def check_losses(aux_gpu, z_gpu, aux_ref, z_ref, label=""):
     assert abs(aux_gpu - aux_ref) <= LOSS_RTOL * abs(aux_ref) + 1e-12, f"{label}: aux {aux_gpu} vs {aux_ref}"
     assert abs(z_gpu - z_ref) <= LOSS_RTOL * abs(z_ref) + 1e-12, f"{label}: z {z_gpu} vs {z_ref}"
+
+
+def ec_tie_tol(p_c, logits):
+    """Near-tie width for an expert's C-th probability p_c: twice the bar on one
+    probability's relative error (fp32 logits of magnitude L enter p relatively)."""
+    finite = np.where(np.isfinite(logits), np.abs(logits), 0.0)
+    return 2.0 * (PROB_RTOL + 4 * ulp_f32(finite.max())) * p_c
+
+
+def check_expert_choice(tokens_gpu, probs_gpu, counts_gpu, p_all, logits, label=""):
+    """Expert-choice selection against the oracle's probabilities p_all [T,64]
+    (fp64).  Every expert's row must hold C distinct ascending token ids;
+    where the oracle's C-th and (C+1)-th probabilities of the expert are further
+    apart than the tie width the set must equal the oracle's exactly, otherwise
+    it must be a valid top-C within that width.  choice_probs within the
+    probability bar, token_counts exactly the GPU selection's multiplicities.
+    Returns the number of near-tie experts."""
+    tok = np.asarray(tokens_gpu, np.int64)
+    E_, C = tok.shape
+    T = p_all.shape[0]
+    assert C == oracle.expert_capacity(T, 8, E_), label
+    if C == 0:
+        return 0
+    assert ((tok >= 0) & (tok < T)).all(), label
+    assert (np.diff(tok, axis=1) > 0).all(), f"{label}: tokens not strictly ascending per expert"
+    ref_chosen, gap = oracle.expert_choice_select(p_all, C)
+    n_tie = 0
+    for e in range(E_):
+        col = p_all[:, e]
+        p_c = np.sort(col)[::-1][C - 1]
+        tol = ec_tie_tol(p_c, logits)
+        if gap[e] >= tol:
+            np.testing.assert_array_equal(tok[e], ref_chosen[e], err_msg=f"{label}: expert {e} chosen set")
+        else:
+            n_tie += 1
+            mask = np.zeros(T, bool)
+            mask[tok[e]] = True
+            if (~mask).any():
+                assert col[mask].min() >= col[~mask].max() - tol, f"{label}: expert {e} invalid near-tie choice"
+    p_ref = np.take_along_axis(p_all.T, tok, axis=1)
+    rel = np.abs(np.asarray(probs_gpu, np.float64) - p_ref) / p_ref
+    finite = np.where(np.isfinite(logits), np.abs(logits), 0.0)
+    bar = PROB_RTOL + 4 * ulp_f32(finite.max(1))[tok]
+    assert (rel <= bar).all(), f"{label}: choice_probs rel err {rel.max():.3e}"
+    np.testing.assert_array_equal(np.asarray(counts_gpu), np.bincount(tok.ravel(), minlength=T),
+                                  err_msg=f"{label}: token_counts")
+    return n_tie

@@ -147,6 +147,35 @@ def test_backward_checks_arguments_first(L):
     assert bwd(dwr=(1 << 32) + 64) == binding.EINVAL           # dW_router over W_gate
 
 
+def test_expert_choice_checks_arguments_first(L):
+    # every call here fails validation, so nothing reaches a device (fake pointers)
+    vp = ctypes.c_void_p
+    T = 100
+    C = binding.ec_capacity(T)
+    assert C == 13 and binding.ec_capacity(0) == 0 and binding.ec_capacity(1) == 1 and binding.ec_capacity(64) == 8
+    wsb = binding.ec_workspace_bytes(T)
+    # the GEMM row buffers hold 64C rows (C per expert), plus per-token tables
+    assert wsb >= 64 * C * (2048 + 1024) * 2 + T * 64 * 8
+    assert binding.ec_workspace_bytes(-1) == 0
+    assert binding.ec_workspace_bytes(binding.EC_MAX_TOKENS) > 0
+    assert binding.ec_workspace_bytes(binding.EC_MAX_TOKENS + 1) == 0
+
+    def ec(out=4 << 20, toks=5 << 20, probs=6 << 20, counts=7 << 20, ws=8 << 36, wsb=wsb, t=T, x=1 << 20, wg=1 << 32):
+        return L.olmoe_moe_forward_expert_choice(vp(x), vp(2 << 20), vp(wg), vp(2 << 32), vp(3 << 32), t, vp(out),
+                                                 vp(toks), vp(probs), vp(counts), None, None, vp(ws), wsb, None)
+    assert ec(t=binding.EC_MAX_TOKENS + 1) == binding.EINVAL
+    assert "out of range" in L.olmoe_last_error().decode()
+    assert ec(t=-1) == binding.EINVAL
+    assert ec(wg=0) == binding.EINVAL                          # weight NULL
+    assert ec(out=0) == binding.EINVAL                         # out NULL with T > 0
+    assert ec(toks=(5 << 20) + 4) == binding.EINVAL            # misaligned
+    assert ec(wsb=1000) == binding.EWORKSPACE
+    assert ec(ws=(8 << 36) + 16) == binding.EINVAL             # workspace alignment
+    assert ec(out=(1 << 20) + 4096) == binding.EINVAL          # out over x
+    assert ec(probs=(5 << 20) + 16) == binding.EINVAL          # two outputs overlap
+    assert ec(counts=(8 << 36) + 256) == binding.EINVAL        # output in the workspace
+
+
 def test_glue_entry_points_reject_bad_arguments(L):
     vp = ctypes.c_void_p
     assert L.olmoe_rmsnorm_bf16(vp(1 << 20), ctypes.c_float(0.0), 4, vp(1 << 30), None) == binding.EINVAL
