@@ -383,6 +383,73 @@ def moe_layer_backward_ref(x, w_router, w_gate, w_up, w_down, dout, g_aux=0.0, g
     return r
 
 
+def expert_choice_backward_ref(x, w_router, w_gate, w_up, w_down, dout, g_aux=0.0, g_z=0.0, k=8,
+                               forced_chosen=None, magnitudes=False):
+    """Gradients of  L = sum_t <dout_t, out_t> + g_aux * aux + g_z * z  for the expert-choice layer
+    of expert_choice_layer_ref, by the chain rule through its steps (the same router, softmax,
+    SwiGLU experts and losses as the token-choice backward: [G] items 1-3). Which tokens each
+    expert takes, and the shares f_e = C/(kT), are piecewise constant and carry no gradient.
+
+    forced_chosen fixes the selection (near ties); magnitudes=True also returns the contractions
+    over |operands| as moe_layer_backward_ref does. Returns dict(dx, dw_router, dw_gate, dw_up,
+    dw_down, dp [T,E] (gradient of the routing weight of every taken pair, 0 elsewhere, before the
+    loss terms), dlogits, fwd)."""
+    fwd = expert_choice_layer_ref(x, w_router, w_gate, w_up, w_down, k, forced_chosen=forced_chosen)
+    x64 = to_f64(x)
+    g = to_f64(dout)
+    T, D = x64.shape
+    wr = to_f64(w_router)
+    E = wr.shape[0]
+    F = np.asarray(w_gate).shape[1]
+    C = fwd["capacity"]
+    p = fwd["p_all"]
+    dx = np.zeros((T, D))
+    dw_gate = np.zeros((E, F, D))
+    dw_up = np.zeros((E, F, D))
+    dw_down = np.zeros((E, D, F))
+    dw = np.zeros((T, E))
+    mags = dict(mag_gate=np.zeros((E, F, D)), mag_up=np.zeros((E, F, D)), mag_down=np.zeros((E, D, F)),
+                mag_dx=np.zeros((T, D))) if magnitudes else None
+    for e in range(E):
+        if C == 0:
+            break
+        t = fwd["chosen"][e]                       # distinct tokens
+        X = x64[t]
+        wg, wu, wd = to_f64(w_gate[e]), to_f64(w_up[e]), to_f64(w_down[e])
+        G = X @ wg.T
+        U = X @ wu.T
+        S = silu(G)
+        H = S * U
+        go = g[t]
+        dw[t, e] = np.sum(go * (H @ wd.T), axis=1)      # out_t = sum_e p[t,e] Y_e(x_t)
+        dY = p[t, e][:, None] * go
+        dw_down[e] = dY.T @ H
+        dH = dY @ wd
+        dG = dH * U * silu_grad(G)
+        dU = dH * S
+        dw_gate[e] = dG.T @ X
+        dw_up[e] = dU.T @ X
+        dx[t] += dG @ wg + dU @ wu
+        if magnitudes:
+            mags["mag_gate"][e] = np.abs(dG).T @ np.abs(X)
+            mags["mag_up"][e] = np.abs(dU).T @ np.abs(X)
+            mags["mag_down"][e] = np.abs(dY).T @ np.abs(H)
+            mags["mag_dx"][t] += np.abs(dG) @ np.abs(wg) + np.abs(dU) @ np.abs(wu)
+    dp = dw.copy()
+    if T:
+        dp += g_aux * ALPHA * E * (C / (k * T)) / T      # aux = alpha E sum_e f_e mean_t p_te
+    dlogits = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+    if T:
+        dlogits += g_z * BETA * (2.0 * fwd["lse"] / T)[:, None] * p
+    dx += dlogits @ wr
+    r = dict(dx=dx, dw_router=dlogits.T @ x64, dw_gate=dw_gate, dw_up=dw_up, dw_down=dw_down, dp=dw,
+             dlogits=dlogits, fwd=fwd)
+    if magnitudes:
+        mags["mag_dx"] += np.abs(dlogits) @ np.abs(wr)
+        r.update(mags)
+    return r
+
+
 # ----------------------------------------------------------------- brute force
 
 

@@ -515,3 +515,74 @@ def test_expert_choice_closed_forms():
     # one token: every expert takes it
     r1 = oracle.expert_choice_layer_ref(L["x"][:1], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], k)
     assert r1["capacity"] == 1 and r1["token_counts"].tolist() == [E]
+
+
+@pytest.mark.parametrize("g_aux,g_z", [(0.0, 0.0), (1.0, 1.0), (3.0, -2.0)])
+def test_expert_choice_backward_matches_dense_autograd(g_aux, g_z):
+    # independent formulation: every expert on every token, masked by the experts' choices
+    # (torch's top-C over each expert's column of probabilities), losses in torch, autograd in fp64
+    T, D, F, E, k = 20, 32, 16, 16, 4
+    L = _small_layer(T, D, F, E, seed=13)
+    b = oracle.expert_choice_backward_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], L["dout"],
+                                          g_aux, g_z, k)
+    C = b["fwd"]["capacity"]
+    assert C == 5
+    tt = {n: torch.tensor(L[n], requires_grad=(n != "dout")) for n in L}
+    logits = tt["x"] @ tt["w_router"].T
+    p = torch.softmax(logits, -1)
+    lse = torch.logsumexp(logits, -1)
+    mask = torch.zeros(T, E, dtype=torch.float64)
+    for e in range(E):
+        mask[torch.topk(p[:, e].detach(), C).indices, e] = 1.0
+    out = torch.zeros(T, D, dtype=torch.float64)
+    for e in range(E):
+        G = tt["x"] @ tt["w_gate"][e].T
+        U = tt["x"] @ tt["w_up"][e].T
+        out = out + (mask[:, e] * p[:, e])[:, None] * ((torch.nn.functional.silu(G) * U) @ tt["w_down"][e].T)
+    aux = oracle.ALPHA * E * torch.sum((C / (k * T)) * p.mean(0))
+    z = oracle.BETA * torch.mean(lse ** 2)
+    (torch.sum(tt["dout"] * out) + g_aux * aux + g_z * z).backward()
+    for e in range(E):   # same selection
+        assert sorted(torch.nonzero(mask[:, e]).flatten().tolist()) == b["fwd"]["chosen"][e].tolist()
+    for mine, name in (("dx", "x"), ("dw_router", "w_router"), ("dw_gate", "w_gate"), ("dw_up", "w_up"),
+                       ("dw_down", "w_down")):
+        np.testing.assert_allclose(b[mine], tt[name].grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=mine)
+
+
+def test_expert_choice_backward_directional_finite_differences():
+    T, D, F, E, k = 12, 16, 8, 8, 2
+    L = _small_layer(T, D, F, E, seed=14)
+    g_aux, g_z = 2.0, 5.0
+    b = oracle.expert_choice_backward_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], L["dout"],
+                                          g_aux, g_z, k)
+    chosen = b["fwd"]["chosen"]
+    names = ("x", "w_router", "w_gate", "w_up", "w_down")
+    grads = dict(x=b["dx"], w_router=b["dw_router"], w_gate=b["dw_gate"], w_up=b["dw_up"], w_down=b["dw_down"])
+
+    def loss(V, eps):
+        P = {n: L[n] + eps * V[n] for n in names}
+        r = oracle.expert_choice_layer_ref(P["x"], P["w_router"], P["w_gate"], P["w_up"], P["w_down"], k,
+                                           forced_chosen=chosen)
+        return float(np.sum(L["dout"] * r["out"]) + g_aux * r["aux"] + g_z * r["z"])
+    rng = np.random.default_rng(15)
+    for only in names + (None,):
+        V = {n: (rng.standard_normal(L[n].shape) if only in (None, n) else np.zeros(L[n].shape)) for n in names}
+        eps = 1e-5
+        fd = (loss(V, eps) - loss(V, -eps)) / (2 * eps)
+        an = sum(float(np.sum(grads[n] * V[n])) for n in names)
+        assert fd == pytest.approx(an, rel=1e-7, abs=1e-9), only
+
+
+def test_expert_choice_backward_zero_upstream_and_untaken_tokens():
+    T, D, F, E, k = 30, 16, 8, 4, 1     # C = 8: 32 choices over 30 tokens leave some untaken
+    L = _small_layer(T, D, F, E, seed=16)
+    b = oracle.expert_choice_backward_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"],
+                                          np.zeros((T, D)), 0.0, 0.0, k)
+    for n in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down"):
+        assert not np.any(b[n]), n
+    # a token no expert took gets gradient only through the router (its softmax feeds the losses)
+    b = oracle.expert_choice_backward_ref(L["x"], L["w_router"], L["w_gate"], L["w_up"], L["w_down"], L["dout"],
+                                          0.0, 0.0, k)
+    untaken = b["fwd"]["token_counts"] == 0
+    assert untaken.any()
+    assert not np.any(b["dx"][untaken]) and not np.any(b["dp"][untaken])
