@@ -47,7 +47,7 @@ extern "C" {
 #define OLMOE_API
 #endif
 
-#define OLMOE_ABI_VERSION 4
+#define OLMOE_ABI_VERSION 5
 
 #define OLMOE_D 2048 /* hidden size */
 #define OLMOE_F 1024 /* expert width (SwiGLU intermediate size) */
@@ -207,6 +207,23 @@ OLMOE_API olmoe_status_t olmoe_moe_forward_expert_choice(const void* x, const fl
                                                int32_t* choice_tokens, float* choice_probs,
                                                int32_t* token_counts, float* aux_loss, float* z_loss,
                                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward pass of the expert-choice layer (olmoe_moe_forward_expert_choice):
+ * the gradients of  L = sum_t <dout[t], out[t]> + g_aux * aux_loss + g_z * z_loss
+ * with respect to x and every weight, by the chain rule through the layer's
+ * steps ("OLMoE Guide", items 1-3; the routing weights are the 64-way
+ * probabilities of the pairs the experts took).  Which tokens each expert takes
+ * and the shares f_e = C / (8T) are piecewise constant and carry no gradient.
+ * The forward is recomputed inside.  Arguments, outputs (fp32, overwritten),
+ * precisions and errors as olmoe_moe_backward, with 0 <= T <=
+ * OLMOE_EC_MAX_TOKENS and a workspace of olmoe_moe_ec_backward_workspace_bytes(T). */
+OLMOE_API size_t olmoe_moe_ec_backward_workspace_bytes(int64_t T);   /* 0 for T out of range; host only */
+OLMOE_API olmoe_status_t olmoe_moe_backward_expert_choice(const void* x, const float* W_router,
+                                                const void* W_gate, const void* W_up,
+                                                const void* W_down, int64_t T, const void* dout,
+                                                float g_aux, float g_z, float* dx, float* dW_router,
+                                                float* dW_gate, float* dW_up, float* dW_down,
+                                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* RMSNorm of the residual stream with unit weight, rounded to the layer's
  * input type: x_out[t] = bf16(h[t] / sqrt(mean_k h[t,k]^2 + eps)), computed in

@@ -393,22 +393,11 @@ olmoe_status_t forward_impl(const void* x, const float* W_router, const void* W_
   return ok();
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t olmoe_moe_backward_workspace_bytes(int64_t T) {
-  if (T < 0 || T > OLMOE_MAX_TOKENS) return 0;
-  return make_bwd_layout(T).total;
-}
-
-olmoe_status_t olmoe_moe_backward(const void* x, const float* W_router, const void* W_gate, const void* W_up,
-                                  const void* W_down, int64_t T, const void* dout, float g_aux, float g_z,
-                                  float* dx, float* dW_router, float* dW_gate, float* dW_up, float* dW_down,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
-  // ---- host-side checks; nothing is enqueued unless all pass
-  if (T < 0 || T > OLMOE_MAX_TOKENS)
-    return fail(OLMOE_EINVAL, "T=%lld out of range [0, %lld]", (long long)T, (long long)OLMOE_MAX_TOKENS);
+// argument checks shared by the backward entry points (T already range-checked)
+olmoe_status_t backward_checks(const void* x, const float* W_router, const void* W_gate, const void* W_up,
+                               const void* W_down, int64_t T, const void* dout, float g_aux, float g_z, float* dx,
+                               float* dW_router, float* dW_gate, float* dW_up, float* dW_down, void* workspace,
+                               size_t workspace_bytes, size_t needed) {
   if (!W_router || !W_gate || !W_up || !W_down) return fail(OLMOE_EINVAL, "a weight pointer is NULL");
   if (!dW_router || !dW_gate || !dW_up || !dW_down) return fail(OLMOE_EINVAL, "a weight-gradient pointer is NULL");
   if (T > 0 && (!x || !dout || !dx)) return fail(OLMOE_EINVAL, "x, dout or dx is NULL");
@@ -425,20 +414,73 @@ olmoe_status_t olmoe_moe_backward(const void* x, const float* W_router, const vo
   const size_t in_n[] = {act, act, wr_bytes, wexp, wexp, wexp};
   void* outs[] = {dx, dW_router, dW_gate, dW_up, dW_down};
   const size_t out_n[] = {act * 2, wr_bytes, wexp * 2, wexp * 2, wexp * 2};
-  const BwdLayout B = make_bwd_layout(T);
   if (!workspace) return fail(OLMOE_EWORKSPACE, "workspace is NULL");
   if (misaligned(workspace, 256)) return fail(OLMOE_EINVAL, "workspace is not 256-byte aligned");
-  if (workspace_bytes < B.total)
-    return fail(OLMOE_EWORKSPACE, "workspace has %zu bytes, %zu needed for T=%lld", workspace_bytes, B.total,
+  if (workspace_bytes < needed)
+    return fail(OLMOE_EWORKSPACE, "workspace has %zu bytes, %zu needed for T=%lld", workspace_bytes, needed,
                 (long long)T);
   for (int o = 0; o < 5; ++o) {
     for (int i = 0; i < 6; ++i)
       if (overlaps(outs[o], out_n[o], ins[i], in_n[i])) return fail(OLMOE_EINVAL, "an output overlaps an input");
     for (int q = o + 1; q < 5; ++q)
       if (overlaps(outs[o], out_n[o], outs[q], out_n[q])) return fail(OLMOE_EINVAL, "two outputs overlap");
-    if (overlaps(outs[o], out_n[o], workspace, B.total)) return fail(OLMOE_EINVAL, "an output overlaps the workspace");
+    if (overlaps(outs[o], out_n[o], workspace, needed)) return fail(OLMOE_EINVAL, "an output overlaps the workspace");
   }
-  olmoe_status_t st = check_device();
+  return check_device();
+}
+
+// expert-choice backward workspace: the expert-choice forward layout, then the backward's buffers
+// for its 64C rows
+struct EcBwdLayout {
+  EcLayout c;
+  size_t p_all, gu, xg, dg, dgu, hw, dxr, dlogits, dwr_part, zero, tp_bwd, tiles_bwd, total;
+};
+EcBwdLayout make_ec_bwd_layout(int64_t T) {
+  EcBwdLayout B{};
+  B.c = make_ec_layout(T);
+  size_t off = B.c.total;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~size_t(255);
+    return o;
+  };
+  const int C = ec_capacity(static_cast<int>(T));
+  const size_t t = static_cast<size_t>(T), rows = static_cast<size_t>(OLMOE_E) * C;
+  B.p_all = take(t * OLMOE_E * 4);
+  B.gu = take(rows * 2 * OLMOE_F * 4);
+  B.xg = take(rows * OLMOE_D * 2);
+  B.dg = take(rows * OLMOE_D * 2);
+  B.dgu = take(rows * 2 * OLMOE_F * 2);
+  B.hw = take(rows * OLMOE_F * 2);
+  B.dxr = take(rows * OLMOE_D * 4);
+  B.dlogits = take(t * OLMOE_E * 4);
+  B.dwr_part = take(static_cast<size_t>(bwd_router_splits(static_cast<int>(T))) * OLMOE_E * OLMOE_D * 4);
+  B.zero = take(4096);
+  B.tp_bwd = take(65 * 4);
+  B.tiles_bwd = take((static_cast<size_t>(max_row_tiles(8 * C, MIN_TILE_ROWS)) + 8) * 8);
+  B.total = off;
+  return B;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t olmoe_moe_backward_workspace_bytes(int64_t T) {
+  if (T < 0 || T > OLMOE_MAX_TOKENS) return 0;
+  return make_bwd_layout(T).total;
+}
+
+olmoe_status_t olmoe_moe_backward(const void* x, const float* W_router, const void* W_gate, const void* W_up,
+                                  const void* W_down, int64_t T, const void* dout, float g_aux, float g_z,
+                                  float* dx, float* dW_router, float* dW_gate, float* dW_up, float* dW_down,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  // ---- host-side checks; nothing is enqueued unless all pass
+  if (T < 0 || T > OLMOE_MAX_TOKENS)
+    return fail(OLMOE_EINVAL, "T=%lld out of range [0, %lld]", (long long)T, (long long)OLMOE_MAX_TOKENS);
+  const BwdLayout B = make_bwd_layout(T);
+  olmoe_status_t st = backward_checks(x, W_router, W_gate, W_up, W_down, T, dout, g_aux, g_z, dx, dW_router, dW_gate,
+                                      dW_up, dW_down, workspace, workspace_bytes, B.total);
   if (st != OLMOE_OK) return st;
 
   // ---- launches: recompute the forward (keeping p, lse, G, U, Y), then the gradients
@@ -628,7 +670,7 @@ olmoe_status_t olmoe_moe_forward_expert_choice(const void* x, const float* W_rou
     if (he != hipSuccess) return fail(OLMOE_EHIP, "router launch: %s", hipGetErrorString(he));
   }
   rec.mark();
-  he = launch_ec_choose(ea, s);   // T == 0: only the losses (0)
+  he = launch_ec_choose(ea, s);   // T == 0: zero offsets, and the losses (0)
   if (he != hipSuccess) return fail(OLMOE_EHIP, "expert-choice selection launch: %s", hipGetErrorString(he));
   rec.mark();
   if (Ti == 0) {
@@ -657,6 +699,121 @@ olmoe_status_t olmoe_moe_forward_expert_choice(const void* x, const float* W_rou
   he = launch_ec_combine(ea, s);
   if (he != hipSuccess) return fail(OLMOE_EHIP, "combine launch: %s", hipGetErrorString(he));
   rec.mark();
+  return ok();
+}
+
+size_t olmoe_moe_ec_backward_workspace_bytes(int64_t T) {
+  if (T < 0 || T > OLMOE_EC_MAX_TOKENS) return 0;
+  return make_ec_bwd_layout(T).total;
+}
+
+olmoe_status_t olmoe_moe_backward_expert_choice(const void* x, const float* W_router, const void* W_gate,
+                                                const void* W_up, const void* W_down, int64_t T, const void* dout,
+                                                float g_aux, float g_z, float* dx, float* dW_router, float* dW_gate,
+                                                float* dW_up, float* dW_down, void* workspace, size_t workspace_bytes,
+                                                void* stream) {
+  if (T < 0 || T > OLMOE_EC_MAX_TOKENS)
+    return fail(OLMOE_EINVAL, "T=%lld out of range [0, %lld]", (long long)T, (long long)OLMOE_EC_MAX_TOKENS);
+  const EcBwdLayout B = make_ec_bwd_layout(T);
+  olmoe_status_t st = backward_checks(x, W_router, W_gate, W_up, W_down, T, dout, g_aux, g_z, dx, dW_router, dW_gate,
+                                      dW_up, dW_down, workspace, workspace_bytes, B.total);
+  if (st != OLMOE_OK) return st;
+
+  // ---- launches: recompute the expert-choice forward (keeping p, lse, G, U, Y), then the gradients
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const EcLayout& L = B.c;
+  const int Ti = static_cast<int>(T);
+  const int C = ec_capacity(Ti);
+  const int Teff = 8 * C;
+  const GemmPlan plan = plan_gemm(Teff);
+  EcArgs ea{};
+  ea.T = Ti;
+  ea.C = C;
+  ea.partial = reinterpret_cast<const float2*>(ws + L.f.partial);
+  ea.pT = reinterpret_cast<float*>(ws + L.pT);
+  ea.lse = reinterpret_cast<float*>(ws + L.lse);
+  ea.inv_ec = reinterpret_cast<int32_t*>(ws + L.inv_ec);
+  ea.perm = reinterpret_cast<int32_t*>(ws + L.f.perm);
+  ea.row_w = reinterpret_cast<float*>(ws + L.row_w);
+  ea.blk_psum = reinterpret_cast<float*>(ws + L.f.blk_psum);
+  ea.blk_lse2 = reinterpret_cast<float*>(ws + L.f.blk_lse2);
+  ea.offsets = reinterpret_cast<int32_t*>(ws + L.f.offsets);
+  ea.tile_prefix_gu = reinterpret_cast<int32_t*>(ws + L.f.tp_gu);
+  ea.tiles_gu = reinterpret_cast<int2*>(ws + L.f.tiles_gu);
+  ea.bm_gu = plan.bm_gu;
+  ea.tile_prefix_dn = reinterpret_cast<int32_t*>(ws + L.f.tp_dn);
+  ea.tiles_dn = reinterpret_cast<int2*>(ws + L.f.tiles_dn);
+  ea.bm_dn = plan.bm_dn;
+  ea.p_all = reinterpret_cast<float*>(ws + B.p_all);
+  hipError_t he = hipSuccess;
+  if (Ti > 0) {
+    RouterArgs ra{static_cast<const uint16_t*>(x), W_router, Ti, reinterpret_cast<float2*>(ws + L.f.partial),
+                  reinterpret_cast<uint16_t*>(ws + L.f.planes)};
+    he = launch_router_partial(ra, s);
+    if (he == hipSuccess) he = launch_ec_softmax(ea, s);
+  }
+  if (he == hipSuccess) he = launch_ec_choose(ea, s);   // T == 0: zero offsets for the weight gradients
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "routing launch: %s", hipGetErrorString(he));
+  const int32_t* perm = reinterpret_cast<const int32_t*>(ws + L.f.perm);
+  const int32_t* offsets = reinterpret_cast<const int32_t*>(ws + L.f.offsets);
+  if (Ti > 0) {
+    GemmArgs ga{Teff,
+                static_cast<const uint16_t*>(x),
+                static_cast<const uint16_t*>(W_gate),
+                static_cast<const uint16_t*>(W_up),
+                static_cast<const uint16_t*>(W_down),
+                perm, offsets,
+                reinterpret_cast<const int32_t*>(ws + L.f.tp_gu),
+                reinterpret_cast<const int32_t*>(ws + L.f.tp_dn),
+                reinterpret_cast<const int2*>(ws + L.f.tiles_gu),
+                reinterpret_cast<const int2*>(ws + L.f.tiles_dn),
+                reinterpret_cast<uint16_t*>(ws + L.f.h),
+                reinterpret_cast<uint16_t*>(ws + L.f.y),
+                reinterpret_cast<float*>(ws + B.gu)};
+    he = launch_gateup(ga, plan, s);
+    if (he == hipSuccess) he = launch_down(ga, plan, s);
+    if (he != hipSuccess) return fail(OLMOE_EHIP, "forward GEMM launch: %s", hipGetErrorString(he));
+  }
+  BwdSmallArgs ba{Ti, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dout), W_router, nullptr,
+                  reinterpret_cast<const float*>(ws + B.p_all), reinterpret_cast<const float*>(ws + L.lse),
+                  offsets, perm, nullptr,
+                  reinterpret_cast<const uint16_t*>(ws + L.f.y), g_aux, g_z,
+                  reinterpret_cast<float*>(ws + B.dlogits), reinterpret_cast<uint16_t*>(ws + B.xg),
+                  reinterpret_cast<uint16_t*>(ws + B.dg), reinterpret_cast<const float*>(ws + B.dxr), dx,
+                  reinterpret_cast<float*>(ws + B.dwr_part), dW_router, reinterpret_cast<uint16_t*>(ws + B.zero),
+                  reinterpret_cast<int32_t*>(ws + B.tp_bwd), reinterpret_cast<int2*>(ws + B.tiles_bwd),
+                  reinterpret_cast<const int32_t*>(ws + L.inv_ec), OLMOE_E * C};
+  he = launch_bwd_prepare(ba, s);
+  if (he == hipSuccess) he = launch_bwd_router(ba, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "backward routing launch: %s", hipGetErrorString(he));
+  const uint16_t* dgu = reinterpret_cast<const uint16_t*>(ws + B.dgu);
+  if (Ti > 0) {
+    BwdDgradArgs dh{reinterpret_cast<const uint16_t*>(ws + B.dg), nullptr, static_cast<const uint16_t*>(W_down),
+                    nullptr, OLMOE_F, (long)OLMOE_D * OLMOE_F, 2 * OLMOE_F,
+                    reinterpret_cast<const int32_t*>(ws + B.tp_bwd) + OLMOE_E,
+                    reinterpret_cast<const int2*>(ws + B.tiles_bwd),
+                    reinterpret_cast<const float*>(ws + L.row_w), reinterpret_cast<const float*>(ws + B.gu),
+                    reinterpret_cast<uint16_t*>(ws + B.dgu), reinterpret_cast<uint16_t*>(ws + B.hw), nullptr};
+    BwdDgradArgs dxa{dgu, nullptr, static_cast<const uint16_t*>(W_gate), static_cast<const uint16_t*>(W_up),
+                     OLMOE_D, (long)OLMOE_F * OLMOE_D, OLMOE_F,
+                     reinterpret_cast<const int32_t*>(ws + B.tp_bwd) + OLMOE_E,
+                     reinterpret_cast<const int2*>(ws + B.tiles_bwd), nullptr, nullptr, nullptr, nullptr,
+                     reinterpret_cast<float*>(ws + B.dxr)};
+    he = launch_dgrad(dh, Teff, true, s);
+    if (he == hipSuccess) he = launch_dgrad(dxa, Teff, false, s);
+    if (he != hipSuccess) return fail(OLMOE_EHIP, "dgrad launch: %s", hipGetErrorString(he));
+  }
+  BwdWgradArgs wd{reinterpret_cast<const uint16_t*>(ws + B.dg), OLMOE_D, reinterpret_cast<const uint16_t*>(ws + B.hw),
+                  OLMOE_F, offsets, reinterpret_cast<const uint16_t*>(ws + B.zero), OLMOE_D, OLMOE_F, dW_down, dW_down,
+                  OLMOE_D, (long)OLMOE_D * OLMOE_F};
+  BwdWgradArgs wgu{dgu, 2 * OLMOE_F, reinterpret_cast<const uint16_t*>(ws + B.xg), OLMOE_D, offsets,
+                   reinterpret_cast<const uint16_t*>(ws + B.zero), 2 * OLMOE_F, OLMOE_D, dW_gate, dW_up, OLMOE_F,
+                   (long)OLMOE_F * OLMOE_D};
+  he = launch_wgrad(wd, s);
+  if (he == hipSuccess) he = launch_wgrad(wgu, s);
+  if (he == hipSuccess) he = launch_bwd_finish(ba, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "weight-gradient launch: %s", hipGetErrorString(he));
   return ok();
 }
 

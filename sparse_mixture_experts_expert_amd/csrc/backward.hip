@@ -1,4 +1,5 @@
-// The non-GEMM steps of the backward pass of the OLMoE MoE layer.
+// The non-GEMM steps of the backward pass of the OLMoE MoE layer (token choice, and the
+// expert-choice form of the layer, whose routing weights are the same probabilities).
 //
 // With out[t] = sum_j w[t,j] Y[t,j] and w[t,j] = p[t, e_j] (the 64-way softmax
 // probabilities, not renormalised: "Mixture-of-experts LLMs from scratch with
@@ -49,7 +50,9 @@ __global__ __launch_bounds__(256) void bwd_prepare_kernel(BwdSmallArgs a, int bm
   *reinterpret_cast<u32x4*>(a.dg + (size_t)r * D + c) = *reinterpret_cast<const u32x4*>(a.dout + (size_t)t * D + c);
 }
 
-// one wavefront per token: dL/dw for its 8 rows, then dL/dlogits with lane = expert
+// one wavefront per token: dL/dw for its 8 rows (expert choice: for the rows of the experts that
+// took it, in ascending expert order), then dL/dlogits with lane = expert
+template <bool EC>
 __global__ __launch_bounds__(256) void bwd_router_kernel(BwdSmallArgs a) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
@@ -65,10 +68,9 @@ __global__ __launch_bounds__(256) void bwd_router_kernel(BwdSmallArgs a) {
       g[c][2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
     }
   }
-  float dw[K];
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const uint16_t* yr = a.y + (size_t)a.inv[t * K + j] * D;
+  // <dout[t], Y row>, the same on every lane
+  auto dot_row = [&](int row) {
+    const uint16_t* yr = a.y + (size_t)row * D;
     float s = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -79,14 +81,28 @@ __global__ __launch_bounds__(256) void bwd_router_kernel(BwdSmallArgs a) {
         s = fmaf(g[c][2 * i + 1], f16_to_f32(static_cast<uint16_t>(v[i] >> 16)), s);
       }
     }
-    dw[j] = wave_sum(s);
-  }
+    return wave_sum(s);
+  };
   const float p = a.p_all[(size_t)t * E + lane];
   const float cnt = static_cast<float>(a.offsets[lane + 1] - a.offsets[lane]);
   const float Tf = static_cast<float>(a.T);
   float dp = a.g_aux * static_cast<float>(LB_ALPHA * E) * (cnt / (K * Tf)) / Tf;
+  if constexpr (EC) {
+    const int myrow = a.inv_ec[(size_t)t * E + lane];
+    float dwl = 0.f;
+    for (uint64_t m = __ballot(myrow >= 0); m; m &= m - 1) {
+      const int ej = __builtin_ctzll(m);
+      const float d = dot_row(__shfl(myrow, ej));
+      dwl = lane == ej ? d : dwl;
+    }
+    dp += dwl;
+  } else {
+    float dw[K];
 #pragma unroll
-  for (int j = 0; j < K; ++j) dp += a.ids[t * K + j] == lane ? dw[j] : 0.f;
+    for (int j = 0; j < K; ++j) dw[j] = dot_row(a.inv[t * K + j]);
+#pragma unroll
+    for (int j = 0; j < K; ++j) dp += a.ids[t * K + j] == lane ? dw[j] : 0.f;
+  }
   const float s = wave_sum(p * dp);
   a.dlogits[(size_t)t * E + lane] =
       p * (dp - s) + a.g_z * static_cast<float>(Z_BETA) * 2.0f * a.lse[t] / Tf * p;
@@ -137,15 +153,30 @@ __global__ __launch_bounds__(256) void bwd_wrouter_reduce_kernel(BwdSmallArgs a,
 }
 
 // dx for DX_TOK tokens and 256 columns per workgroup, one column per thread: dl W_router, then
-// the token's 8 per-row input gradients in slot order
+// the token's 8 per-row input gradients in slot order (expert choice: the rows of the experts
+// that took it, in ascending expert order)
 constexpr int DX_TOK = 16;
+template <bool EC>
 __global__ __launch_bounds__(256) void bwd_dx_kernel(BwdSmallArgs a) {
   __shared__ float sdl[DX_TOK][E];
+  __shared__ int srow[EC ? DX_TOK : 1][E];
+  __shared__ int scnt[DX_TOK];
   const int t0 = blockIdx.x * DX_TOK;
   const int tid = threadIdx.x;
   for (int i = tid; i < DX_TOK * E; i += 256) {
     const int tk = i / E;
     sdl[tk][i % E] = t0 + tk < a.T ? a.dlogits[(size_t)(t0 + tk) * E + i % E] : 0.f;
+  }
+  if constexpr (EC) {   // wave w lists the rows of tokens w, w + 4, ... in ascending expert order
+    const int lane = tid & 63;
+    for (int tk = tid >> 6; tk < DX_TOK; tk += 4) {
+      const int row = t0 + tk < a.T ? a.inv_ec[(size_t)(t0 + tk) * E + lane] : -1;
+      const uint64_t m = __ballot(row >= 0);
+      const int pos = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+      if (row >= 0) srow[tk][pos] = row;
+      if (lane == 0) scnt[tk] = __popcll(m);
+    }
   }
   const int col = blockIdx.y * 256 + tid;
   float wr[E];
@@ -163,11 +194,16 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(BwdSmallArgs a) {
   for (int tk = 0; tk < DX_TOK; ++tk) {
     const int t = t0 + tk;
     if (t >= a.T) break;
-    float r[K];
+    if constexpr (EC) {
+      const int n = scnt[tk];
+      for (int j = 0; j < n; ++j) acc[tk] += a.dxr[(size_t)srow[tk][j] * D + col];
+    } else {
+      float r[K];
 #pragma unroll
-    for (int j = 0; j < K; ++j) r[j] = a.dxr[(size_t)a.inv[t * K + j] * D + col];
+      for (int j = 0; j < K; ++j) r[j] = a.dxr[(size_t)a.inv[t * K + j] * D + col];
 #pragma unroll
-    for (int j = 0; j < K; ++j) acc[tk] += r[j];
+      for (int j = 0; j < K; ++j) acc[tk] += r[j];
+    }
     a.dx[(size_t)t * D + col] = acc[tk];
   }
 }
@@ -177,13 +213,17 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(BwdSmallArgs a) {
 int bwd_router_splits(int T) { return (T + WR_SPLIT_TOKENS - 1) / WR_SPLIT_TOKENS; }
 
 hipError_t launch_bwd_prepare(const BwdSmallArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(bwd_prepare_kernel, dim3(1 + K * a.T), dim3(256), 0, stream, a, bwd_tile_rows());
+  hipLaunchKernelGGL(bwd_prepare_kernel, dim3(1 + (a.rows ? a.rows : K * a.T)), dim3(256), 0, stream, a,
+                     bwd_tile_rows());
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_router(const BwdSmallArgs& a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_router_kernel, dim3((a.T + 3) / 4), dim3(256), 0, stream, a);
+  if (a.inv_ec)
+    hipLaunchKernelGGL(bwd_router_kernel<true>, dim3((a.T + 3) / 4), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(bwd_router_kernel<false>, dim3((a.T + 3) / 4), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -195,7 +235,11 @@ hipError_t launch_bwd_finish(const BwdSmallArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(bwd_wrouter_reduce_kernel, dim3(E * D / 256), dim3(256), 0, stream, a, ns);
   e = hipGetLastError();
   if (e != hipSuccess || a.T == 0) return e;
-  hipLaunchKernelGGL(bwd_dx_kernel, dim3((a.T + DX_TOK - 1) / DX_TOK, D / 256), dim3(256), 0, stream, a);
+  const dim3 grid((a.T + DX_TOK - 1) / DX_TOK, D / 256);
+  if (a.inv_ec)
+    hipLaunchKernelGGL(bwd_dx_kernel<true>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(bwd_dx_kernel<false>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -78,6 +78,7 @@ __global__ __launch_bounds__(256) void ec_softmax_kernel(EcArgs a) {
   if (valid) {
     if (j == 0) a.lse[t] = lse;
     *reinterpret_cast<int4*>(a.inv_ec + (size_t)t * E + j * 4) = make_int4(-1, -1, -1, -1);
+    if (a.p_all) *reinterpret_cast<f32x4*>(a.p_all + (size_t)t * E + j * 4) = f32x4{p[0] * rs, p[1] * rs, p[2] * rs, p[3] * rs};
   }
   __syncthreads();
   const int e = tid >> 2, q = tid & 3;
@@ -183,7 +184,14 @@ __global__ __launch_bounds__(NT) void ec_choose_kernel(EcArgs a) {
     }
     return;
   }
-  if (T == 0) return;
+  if (T == 0) {   // no rows: zero offsets and tile counts (the backward's weight gradients read them)
+    if (e == 0 && tid <= E) {
+      a.offsets[tid] = 0;
+      a.tile_prefix_gu[tid] = 0;
+      a.tile_prefix_dn[tid] = 0;
+    }
+    return;
+  }
   const float* col = a.pT + (size_t)e * T;
   const int tbase = tid * VPT;
 
@@ -375,7 +383,6 @@ hipError_t launch_ec_softmax(const EcArgs& a, hipStream_t stream) {
 
 hipError_t launch_ec_choose(const EcArgs& a, hipStream_t stream) {
   const bool losses = a.aux_loss || a.z_loss;
-  if (a.T == 0 && !losses) return hipSuccess;
   const dim3 grid(E + (losses ? 1 : 0));
   if (a.T <= 256)
     hipLaunchKernelGGL((ec_choose_kernel<256, 1>), grid, dim3(256), 0, stream, a);

@@ -141,6 +141,7 @@ struct EcArgs {
   int32_t* token_counts;      // [T] or null
   float* aux_loss;            // [1] or null
   float* z_loss;              // [1] or null
+  float* p_all = nullptr;     // fp32 [T,64] probabilities by token (backward pass), or null
 };
 hipError_t launch_ec_softmax(const EcArgs& a, hipStream_t stream);   // p (transposed), lse, inv_ec = -1
 // top-C per expert and the tile lists (one workgroup per expert), aux and z (one more)
@@ -209,6 +210,8 @@ struct BwdSmallArgs {
   uint16_t* zero;             // 4 KiB
   int32_t* tp_bwd;            // [65] row-tile prefix of the dgrad tile list
   int2* tiles_bwd;
+  const int32_t* inv_ec = nullptr;   // expert choice: [T,64] row of (t, e) or -1 (replaces ids / inv)
+  int rows = 0;                      // rows in expert order (0: 8T)
 };
 int bwd_router_splits(int T);
 hipError_t launch_bwd_prepare(const BwdSmallArgs& a, hipStream_t stream);   // zero row, tile list, gathers

@@ -176,6 +176,31 @@ def test_expert_choice_checks_arguments_first(L):
     assert ec(counts=(8 << 36) + 256) == binding.EINVAL        # output in the workspace
 
 
+def test_expert_choice_backward_checks_arguments_first(L):
+    # every call here fails validation, so nothing reaches a device (fake pointers)
+    vp = ctypes.c_void_p
+    T = 100
+    C = binding.ec_capacity(T)
+    wsb = binding.ec_backward_workspace_bytes(T)
+    # the forward's buffers plus G|U fp32, x / dout rows, dG|dU, w*H and per-row dx for 64C rows
+    assert wsb >= binding.ec_workspace_bytes(T) + 64 * C * (2048 * 4 + 2048 * 2 * 3 + 1024 * 2 + 2048 * 4)
+    assert binding.ec_backward_workspace_bytes(-1) == 0
+    assert binding.ec_backward_workspace_bytes(binding.EC_MAX_TOKENS + 1) == 0
+
+    def bwd(dx=5 << 20, dwr=6 << 20, dwg=1 << 34, dwu=2 << 34, dwd=3 << 34, ws=8 << 36, wsb=wsb, g=1.0, t=T):
+        return L.olmoe_moe_backward_expert_choice(vp(1 << 20), vp(2 << 20), vp(1 << 32), vp(2 << 32), vp(3 << 32), t,
+                                                  vp(4 << 20), ctypes.c_float(g), ctypes.c_float(0.5), vp(dx),
+                                                  vp(dwr), vp(dwg), vp(dwu), vp(dwd), vp(ws), wsb, None)
+    assert bwd(t=binding.EC_MAX_TOKENS + 1) == binding.EINVAL
+    assert bwd(dwg=0) == binding.EINVAL
+    assert bwd(dx=0) == binding.EINVAL
+    assert bwd(g=float("inf")) == binding.EINVAL
+    assert bwd(dwr=(6 << 20) + 4) == binding.EINVAL
+    assert bwd(wsb=1000) == binding.EWORKSPACE
+    assert bwd(dwu=(1 << 34) + 4096) == binding.EINVAL
+    assert bwd(dwd=(8 << 36) + 256) == binding.EINVAL
+
+
 def test_glue_entry_points_reject_bad_arguments(L):
     vp = ctypes.c_void_p
     assert L.olmoe_rmsnorm_bf16(vp(1 << 20), ctypes.c_float(0.0), 4, vp(1 << 30), None) == binding.EINVAL

@@ -1,6 +1,8 @@
-"""GPU parity of the layer's backward pass (olmoe_moe_backward, through the C ABI)
-against the float64 oracle's chain rule (oracle.moe_layer_backward_ref, itself pinned
-against autograd and finite differences).  Every gradient tensor is compared whole."""
+"""GPU parity of the layer's backward pass (olmoe_moe_backward, and
+olmoe_moe_backward_expert_choice for the expert-choice layer, through the C ABI) against
+the float64 oracle's chain rule (oracle.moe_layer_backward_ref and
+oracle.expert_choice_backward_ref, pinned against autograd and finite differences).
+Every gradient tensor is compared whole."""
 import numpy as np
 import pytest
 
@@ -109,6 +111,64 @@ def test_backward_bitwise_reproducible(weights):
     dout = inputs.device_x(T, seed=32, workload="parity")
     a = binding.moe_backward(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], dout)
     b = binding.moe_backward(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], dout)
+    torch.cuda.synchronize()
+    for k in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down"):
+        assert torch.equal(a[k], b[k]), k
+
+
+# ------------------------------------------------------------------ expert choice
+
+
+def run_ec_backward(w, hw, T, seed, g_aux, g_z):
+    x = inputs.device_x(T, seed=seed, workload="parity")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 100)
+    dout = torch.randn((T, 2048), generator=g, device="cuda").to(torch.bfloat16)
+    fwd = binding.moe_forward_expert_choice(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"])
+    b = binding.moe_backward_expert_choice(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], dout,
+                                           g_aux=g_aux, g_z=g_z)
+    torch.cuda.synchronize()
+    xb = parity.bf16_tensor_to_bits(x)
+    tok = fwd["choice_tokens"].cpu().numpy()
+    logits = oracle.router_logits(xb, hw["w_router"])
+    _, p_all = oracle.softmax_all(logits)
+    ntie = parity.check_expert_choice(tok, fwd["choice_probs"].cpu().numpy(), fwd["token_counts"].cpu().numpy(),
+                                      p_all, logits, f"EC backward T={T}")
+    ref = oracle.expert_choice_backward_ref(xb, hw["w_router"], hw["w_gate"], hw["w_up"], hw["w_down"],
+                                            parity.bf16_tensor_to_bits(dout), g_aux, g_z, 8, forced_chosen=tok,
+                                            magnitudes=True)
+    out = {}
+    for name, mag in (("dx", "mag_dx"), ("dw_router", None), ("dw_gate", "mag_gate"), ("dw_up", "mag_up"),
+                      ("dw_down", "mag_down")):
+        out[name] = check_grad(b[name].cpu().numpy(), ref[name], f"EC T={T} {name}", ref[mag] if mag else None)
+    _log(f"EC T={T} g_aux={g_aux} g_z={g_z} tie experts={ntie} " +
+         " ".join(f"{n}=({r:.1e},{m:.1e})" for n, (r, m) in out.items()))
+
+
+@pytest.mark.parametrize("T,g_aux,g_z", [(1, 1.0, 1.0), (9, 1.0, 1.0), (200, 0.0, 0.0), (200, 5.0, -3.0),
+                                         (700, 1.0, 1.0), (2100, 1.0, 1.0), (4096, 1.0, 1.0)])
+def test_expert_choice_backward_matches_oracle(weights, T, g_aux, g_z):
+    w, hw = weights
+    _log(f"EC backward T={T}")
+    run_ec_backward(w, hw, T, seed=40 + T, g_aux=g_aux, g_z=g_z)
+
+
+def test_expert_choice_backward_zero_tokens(weights):
+    w, _ = weights
+    x = torch.empty((0, 2048), dtype=torch.bfloat16, device="cuda")
+    b = binding.moe_backward_expert_choice(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], x.clone())
+    torch.cuda.synchronize()
+    for k in ("dw_router", "dw_gate", "dw_up", "dw_down"):
+        assert not torch.any(b[k]).item(), k
+
+
+def test_expert_choice_backward_bitwise_reproducible(weights):
+    w, _ = weights
+    T = 300
+    x = inputs.device_x(T, seed=33, workload="parity")
+    dout = inputs.device_x(T, seed=34, workload="parity")
+    a = binding.moe_backward_expert_choice(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], dout)
+    b = binding.moe_backward_expert_choice(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], dout)
     torch.cuda.synchronize()
     for k in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down"):
         assert torch.equal(a[k], b[k]), k
