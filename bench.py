@@ -200,8 +200,10 @@ def measure(workload, steps, warmup, seed=0, tokens=None):
 BWD_FLOP_PER_TOKEN = 2 * K * 3 * 2 * D * F + 2 * 2 * D * E
 
 
-def measure_backward(workload, steps, warmup, seed=0):
-    """Wall-clock time of olmoe_moe_backward (forward recompute + gradients) per call."""
+def measure_backward(workload, steps, warmup, seed=0, routing="token"):
+    """Wall-clock time per call of the backward pass (forward recompute + gradients), and of a
+    training step of the layer: one forward call and one backward call.  routing "token" uses
+    olmoe_moe_forward / olmoe_moe_backward, "expert" the expert-choice entry points."""
     import torch
     from sparse_mixture_experts_expert_amd import binding, inputs
 
@@ -213,32 +215,69 @@ def measure_backward(workload, steps, warmup, seed=0):
     g.manual_seed(seed + 7)
     dout = torch.randn((T, D), generator=g, device="cuda").to(torch.bfloat16)
     f32 = torch.float32
-    outs = dict(dx=torch.empty((T, D), dtype=f32, device="cuda"),
-                dw_router=torch.empty((E, D), dtype=f32, device="cuda"),
-                dw_gate=torch.empty((E, F, D), dtype=f32, device="cuda"),
-                dw_up=torch.empty((E, F, D), dtype=f32, device="cuda"),
-                dw_down=torch.empty((E, D, F), dtype=f32, device="cuda"))
-    ws = torch.empty(binding.backward_workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    dev = "cuda"
+    outs = dict(dx=torch.empty((T, D), dtype=f32, device=dev),
+                dw_router=torch.empty((E, D), dtype=f32, device=dev),
+                dw_gate=torch.empty((E, F, D), dtype=f32, device=dev),
+                dw_up=torch.empty((E, F, D), dtype=f32, device=dev),
+                dw_down=torch.empty((E, D, F), dtype=f32, device=dev))
+    y = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    aux = torch.empty(1, dtype=f32, device=dev)
+    z = torch.empty(1, dtype=f32, device=dev)
+    if routing == "expert":
+        bws = torch.empty(binding.ec_backward_workspace_bytes(T), dtype=torch.uint8, device=dev)
+        fws = torch.empty(binding.ec_workspace_bytes(T), dtype=torch.uint8, device=dev)
+        C = binding.ec_capacity(T)
+        ct = torch.empty((E, C), dtype=torch.int32, device=dev)
+        tc = torch.empty(T, dtype=torch.int32, device=dev)
+
+        def fwd(w):
+            binding.moe_forward_expert_choice(d["x"], w["w_router"], w["w_gate"], w["w_up"], w["w_down"], out=y,
+                                              choice_tokens=ct, token_counts=tc, choice_probs=None, aux_loss=aux,
+                                              z_loss=z, workspace=fws, want_routing=False)
+
+        def bwd(w):
+            binding.moe_backward_expert_choice(d["x"], w["w_router"], w["w_gate"], w["w_up"], w["w_down"], dout,
+                                               g_aux=1.0, g_z=1.0, workspace=bws, **outs)
+    else:
+        bws = torch.empty(binding.backward_workspace_bytes(T), dtype=torch.uint8, device=dev)
+        fws = binding.make_workspace(T)
+        ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+        cnt = torch.empty(E, dtype=torch.int32, device=dev)
+
+        def fwd(w):
+            binding.moe_forward(d["x"], w["w_router"], w["w_gate"], w["w_up"], w["w_down"], out=y, route_ids=ids,
+                                expert_counts=cnt, aux_loss=aux, z_loss=z, workspace=fws, want_routing=False)
+
+        def bwd(w):
+            binding.moe_backward(d["x"], w["w_router"], w["w_gate"], w["w_up"], w["w_down"], dout, g_aux=1.0,
+                                 g_z=1.0, workspace=bws, **outs)
     it = [0]
 
-    def step():
-        w = sets[it[0] % N_WEIGHT_SETS]
-        it[0] += 1
-        binding.moe_backward(d["x"], w["w_router"], w["w_gate"], w["w_up"], w["w_down"], dout, g_aux=1.0,
-                             g_z=1.0, workspace=ws, **outs)
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    sec = (time.perf_counter() - t0) / steps
-    return {"workload": workload, "tokens": T, "ms_per_step": round(sec * 1e3, 5),
+    def timed(fn_list):
+        for _ in range(warmup):
+            w = sets[it[0] % N_WEIGHT_SETS]
+            it[0] += 1
+            for fn in fn_list:
+                fn(w)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            w = sets[it[0] % N_WEIGHT_SETS]
+            it[0] += 1
+            for fn in fn_list:
+                fn(w)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+    sec = timed([bwd])
+    sec_train = timed([fwd, bwd])
+    return {"routing": routing, "workload": workload, "tokens": T, "ms_per_step": round(sec * 1e3, 5),
             "tokens_per_s": round(T / sec, 1),
             "tflops": round(BWD_FLOP_PER_TOKEN * T / sec / 1e12, 2),
             "mfma_frac": round(BWD_FLOP_PER_TOKEN * T / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "note": "gradients of x and all weights; the forward recompute inside is timed, not counted"}
+            "train_step_ms": round(sec_train * 1e3, 5), "train_tokens_per_s": round(T / sec_train, 1),
+            "note": "backward: gradients of x and all weights, the forward recompute inside timed, not counted "
+                    "in tflops; train step: one forward call + one backward call"}
 
 
 def measure_expert_choice(workload, steps, warmup, seed=0):
@@ -540,7 +579,8 @@ def main():
     if not args.no_backward and wl_layers_of(args.workload) == 1:
         wls = [args.workload] + ([] if args.no_secondary or args.workload == "prefill-4096" else ["prefill-4096"])
         torch.cuda.empty_cache()
-        line["backward"] = [measure_backward(w, max(5, args.steps // 5), 2, args.seed) for w in wls]
+        line["backward"] = [measure_backward(w, max(5, args.steps // 5), 2, args.seed, routing=r)
+                            for w in wls for r in ("token", "expert")]
     if not args.no_expert_choice and wl_layers_of(args.workload) == 1:
         wls = [args.workload] + ([] if args.no_secondary or args.workload == "prefill-4096" else ["prefill-4096"])
         torch.cuda.empty_cache()
