@@ -214,7 +214,7 @@ int bwd_router_splits(int T) { return (T + WR_SPLIT_TOKENS - 1) / WR_SPLIT_TOKEN
 
 hipError_t launch_bwd_prepare(const BwdSmallArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(bwd_prepare_kernel, dim3(1 + (a.rows ? a.rows : K * a.T)), dim3(256), 0, stream, a,
-                     bwd_tile_rows());
+                     bwd_tile_rows(a.rows ? a.rows / K : a.T));
   return hipGetLastError();
 }
 

@@ -168,7 +168,7 @@ struct BwdDgradArgs {
   uint16_t* hw;
   float* out_f32;             // fp32 [rows, 2048]
 };
-int bwd_tile_rows();   // row tile height of the dgrad kernels
+int bwd_tile_rows(int T);   // row tile height of the dgrad kernels for T tokens (rows 8T)
 hipError_t launch_dgrad(const BwdDgradArgs& a, int T, bool dh, hipStream_t stream);
 
 // wgrad: per expert, out[m][n] = sum over the expert's rows r of a[r][m] * b[r][n]
