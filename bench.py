@@ -59,12 +59,20 @@ def stage_model(stage, T, touched):
     return 0, 0
 
 
-def kernel_source_hash():
+# sources that define each forward stage's kernels (besides the shared common.hpp / kernels.hpp)
+STAGE_SOURCES = {"router": ("router.hip", "routing.hpp"), "dispatch": ("dispatch.hip", "routing.hpp"),
+                 "gateup": ("grouped_gemm.hip",), "down": ("grouped_gemm.hip",), "combine": ("combine.hip",)}
+
+
+def kernel_source_hash(stage=None):
+    """Hash of the kernel sources: of every source, or of those that define one stage's kernels."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_mixture_experts_expert_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    names = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".hpp")))
+    if stage is not None:
+        names = sorted(set(STAGE_SOURCES[stage]) | {"common.hpp", "kernels.hpp"})
+    for f in names:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -75,7 +83,7 @@ def traffic_from_profiles(workload, stage):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("source_hash") != kernel_source_hash(stage):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -382,6 +390,8 @@ def copy_probe():
 
 def _stage_of(kernel_name):
     n = kernel_name
+    if "ec_softmax" in n or "ec_choose" in n or "ec_combine" in n:
+        return "expert_choice"
     for key in ("dgrad_kernel", "wgrad_kernel", "bwd_"):
         if key in n:
             return "backward"
@@ -428,16 +438,16 @@ def traffic_summary(args):
     copy_w, _ = _per_dispatch(cw, "WRITE_SIZE", is_copy)
     kf = COPY_PROBE_BYTES / copy_f      # bytes per counted unit (nominally KiB)
     kw = COPY_PROBE_BYTES / copy_w
-    src_hash = kernel_source_hash()
     lines = [f"# HBM traffic per launch, {wl}", "",
              "Counters FETCH_SIZE and WRITE_SIZE (rocprofv3, one counter per run), median over",
              "dispatches, scaled by the same counters for a plain 1 GiB elementwise copy",
              f"(torch.neg over float32: reads and writes {COPY_PROBE_BYTES} B).", "",
              f"- copy probe: FETCH_SIZE {copy_f:.1f}, WRITE_SIZE {copy_w:.1f} per dispatch",
              f"- scale: fetch {kf:.2f} B/unit, write {kw:.2f} B/unit",
-             f"- kernel sources hash: {src_hash}", "",
-             "| stage | dispatches | fetch bytes | write bytes | HBM bytes / launch | algorithmic bytes | ratio |",
-             "|---|---|---|---|---|---|---|"]
+             "- source hash per stage: of the files defining that stage's kernels (plus common.hpp",
+             "  and kernels.hpp); bench.py reports traffic only while it matches", "",
+             "| stage | dispatches | fetch bytes | write bytes | HBM bytes / launch | algorithmic bytes | ratio | source hash |",
+             "|---|---|---|---|---|---|---|---|"]
     T = None
     from sparse_mixture_experts_expert_amd import inputs
     T = inputs.WORKLOADS[wl].tokens
@@ -450,7 +460,8 @@ def traffic_summary(args):
         fb, wb = f * kf, w * kw
         _, alg = stage_model(stage, T, touched)
         ratio = f"{(fb + wb) / alg:.3f}" if alg else "-"
-        lines.append(f"| {stage} | {nf} | {fb:.4g} | {wb:.4g} | {fb + wb:.4g} | {alg:.4g} | {ratio} |")
+        src_hash = kernel_source_hash(stage)
+        lines.append(f"| {stage} | {nf} | {fb:.4g} | {wb:.4g} | {fb + wb:.4g} | {alg:.4g} | {ratio} | {src_hash} |")
         rec = {"workload": wl, "stage": stage, "hbm_bytes_per_launch": round(fb + wb),
                "fetch_bytes": round(fb), "write_bytes": round(wb), "algorithmic_bytes": alg,
                "source_hash": src_hash, "copy_scale_fetch": kf, "copy_scale_write": kw}
@@ -470,7 +481,7 @@ def stats_summary(args):
     if not fs:
         raise SystemExit(f"no kernel_stats.csv under {args.stats_dir}")
     rows = list(csv.DictReader(open(fs[0])))
-    lines = [f"# Kernel durations, {args.workload}", "",
+    lines = [f"# Kernel durations, {args.workload}{' (' + args.profile_label + ')' if args.profile_label else ''}", "",
              "rocprofv3 --kernel-trace --stats; durations in microseconds per dispatch.", "",
              "| kernel | stage | calls | average | min | max |", "|---|---|---|---|---|---|"]
     for r in rows:
@@ -489,7 +500,8 @@ def stats_summary(args):
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     lines += ["", f"kernel sources hash: {kernel_source_hash()}", "",
               "Command (from the repository root, TMPDIR=/tmp):", "", "```"] + args.commands + ["```", ""]
-    with open(os.path.join(ROOT, "profiles", f"kernels_{args.workload}.md"), "w") as fh:
+    name = f"kernels_{args.profile_label + '_' if args.profile_label else ''}{args.workload}.md"
+    with open(os.path.join(ROOT, "profiles", name), "w") as fh:
         fh.write("\n".join(lines))
     print("\n".join(lines))
 
@@ -509,6 +521,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="run the counter-calibration copy and exit")
     ap.add_argument("--traffic-summary", action="store_true", help="summarise --pmc runs into profiles/")
     ap.add_argument("--stats-summary", metavar="DIR", dest="stats_dir", help="summarise a --stats run")
+    ap.add_argument("--profile-label", default="", help="extra word in the kernel summary's file name")
     ap.add_argument("--fetch-dir")
     ap.add_argument("--write-dir")
     ap.add_argument("--copy-fetch-dir")
