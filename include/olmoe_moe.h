@@ -47,7 +47,7 @@ extern "C" {
 #define OLMOE_API
 #endif
 
-#define OLMOE_ABI_VERSION 5
+#define OLMOE_ABI_VERSION 6
 
 #define OLMOE_D 2048 /* hidden size */
 #define OLMOE_F 1024 /* expert width (SwiGLU intermediate size) */
@@ -172,6 +172,37 @@ OLMOE_API olmoe_status_t olmoe_moe_forward_residual(const void* x, const float* 
                                           int32_t* expert_counts, float* aux_loss, float* z_loss,
                                           uint32_t route_flags, uint64_t keep_mask,
                                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Training pair for the default router (token choice): a forward that keeps its
+ * state, and a backward that starts from it instead of recomputing the forward.
+ *
+ * olmoe_moe_forward_train: the layer exactly as olmoe_moe_forward (same outputs,
+ * bit for bit), which also leaves in `saved` the routing, the probabilities and
+ * lse, the fp32 pre-activations G = x W_gate^T and U = x W_up^T of every routed row,
+ * and the expert outputs.  saved: device buffer of at least
+ * olmoe_moe_saved_bytes(T) bytes (the backward workspace size), 256-byte aligned,
+ * not overlapping any argument.
+ *
+ * olmoe_moe_backward_saved: the gradients of olmoe_moe_backward (same results, bit
+ * for bit) from `saved` as the last olmoe_moe_forward_train left it for the same x,
+ * weights and T; the caller keeps that pairing (the library cannot detect a
+ * mismatch, and results are then meaningless).  saved is used as the backward's
+ * workspace, so its forward state is consumed: run olmoe_moe_forward_train again
+ * before another olmoe_moe_backward_saved.
+ * Errors: as olmoe_moe_forward / olmoe_moe_backward (EWORKSPACE for a NULL or
+ * short `saved`). */
+OLMOE_API size_t olmoe_moe_saved_bytes(int64_t T);   /* 0 for T out of range; host only */
+OLMOE_API olmoe_status_t olmoe_moe_forward_train(const void* x, const float* W_router, const void* W_gate,
+                                       const void* W_up, const void* W_down, int64_t T, void* out,
+                                       int32_t* route_ids, float* route_probs,
+                                       int32_t* expert_counts, float* aux_loss, float* z_loss,
+                                       void* saved, size_t saved_bytes, void* stream);
+OLMOE_API olmoe_status_t olmoe_moe_backward_saved(const void* x, const float* W_router, const void* W_gate,
+                                        const void* W_up, const void* W_down, int64_t T,
+                                        const void* dout, float g_aux, float g_z, float* dx,
+                                        float* dW_router, float* dW_gate, float* dW_up,
+                                        float* dW_down, void* saved, size_t saved_bytes,
+                                        void* stream);
 
 /* Expert-choice routing: the experts choose their tokens ("OLMoE: Open
  * Mixture-of-Experts Language Models", section 4.1.4, where it is compared with

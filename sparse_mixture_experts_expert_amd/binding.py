@@ -68,6 +68,13 @@ def lib() -> ctypes.CDLL:
     L.olmoe_moe_backward_expert_choice.restype = i32
     L.olmoe_moe_backward_expert_choice.argtypes = [vp, vp, vp, vp, vp, i64, vp, ctypes.c_float, ctypes.c_float, vp,
                                                    vp, vp, vp, vp, vp, sz, vp]
+    L.olmoe_moe_saved_bytes.restype = sz
+    L.olmoe_moe_saved_bytes.argtypes = [i64]
+    L.olmoe_moe_forward_train.restype = i32
+    L.olmoe_moe_forward_train.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.olmoe_moe_backward_saved.restype = i32
+    L.olmoe_moe_backward_saved.argtypes = [vp, vp, vp, vp, vp, i64, vp, ctypes.c_float, ctypes.c_float, vp, vp, vp,
+                                           vp, vp, vp, sz, vp]
     L.olmoe_rmsnorm_bf16.restype = i32
     L.olmoe_rmsnorm_bf16.argtypes = [vp, ctypes.c_float, i64, vp, vp]
     L.olmoe_residual_add.restype = i32
@@ -260,6 +267,56 @@ def moe_forward_expert_choice(x, w_router, w_gate, w_up, w_down, *, out=None, ch
         _ptr(workspace), workspace.numel(), _stream(stream)))
     return {"out": out, "choice_tokens": choice_tokens, "choice_probs": choice_probs,
             "token_counts": token_counts, "aux_loss": aux_loss, "z_loss": z_loss, "workspace": workspace}
+
+
+def saved_bytes(T: int) -> int:
+    return int(lib().olmoe_moe_saved_bytes(int(T)))
+
+
+def moe_forward_train(x, w_router, w_gate, w_up, w_down, *, saved=None, out=None, route_ids=None,
+                      route_probs=None, expert_counts=None, aux_loss=None, z_loss=None, stream=None):
+    """olmoe_moe_forward_train: the layer's forward, keeping its state in `saved` (allocated
+    when missing, olmoe_moe_saved_bytes(T)) for moe_backward_saved.  Returns a dict of the
+    outputs and `saved`."""
+    import torch
+    T = x.shape[0]
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, D))
+    _need(w_router, "w_router", torch.float32, (E, D))
+    _need(w_gate, "w_gate", torch.bfloat16, (E, F, D))
+    _need(w_up, "w_up", torch.bfloat16, (E, F, D))
+    _need(w_down, "w_down", torch.bfloat16, (E, D, F))
+    out = out if out is not None else torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    if saved is None:
+        saved = torch.empty(max(saved_bytes(T), 256), dtype=torch.uint8, device=dev)
+    _check(lib().olmoe_moe_forward_train(
+        _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), int(T), _ptr(out), _ptr(route_ids),
+        _ptr(route_probs), _ptr(expert_counts), _ptr(aux_loss), _ptr(z_loss), _ptr(saved), saved.numel(),
+        _stream(stream)))
+    return {"out": out, "route_ids": route_ids, "route_probs": route_probs, "expert_counts": expert_counts,
+            "aux_loss": aux_loss, "z_loss": z_loss, "saved": saved}
+
+
+def moe_backward_saved(x, w_router, w_gate, w_up, w_down, dout, saved, *, g_aux: float = 1.0, g_z: float = 1.0,
+                       dx=None, dw_router=None, dw_gate=None, dw_up=None, dw_down=None, stream=None):
+    """olmoe_moe_backward_saved: the gradients of moe_backward from the state moe_forward_train left
+    in `saved` for the same x and weights (which this call consumes)."""
+    import torch
+    T = x.shape[0]
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, D))
+    _need(dout, "dout", torch.bfloat16, (T, D))
+    f32 = torch.float32
+    dx = dx if dx is not None else torch.empty((T, D), dtype=f32, device=dev)
+    dw_router = dw_router if dw_router is not None else torch.empty((E, D), dtype=f32, device=dev)
+    dw_gate = dw_gate if dw_gate is not None else torch.empty((E, F, D), dtype=f32, device=dev)
+    dw_up = dw_up if dw_up is not None else torch.empty((E, F, D), dtype=f32, device=dev)
+    dw_down = dw_down if dw_down is not None else torch.empty((E, D, F), dtype=f32, device=dev)
+    _check(lib().olmoe_moe_backward_saved(
+        _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), int(T), _ptr(dout),
+        ctypes.c_float(g_aux), ctypes.c_float(g_z), _ptr(dx), _ptr(dw_router), _ptr(dw_gate), _ptr(dw_up),
+        _ptr(dw_down), _ptr(saved), saved.numel(), _stream(stream)))
+    return {"dx": dx, "dw_router": dw_router, "dw_gate": dw_gate, "dw_up": dw_up, "dw_down": dw_down}
 
 
 def ec_backward_workspace_bytes(T: int) -> int:

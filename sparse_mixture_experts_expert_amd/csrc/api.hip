@@ -429,6 +429,118 @@ olmoe_status_t backward_checks(const void* x, const float* W_router, const void*
   return check_device();
 }
 
+// the backward's forward part (token choice, default router): routing, the gate/up GEMM keeping
+// the fp32 pre-activations G | U, and the down GEMM, all into the backward layout B
+olmoe_status_t bwd_forward_state(const void* x, const float* W_router, const void* W_gate, const void* W_up,
+                                 const void* W_down, int Ti, char* ws, const BwdLayout& B, int32_t* expert_counts,
+                                 float* aux_loss, float* z_loss, hipStream_t s) {
+  const Layout& L = B.f;
+  const GemmPlan plan = plan_gemm(Ti);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
+  float* probs = reinterpret_cast<float*>(ws + L.probs);
+  RouterArgs ra{static_cast<const uint16_t*>(x), W_router, Ti, reinterpret_cast<float2*>(ws + L.partial),
+                reinterpret_cast<uint16_t*>(ws + L.planes)};
+  SelectArgs se{reinterpret_cast<const float2*>(ws + L.partial), Ti, ids, probs,
+                reinterpret_cast<uint8_t*>(ws + L.lrank), reinterpret_cast<int32_t*>(ws + L.blk_counts),
+                reinterpret_cast<float*>(ws + L.blk_psum), reinterpret_cast<float*>(ws + L.blk_lse2),
+                OLMOE_KEEP_ALL, 0, reinterpret_cast<float*>(ws + B.p_all), reinterpret_cast<float*>(ws + B.lse)};
+  ScanArgs sa{Ti,
+              reinterpret_cast<const int32_t*>(ws + L.blk_counts),
+              reinterpret_cast<const float*>(ws + L.blk_psum),
+              reinterpret_cast<const float*>(ws + L.blk_lse2),
+              reinterpret_cast<int32_t*>(ws + L.blk_base),
+              reinterpret_cast<int32_t*>(ws + L.offsets),
+              reinterpret_cast<int32_t*>(ws + L.tp_gu), reinterpret_cast<int2*>(ws + L.tiles_gu), plan.bm_gu,
+              reinterpret_cast<int32_t*>(ws + L.tp_dn), reinterpret_cast<int2*>(ws + L.tiles_dn), plan.bm_dn,
+              expert_counts, aux_loss, z_loss};
+  PermuteArgs pa{Ti, ids, reinterpret_cast<const uint8_t*>(ws + L.lrank),
+                 reinterpret_cast<const int32_t*>(ws + L.blk_base), reinterpret_cast<int32_t*>(ws + L.perm),
+                 reinterpret_cast<int32_t*>(ws + L.inv), probs, reinterpret_cast<float*>(ws + B.row_w)};
+  hipError_t he = launch_router_partial(ra, s);
+  if (he == hipSuccess) he = launch_router_select(se, s);
+  if (he == hipSuccess) {
+    if (Ti <= SMALL_TOKENS) {
+      he = launch_scan_permute(sa, pa, s);
+    } else {
+      he = launch_scan(sa, s);
+      if (he == hipSuccess) he = launch_permute(pa, s);
+    }
+  }
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "routing launch: %s", hipGetErrorString(he));
+  const int32_t* perm = reinterpret_cast<const int32_t*>(ws + L.perm);
+  const int32_t* offsets = reinterpret_cast<const int32_t*>(ws + L.offsets);
+  if (Ti > 0) {
+    GemmArgs ga{Ti,
+                static_cast<const uint16_t*>(x),
+                static_cast<const uint16_t*>(W_gate),
+                static_cast<const uint16_t*>(W_up),
+                static_cast<const uint16_t*>(W_down),
+                perm, offsets,
+                reinterpret_cast<const int32_t*>(ws + L.tp_gu),
+                reinterpret_cast<const int32_t*>(ws + L.tp_dn),
+                reinterpret_cast<const int2*>(ws + L.tiles_gu),
+                reinterpret_cast<const int2*>(ws + L.tiles_dn),
+                reinterpret_cast<uint16_t*>(ws + L.h),
+                reinterpret_cast<uint16_t*>(ws + L.y),
+                reinterpret_cast<float*>(ws + B.gu)};
+    he = launch_gateup(ga, plan, s);
+    if (he == hipSuccess) he = launch_down(ga, plan, s);
+    if (he != hipSuccess) return fail(OLMOE_EHIP, "forward GEMM launch: %s", hipGetErrorString(he));
+  }
+  return OLMOE_OK;
+}
+
+// the gradients from the state bwd_forward_state left in B
+olmoe_status_t bwd_gradients(const void* x, const float* W_router, const void* W_gate, const void* W_up,
+                             const void* W_down, int Ti, const void* dout, float g_aux, float g_z, float* dx,
+                             float* dW_router, float* dW_gate, float* dW_up, float* dW_down, char* ws,
+                             const BwdLayout& B, hipStream_t s) {
+  const Layout& L = B.f;
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
+  const int32_t* perm = reinterpret_cast<const int32_t*>(ws + L.perm);
+  const int32_t* offsets = reinterpret_cast<const int32_t*>(ws + L.offsets);
+  hipError_t he = hipSuccess;
+  BwdSmallArgs ba{Ti, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dout), W_router, ids,
+                  reinterpret_cast<const float*>(ws + B.p_all), reinterpret_cast<const float*>(ws + B.lse),
+                  offsets, perm, reinterpret_cast<const int32_t*>(ws + L.inv),
+                  reinterpret_cast<const uint16_t*>(ws + L.y), g_aux, g_z,
+                  reinterpret_cast<float*>(ws + B.dlogits), reinterpret_cast<uint16_t*>(ws + B.xg),
+                  reinterpret_cast<uint16_t*>(ws + B.dg), reinterpret_cast<const float*>(ws + B.dxr), dx,
+                  reinterpret_cast<float*>(ws + B.dwr_part), dW_router, reinterpret_cast<uint16_t*>(ws + B.zero),
+                  reinterpret_cast<int32_t*>(ws + B.tp_bwd), reinterpret_cast<int2*>(ws + B.tiles_bwd)};
+  he = launch_bwd_prepare(ba, s);
+  if (he == hipSuccess) he = launch_bwd_router(ba, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "backward routing launch: %s", hipGetErrorString(he));
+  const uint16_t* dgu = reinterpret_cast<const uint16_t*>(ws + B.dgu);
+  if (Ti > 0) {
+    BwdDgradArgs dh{reinterpret_cast<const uint16_t*>(ws + B.dg), nullptr, static_cast<const uint16_t*>(W_down),
+                    nullptr, OLMOE_F, (long)OLMOE_D * OLMOE_F, 2 * OLMOE_F,
+                    reinterpret_cast<const int32_t*>(ws + B.tp_bwd) + OLMOE_E,
+                    reinterpret_cast<const int2*>(ws + B.tiles_bwd),
+                    reinterpret_cast<const float*>(ws + B.row_w), reinterpret_cast<const float*>(ws + B.gu),
+                    reinterpret_cast<uint16_t*>(ws + B.dgu), reinterpret_cast<uint16_t*>(ws + B.hw), nullptr};
+    BwdDgradArgs dxa{dgu, nullptr, static_cast<const uint16_t*>(W_gate), static_cast<const uint16_t*>(W_up),
+                     OLMOE_D, (long)OLMOE_F * OLMOE_D, OLMOE_F,
+                     reinterpret_cast<const int32_t*>(ws + B.tp_bwd) + OLMOE_E,
+                     reinterpret_cast<const int2*>(ws + B.tiles_bwd), nullptr, nullptr, nullptr, nullptr,
+                     reinterpret_cast<float*>(ws + B.dxr)};
+    he = launch_dgrad(dh, Ti, true, s);
+    if (he == hipSuccess) he = launch_dgrad(dxa, Ti, false, s);
+    if (he != hipSuccess) return fail(OLMOE_EHIP, "dgrad launch: %s", hipGetErrorString(he));
+  }
+  BwdWgradArgs wd{reinterpret_cast<const uint16_t*>(ws + B.dg), OLMOE_D, reinterpret_cast<const uint16_t*>(ws + B.hw),
+                  OLMOE_F, offsets, reinterpret_cast<const uint16_t*>(ws + B.zero), OLMOE_D, OLMOE_F, dW_down, dW_down,
+                  OLMOE_D, (long)OLMOE_D * OLMOE_F};
+  BwdWgradArgs wgu{dgu, 2 * OLMOE_F, reinterpret_cast<const uint16_t*>(ws + B.xg), OLMOE_D, offsets,
+                   reinterpret_cast<const uint16_t*>(ws + B.zero), 2 * OLMOE_F, OLMOE_D, dW_gate, dW_up, OLMOE_F,
+                   (long)OLMOE_F * OLMOE_D};
+  he = launch_wgrad(wd, s);
+  if (he == hipSuccess) he = launch_wgrad(wgu, s);
+  if (he == hipSuccess) he = launch_bwd_finish(ba, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "weight-gradient launch: %s", hipGetErrorString(he));
+  return ok();
+}
+
 // expert-choice backward workspace: the expert-choice forward layout, then the backward's buffers
 // for its 64C rows
 struct EcBwdLayout {
@@ -482,103 +594,87 @@ olmoe_status_t olmoe_moe_backward(const void* x, const float* W_router, const vo
   olmoe_status_t st = backward_checks(x, W_router, W_gate, W_up, W_down, T, dout, g_aux, g_z, dx, dW_router, dW_gate,
                                       dW_up, dW_down, workspace, workspace_bytes, B.total);
   if (st != OLMOE_OK) return st;
-
   // ---- launches: recompute the forward (keeping p, lse, G, U, Y), then the gradients
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
+  st = bwd_forward_state(x, W_router, W_gate, W_up, W_down, static_cast<int>(T), ws, B, nullptr, nullptr, nullptr, s);
+  if (st != OLMOE_OK) return st;
+  return bwd_gradients(x, W_router, W_gate, W_up, W_down, static_cast<int>(T), dout, g_aux, g_z, dx, dW_router,
+                       dW_gate, dW_up, dW_down, ws, B, s);
+}
+
+size_t olmoe_moe_saved_bytes(int64_t T) { return olmoe_moe_backward_workspace_bytes(T); }
+
+olmoe_status_t olmoe_moe_forward_train(const void* x, const float* W_router, const void* W_gate, const void* W_up,
+                                       const void* W_down, int64_t T, void* out, int32_t* route_ids,
+                                       float* route_probs, int32_t* expert_counts, float* aux_loss, float* z_loss,
+                                       void* saved, size_t saved_bytes, void* stream) {
+  // ---- host-side checks; nothing is enqueued unless all pass
+  if (T < 0 || T > OLMOE_MAX_TOKENS)
+    return fail(OLMOE_EINVAL, "T=%lld out of range [0, %lld]", (long long)T, (long long)OLMOE_MAX_TOKENS);
+  if (!W_router || !W_gate || !W_up || !W_down) return fail(OLMOE_EINVAL, "a weight pointer is NULL");
+  if (T > 0 && (!x || !out)) return fail(OLMOE_EINVAL, "x or out is NULL");
+  const void* ptrs[] = {x, W_router, W_gate, W_up, W_down, out, route_ids, route_probs, expert_counts};
+  const char* names[] = {"x", "W_router", "W_gate", "W_up", "W_down", "out", "route_ids", "route_probs",
+                         "expert_counts"};
+  for (int i = 0; i < 9; ++i)
+    if (ptrs[i] && misaligned(ptrs[i])) return fail(OLMOE_EINVAL, "%s is not 16-byte aligned", names[i]);
+  if ((aux_loss && misaligned(aux_loss, 4)) || (z_loss && misaligned(z_loss, 4)))
+    return fail(OLMOE_EINVAL, "aux_loss / z_loss not 4-byte aligned");
+  const BwdLayout B = make_bwd_layout(T);
+  if (!saved) return fail(OLMOE_EWORKSPACE, "saved is NULL");
+  if (misaligned(saved, 256)) return fail(OLMOE_EINVAL, "saved is not 256-byte aligned");
+  if (saved_bytes < B.total)
+    return fail(OLMOE_EWORKSPACE, "saved has %zu bytes, %zu needed for T=%lld", saved_bytes, B.total, (long long)T);
+  const size_t act = static_cast<size_t>(T) * OLMOE_D * 2;
+  const size_t wexp = static_cast<size_t>(OLMOE_E) * OLMOE_F * OLMOE_D * 2;
+  const size_t wr_bytes = (size_t)OLMOE_E * OLMOE_D * 4;
+  const size_t rows = static_cast<size_t>(T) * OLMOE_K * 4;
+  const void* ins[] = {x, W_router, W_gate, W_up, W_down};
+  const size_t in_n[] = {act, wr_bytes, wexp, wexp, wexp};
+  void* outs[] = {out, route_ids, route_probs, expert_counts, aux_loss, z_loss};
+  const size_t out_n[] = {act, rows, rows, OLMOE_E * 4, 4, 4};
+  for (int o = 0; o < 6; ++o) {
+    for (int i = 0; i < 5; ++i)
+      if (overlaps(outs[o], out_n[o], ins[i], in_n[i])) return fail(OLMOE_EINVAL, "an output overlaps an input");
+    for (int q = o + 1; q < 6; ++q)
+      if (overlaps(outs[o], out_n[o], outs[q], out_n[q])) return fail(OLMOE_EINVAL, "two outputs overlap");
+    if (overlaps(outs[o], out_n[o], saved, B.total)) return fail(OLMOE_EINVAL, "an output overlaps saved");
+  }
+  olmoe_status_t st = check_device();
+  if (st != OLMOE_OK) return st;
+  // ---- launches: the backward's forward part (routing, G | U kept, Y), then the weighted sum
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(saved);
   const Layout& L = B.f;
-  const int Ti = static_cast<int>(T);
-  const GemmPlan plan = plan_gemm(Ti);
-  int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
-  float* probs = reinterpret_cast<float*>(ws + L.probs);
-  RouterArgs ra{static_cast<const uint16_t*>(x), W_router, Ti, reinterpret_cast<float2*>(ws + L.partial),
-                reinterpret_cast<uint16_t*>(ws + L.planes)};
-  SelectArgs se{reinterpret_cast<const float2*>(ws + L.partial), Ti, ids, probs,
-                reinterpret_cast<uint8_t*>(ws + L.lrank), reinterpret_cast<int32_t*>(ws + L.blk_counts),
-                reinterpret_cast<float*>(ws + L.blk_psum), reinterpret_cast<float*>(ws + L.blk_lse2),
-                OLMOE_KEEP_ALL, 0, reinterpret_cast<float*>(ws + B.p_all), reinterpret_cast<float*>(ws + B.lse)};
-  ScanArgs sa{Ti,
-              reinterpret_cast<const int32_t*>(ws + L.blk_counts),
-              reinterpret_cast<const float*>(ws + L.blk_psum),
-              reinterpret_cast<const float*>(ws + L.blk_lse2),
-              reinterpret_cast<int32_t*>(ws + L.blk_base),
-              reinterpret_cast<int32_t*>(ws + L.offsets),
-              reinterpret_cast<int32_t*>(ws + L.tp_gu), reinterpret_cast<int2*>(ws + L.tiles_gu), plan.bm_gu,
-              reinterpret_cast<int32_t*>(ws + L.tp_dn), reinterpret_cast<int2*>(ws + L.tiles_dn), plan.bm_dn,
-              nullptr, nullptr, nullptr};
-  PermuteArgs pa{Ti, ids, reinterpret_cast<const uint8_t*>(ws + L.lrank),
-                 reinterpret_cast<const int32_t*>(ws + L.blk_base), reinterpret_cast<int32_t*>(ws + L.perm),
-                 reinterpret_cast<int32_t*>(ws + L.inv), probs, reinterpret_cast<float*>(ws + B.row_w)};
-  hipError_t he = launch_router_partial(ra, s);
-  if (he == hipSuccess) he = launch_router_select(se, s);
-  if (he == hipSuccess) {
-    if (Ti <= SMALL_TOKENS) {
-      he = launch_scan_permute(sa, pa, s);
-    } else {
-      he = launch_scan(sa, s);
-      if (he == hipSuccess) he = launch_permute(pa, s);
-    }
-  }
-  if (he != hipSuccess) return fail(OLMOE_EHIP, "routing launch: %s", hipGetErrorString(he));
-  const int32_t* perm = reinterpret_cast<const int32_t*>(ws + L.perm);
-  const int32_t* offsets = reinterpret_cast<const int32_t*>(ws + L.offsets);
-  if (Ti > 0) {
-    GemmArgs ga{Ti,
-                static_cast<const uint16_t*>(x),
-                static_cast<const uint16_t*>(W_gate),
-                static_cast<const uint16_t*>(W_up),
-                static_cast<const uint16_t*>(W_down),
-                perm, offsets,
-                reinterpret_cast<const int32_t*>(ws + L.tp_gu),
-                reinterpret_cast<const int32_t*>(ws + L.tp_dn),
-                reinterpret_cast<const int2*>(ws + L.tiles_gu),
-                reinterpret_cast<const int2*>(ws + L.tiles_dn),
-                reinterpret_cast<uint16_t*>(ws + L.h),
-                reinterpret_cast<uint16_t*>(ws + L.y),
-                reinterpret_cast<float*>(ws + B.gu)};
-    he = launch_gateup(ga, plan, s);
-    if (he == hipSuccess) he = launch_down(ga, plan, s);
-    if (he != hipSuccess) return fail(OLMOE_EHIP, "forward GEMM launch: %s", hipGetErrorString(he));
-  }
-  BwdSmallArgs ba{Ti, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dout), W_router, ids,
-                  reinterpret_cast<const float*>(ws + B.p_all), reinterpret_cast<const float*>(ws + B.lse),
-                  offsets, perm, reinterpret_cast<const int32_t*>(ws + L.inv),
-                  reinterpret_cast<const uint16_t*>(ws + L.y), g_aux, g_z,
-                  reinterpret_cast<float*>(ws + B.dlogits), reinterpret_cast<uint16_t*>(ws + B.xg),
-                  reinterpret_cast<uint16_t*>(ws + B.dg), reinterpret_cast<const float*>(ws + B.dxr), dx,
-                  reinterpret_cast<float*>(ws + B.dwr_part), dW_router, reinterpret_cast<uint16_t*>(ws + B.zero),
-                  reinterpret_cast<int32_t*>(ws + B.tp_bwd), reinterpret_cast<int2*>(ws + B.tiles_bwd)};
-  he = launch_bwd_prepare(ba, s);
-  if (he == hipSuccess) he = launch_bwd_router(ba, s);
-  if (he != hipSuccess) return fail(OLMOE_EHIP, "backward routing launch: %s", hipGetErrorString(he));
-  const uint16_t* dgu = reinterpret_cast<const uint16_t*>(ws + B.dgu);
-  if (Ti > 0) {
-    BwdDgradArgs dh{reinterpret_cast<const uint16_t*>(ws + B.dg), nullptr, static_cast<const uint16_t*>(W_down),
-                    nullptr, OLMOE_F, (long)OLMOE_D * OLMOE_F, 2 * OLMOE_F,
-                    reinterpret_cast<const int32_t*>(ws + B.tp_bwd) + OLMOE_E,
-                    reinterpret_cast<const int2*>(ws + B.tiles_bwd),
-                    reinterpret_cast<const float*>(ws + B.row_w), reinterpret_cast<const float*>(ws + B.gu),
-                    reinterpret_cast<uint16_t*>(ws + B.dgu), reinterpret_cast<uint16_t*>(ws + B.hw), nullptr};
-    BwdDgradArgs dxa{dgu, nullptr, static_cast<const uint16_t*>(W_gate), static_cast<const uint16_t*>(W_up),
-                     OLMOE_D, (long)OLMOE_F * OLMOE_D, OLMOE_F,
-                     reinterpret_cast<const int32_t*>(ws + B.tp_bwd) + OLMOE_E,
-                     reinterpret_cast<const int2*>(ws + B.tiles_bwd), nullptr, nullptr, nullptr, nullptr,
-                     reinterpret_cast<float*>(ws + B.dxr)};
-    he = launch_dgrad(dh, Ti, true, s);
-    if (he == hipSuccess) he = launch_dgrad(dxa, Ti, false, s);
-    if (he != hipSuccess) return fail(OLMOE_EHIP, "dgrad launch: %s", hipGetErrorString(he));
-  }
-  BwdWgradArgs wd{reinterpret_cast<const uint16_t*>(ws + B.dg), OLMOE_D, reinterpret_cast<const uint16_t*>(ws + B.hw),
-                  OLMOE_F, offsets, reinterpret_cast<const uint16_t*>(ws + B.zero), OLMOE_D, OLMOE_F, dW_down, dW_down,
-                  OLMOE_D, (long)OLMOE_D * OLMOE_F};
-  BwdWgradArgs wgu{dgu, 2 * OLMOE_F, reinterpret_cast<const uint16_t*>(ws + B.xg), OLMOE_D, offsets,
-                   reinterpret_cast<const uint16_t*>(ws + B.zero), 2 * OLMOE_F, OLMOE_D, dW_gate, dW_up, OLMOE_F,
-                   (long)OLMOE_F * OLMOE_D};
-  he = launch_wgrad(wd, s);
-  if (he == hipSuccess) he = launch_wgrad(wgu, s);
-  if (he == hipSuccess) he = launch_bwd_finish(ba, s);
-  if (he != hipSuccess) return fail(OLMOE_EHIP, "weight-gradient launch: %s", hipGetErrorString(he));
+  st = bwd_forward_state(x, W_router, W_gate, W_up, W_down, static_cast<int>(T), ws, B, expert_counts, aux_loss,
+                         z_loss, s);
+  if (st != OLMOE_OK) return st;
+  if (T == 0) return ok();
+  hipError_t he = hipSuccess;
+  if (route_ids) he = hipMemcpyAsync(route_ids, ws + L.ids, rows, hipMemcpyDeviceToDevice, s);
+  if (he == hipSuccess && route_probs) he = hipMemcpyAsync(route_probs, ws + L.probs, rows, hipMemcpyDeviceToDevice, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "routing copy: %s", hipGetErrorString(he));
+  CombineArgs ca{static_cast<int>(T), reinterpret_cast<const uint16_t*>(ws + L.y),
+                 reinterpret_cast<const int32_t*>(ws + L.inv), reinterpret_cast<const float*>(ws + L.probs),
+                 static_cast<uint16_t*>(out), nullptr, nullptr, 0.f};
+  he = launch_combine(ca, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "combine launch: %s", hipGetErrorString(he));
   return ok();
+}
+
+olmoe_status_t olmoe_moe_backward_saved(const void* x, const float* W_router, const void* W_gate, const void* W_up,
+                                        const void* W_down, int64_t T, const void* dout, float g_aux, float g_z,
+                                        float* dx, float* dW_router, float* dW_gate, float* dW_up, float* dW_down,
+                                        void* saved, size_t saved_bytes, void* stream) {
+  if (T < 0 || T > OLMOE_MAX_TOKENS)
+    return fail(OLMOE_EINVAL, "T=%lld out of range [0, %lld]", (long long)T, (long long)OLMOE_MAX_TOKENS);
+  const BwdLayout B = make_bwd_layout(T);
+  olmoe_status_t st = backward_checks(x, W_router, W_gate, W_up, W_down, T, dout, g_aux, g_z, dx, dW_router, dW_gate,
+                                      dW_up, dW_down, saved, saved_bytes, B.total);
+  if (st != OLMOE_OK) return st;
+  return bwd_gradients(x, W_router, W_gate, W_up, W_down, static_cast<int>(T), dout, g_aux, g_z, dx, dW_router,
+                       dW_gate, dW_up, dW_down, static_cast<char*>(saved), B, static_cast<hipStream_t>(stream));
 }
 
 size_t olmoe_moe_ec_workspace_bytes(int64_t T) {

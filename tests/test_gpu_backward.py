@@ -172,3 +172,32 @@ def test_expert_choice_backward_bitwise_reproducible(weights):
     torch.cuda.synchronize()
     for k in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down"):
         assert torch.equal(a[k], b[k]), k
+
+
+# ------------------------------------------------------------------ training pair
+
+
+@pytest.mark.parametrize("T", [0, 1, 200, 700, 4096])
+def test_training_pair_equals_stateless_calls(weights, T):
+    """olmoe_moe_forward_train gives olmoe_moe_forward's outputs and olmoe_moe_backward_saved
+    olmoe_moe_backward's gradients, bit for bit (the same kernels in the same order)."""
+    w, _ = weights
+    _log(f"training pair T={T}")
+    x = inputs.device_x(T, seed=50 + T, workload="parity")
+    dout = inputs.device_x(T, seed=60 + T, workload="parity")
+    i32, f32 = torch.int32, torch.float32
+    ref = binding.moe_forward(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"])
+    got = dict(route_ids=torch.empty((T, 8), dtype=i32, device="cuda"),
+               route_probs=torch.empty((T, 8), dtype=f32, device="cuda"),
+               expert_counts=torch.empty(64, dtype=i32, device="cuda"),
+               aux_loss=torch.empty(1, dtype=f32, device="cuda"), z_loss=torch.empty(1, dtype=f32, device="cuda"))
+    tr = binding.moe_forward_train(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], **got)
+    torch.cuda.synchronize()
+    for k in ("out", "route_ids", "route_probs", "expert_counts", "aux_loss", "z_loss"):
+        assert torch.equal(tr[k], ref[k]), k
+    b_ref = binding.moe_backward(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], dout, g_aux=2.0, g_z=0.5)
+    b = binding.moe_backward_saved(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], dout, tr["saved"],
+                                   g_aux=2.0, g_z=0.5)
+    torch.cuda.synchronize()
+    for k in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down"):
+        assert torch.equal(b[k], b_ref[k]), k

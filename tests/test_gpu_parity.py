@@ -292,10 +292,10 @@ def sampled_check(g, hw, ref_rt, n, seed, label, extra_rows=()):
     return rel, mx
 
 
-def full_size_layer(name):
+def full_size_layer(name, tokens=None):
     wl = inputs.WORKLOADS[name]
     t0 = time.time()
-    d = inputs.device_workload(name, seed=0)
+    d = inputs.device_workload(name, seed=0, tokens=tokens)
     g = run_layer(d["x"], d)
     hw = {k: (d[k].cpu().numpy() if d[k].dtype == torch.float32 else parity.bf16_tensor_to_bits(d[k]))
           for k in ("w_router", "w_gate", "w_up", "w_down")}
@@ -307,7 +307,8 @@ def full_size_layer(name):
     parity.check_losses(float(g["aux_loss"][0]), float(g["z_loss"][0]), aux, z, name)
     extra = np.nonzero(ref["gap"] < parity.GAP_TOL)[0][:8]
     if wl.scaled_rows_frac:
-        extra = np.concatenate([extra, inputs._scaled_rows(0, name, wl.tokens, wl.scaled_rows_frac)[:8]])
+        T_run = g["route_ids"].shape[0]
+        extra = np.concatenate([extra, inputs._scaled_rows(0, name, T_run, wl.scaled_rows_frac)[:8]])
     rel, mx = sampled_check(g, hw, ref, 40, 1, name, extra)
     _log(f"{name}: ties={ntie} max count={counts.max()} empty={int((counts == 0).sum())} "
          f"sampled relL2={rel:.2e} maxabs/rms={mx:.2e} ({time.time() - t0:.1f}s)")
@@ -320,6 +321,14 @@ def test_full_size_workload(name):
     g = full_size_layer(name)
     if name == "skew-16384":
         assert g["expert_counts"].max() > 4 * (8 * 16384 / 64)
+
+
+def test_largest_batch():
+    """65,536 tokens (the row indices, tile lists and workspace at 16x the prefill batch): routing,
+    dispatch tables and losses in full, the output on sampled tokens."""
+    _log("largest batch 65536")
+    g = full_size_layer("prefill-4096", tokens=65536)
+    assert g["expert_counts"].sum() == 8 * 65536
 
 
 def test_full_size_stack():
