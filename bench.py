@@ -280,6 +280,17 @@ def measure_backward(workload, steps, warmup, seed=0, routing="token"):
     sec = timed([bwd])
     sec_train = timed([fwd, bwd])
     extra = {}
+    if routing == "expert":   # the training pair: the forward keeps its state, the backward starts from it
+        def fwd_train(w):
+            binding.moe_forward_expert_choice_train(d["x"], w["w_router"], w["w_gate"], w["w_up"], w["w_down"],
+                                                    saved=bws, out=y, choice_tokens=ct, token_counts=tc,
+                                                    aux_loss=aux, z_loss=z)
+
+        def bwd_saved(w):
+            binding.moe_backward_expert_choice_saved(d["x"], w["w_router"], w["w_gate"], w["w_up"], w["w_down"],
+                                                     dout, bws, g_aux=1.0, g_z=1.0, **outs)
+        sec_pair = timed([fwd_train, bwd_saved])
+        extra = {"train_step_saved_ms": round(sec_pair * 1e3, 5), "train_saved_tokens_per_s": round(T / sec_pair, 1)}
     if routing == "token":   # the training pair: the forward keeps its state, the backward starts from it
         def fwd_train(w):
             binding.moe_forward_train(d["x"], w["w_router"], w["w_gate"], w["w_up"], w["w_down"], saved=bws, out=y,
@@ -296,8 +307,8 @@ def measure_backward(workload, steps, warmup, seed=0, routing="token"):
             "mfma_frac": round(BWD_FLOP_PER_TOKEN * T / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "train_step_ms": round(sec_train * 1e3, 5), "train_tokens_per_s": round(T / sec_train, 1),
             "note": "backward: gradients of x and all weights, the forward recompute inside timed, not counted "
-                    "in tflops; train step: one forward call + one backward call; train step saved: "
-                    "olmoe_moe_forward_train + olmoe_moe_backward_saved (no recompute)"}
+                    "in tflops; train step: one forward call + one backward call; train step saved: the "
+                    "training pair (forward keeping its state + backward from it, no recompute)"}
 
 
 def measure_expert_choice(workload, steps, warmup, seed=0):

@@ -47,7 +47,7 @@ extern "C" {
 #define OLMOE_API
 #endif
 
-#define OLMOE_ABI_VERSION 6
+#define OLMOE_ABI_VERSION 7
 
 #define OLMOE_D 2048 /* hidden size */
 #define OLMOE_F 1024 /* expert width (SwiGLU intermediate size) */
@@ -255,6 +255,28 @@ OLMOE_API olmoe_status_t olmoe_moe_backward_expert_choice(const void* x, const f
                                                 float g_aux, float g_z, float* dx, float* dW_router,
                                                 float* dW_gate, float* dW_up, float* dW_down,
                                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Training pair of the expert-choice layer, as olmoe_moe_forward_train /
+ * olmoe_moe_backward_saved for token choice: the forward gives
+ * olmoe_moe_forward_expert_choice's outputs bit for bit and keeps its state in
+ * `saved` (at least olmoe_moe_ec_saved_bytes(T) bytes, 256-byte aligned); the
+ * backward gives olmoe_moe_backward_expert_choice's gradients bit for bit from that
+ * state (same x, weights and T; consumed by the call). */
+OLMOE_API size_t olmoe_moe_ec_saved_bytes(int64_t T);   /* 0 for T out of range; host only */
+OLMOE_API olmoe_status_t olmoe_moe_forward_expert_choice_train(const void* x, const float* W_router,
+                                                     const void* W_gate, const void* W_up,
+                                                     const void* W_down, int64_t T, void* out,
+                                                     int32_t* choice_tokens, float* choice_probs,
+                                                     int32_t* token_counts, float* aux_loss,
+                                                     float* z_loss, void* saved, size_t saved_bytes,
+                                                     void* stream);
+OLMOE_API olmoe_status_t olmoe_moe_backward_expert_choice_saved(const void* x, const float* W_router,
+                                                      const void* W_gate, const void* W_up,
+                                                      const void* W_down, int64_t T, const void* dout,
+                                                      float g_aux, float g_z, float* dx,
+                                                      float* dW_router, float* dW_gate, float* dW_up,
+                                                      float* dW_down, void* saved, size_t saved_bytes,
+                                                      void* stream);
 
 /* RMSNorm of the residual stream with unit weight, rounded to the layer's
  * input type: x_out[t] = bf16(h[t] / sqrt(mean_k h[t,k]^2 + eps)), computed in

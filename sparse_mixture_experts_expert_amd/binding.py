@@ -75,6 +75,13 @@ def lib() -> ctypes.CDLL:
     L.olmoe_moe_backward_saved.restype = i32
     L.olmoe_moe_backward_saved.argtypes = [vp, vp, vp, vp, vp, i64, vp, ctypes.c_float, ctypes.c_float, vp, vp, vp,
                                            vp, vp, vp, sz, vp]
+    L.olmoe_moe_ec_saved_bytes.restype = sz
+    L.olmoe_moe_ec_saved_bytes.argtypes = [i64]
+    L.olmoe_moe_forward_expert_choice_train.restype = i32
+    L.olmoe_moe_forward_expert_choice_train.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.olmoe_moe_backward_expert_choice_saved.restype = i32
+    L.olmoe_moe_backward_expert_choice_saved.argtypes = [vp, vp, vp, vp, vp, i64, vp, ctypes.c_float, ctypes.c_float,
+                                                         vp, vp, vp, vp, vp, vp, sz, vp]
     L.olmoe_rmsnorm_bf16.restype = i32
     L.olmoe_rmsnorm_bf16.argtypes = [vp, ctypes.c_float, i64, vp, vp]
     L.olmoe_residual_add.restype = i32
@@ -313,6 +320,52 @@ def moe_backward_saved(x, w_router, w_gate, w_up, w_down, dout, saved, *, g_aux:
     dw_up = dw_up if dw_up is not None else torch.empty((E, F, D), dtype=f32, device=dev)
     dw_down = dw_down if dw_down is not None else torch.empty((E, D, F), dtype=f32, device=dev)
     _check(lib().olmoe_moe_backward_saved(
+        _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), int(T), _ptr(dout),
+        ctypes.c_float(g_aux), ctypes.c_float(g_z), _ptr(dx), _ptr(dw_router), _ptr(dw_gate), _ptr(dw_up),
+        _ptr(dw_down), _ptr(saved), saved.numel(), _stream(stream)))
+    return {"dx": dx, "dw_router": dw_router, "dw_gate": dw_gate, "dw_up": dw_up, "dw_down": dw_down}
+
+
+def ec_saved_bytes(T: int) -> int:
+    return int(lib().olmoe_moe_ec_saved_bytes(int(T)))
+
+
+def moe_forward_expert_choice_train(x, w_router, w_gate, w_up, w_down, *, saved=None, out=None, choice_tokens=None,
+                                    choice_probs=None, token_counts=None, aux_loss=None, z_loss=None, stream=None):
+    """olmoe_moe_forward_expert_choice_train: the expert-choice forward, keeping its state in `saved`
+    (allocated when missing) for moe_backward_expert_choice_saved."""
+    import torch
+    T = x.shape[0]
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, D))
+    out = out if out is not None else torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    if saved is None:
+        saved = torch.empty(max(ec_saved_bytes(T), 256), dtype=torch.uint8, device=dev)
+    _check(lib().olmoe_moe_forward_expert_choice_train(
+        _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), int(T), _ptr(out), _ptr(choice_tokens),
+        _ptr(choice_probs), _ptr(token_counts), _ptr(aux_loss), _ptr(z_loss), _ptr(saved), saved.numel(),
+        _stream(stream)))
+    return {"out": out, "choice_tokens": choice_tokens, "choice_probs": choice_probs, "token_counts": token_counts,
+            "aux_loss": aux_loss, "z_loss": z_loss, "saved": saved}
+
+
+def moe_backward_expert_choice_saved(x, w_router, w_gate, w_up, w_down, dout, saved, *, g_aux: float = 1.0,
+                                     g_z: float = 1.0, dx=None, dw_router=None, dw_gate=None, dw_up=None,
+                                     dw_down=None, stream=None):
+    """olmoe_moe_backward_expert_choice_saved: moe_backward_expert_choice's gradients from the state
+    moe_forward_expert_choice_train left in `saved`."""
+    import torch
+    T = x.shape[0]
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, D))
+    _need(dout, "dout", torch.bfloat16, (T, D))
+    f32 = torch.float32
+    dx = dx if dx is not None else torch.empty((T, D), dtype=f32, device=dev)
+    dw_router = dw_router if dw_router is not None else torch.empty((E, D), dtype=f32, device=dev)
+    dw_gate = dw_gate if dw_gate is not None else torch.empty((E, F, D), dtype=f32, device=dev)
+    dw_up = dw_up if dw_up is not None else torch.empty((E, F, D), dtype=f32, device=dev)
+    dw_down = dw_down if dw_down is not None else torch.empty((E, D, F), dtype=f32, device=dev)
+    _check(lib().olmoe_moe_backward_expert_choice_saved(
         _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), int(T), _ptr(dout),
         ctypes.c_float(g_aux), ctypes.c_float(g_z), _ptr(dx), _ptr(dw_router), _ptr(dw_gate), _ptr(dw_up),
         _ptr(dw_down), _ptr(saved), saved.numel(), _stream(stream)))

@@ -574,6 +574,125 @@ EcBwdLayout make_ec_bwd_layout(int64_t T) {
   return B;
 }
 
+// the expert-choice backward's forward part: routing, the gate/up GEMM keeping G | U, the down
+// GEMM, into the layout B; the selection and loss outputs are optional
+olmoe_status_t ec_bwd_forward_state(const void* x, const float* W_router, const void* W_gate, const void* W_up,
+                                    const void* W_down, int Ti, char* ws, const EcBwdLayout& B,
+                                    int32_t* choice_tokens, float* choice_probs, float* aux_loss, float* z_loss,
+                                    hipStream_t s) {
+  const EcLayout& L = B.c;
+  const int C = ec_capacity(Ti);
+  const int Teff = 8 * C;
+  const GemmPlan plan = plan_gemm(Teff);
+  EcArgs ea{};
+  ea.T = Ti;
+  ea.C = C;
+  ea.partial = reinterpret_cast<const float2*>(ws + L.f.partial);
+  ea.pT = reinterpret_cast<float*>(ws + L.pT);
+  ea.lse = reinterpret_cast<float*>(ws + L.lse);
+  ea.inv_ec = reinterpret_cast<int32_t*>(ws + L.inv_ec);
+  ea.perm = reinterpret_cast<int32_t*>(ws + L.f.perm);
+  ea.row_w = reinterpret_cast<float*>(ws + L.row_w);
+  ea.blk_psum = reinterpret_cast<float*>(ws + L.f.blk_psum);
+  ea.blk_lse2 = reinterpret_cast<float*>(ws + L.f.blk_lse2);
+  ea.offsets = reinterpret_cast<int32_t*>(ws + L.f.offsets);
+  ea.tile_prefix_gu = reinterpret_cast<int32_t*>(ws + L.f.tp_gu);
+  ea.tiles_gu = reinterpret_cast<int2*>(ws + L.f.tiles_gu);
+  ea.bm_gu = plan.bm_gu;
+  ea.tile_prefix_dn = reinterpret_cast<int32_t*>(ws + L.f.tp_dn);
+  ea.tiles_dn = reinterpret_cast<int2*>(ws + L.f.tiles_dn);
+  ea.bm_dn = plan.bm_dn;
+  ea.p_all = reinterpret_cast<float*>(ws + B.p_all);
+  ea.choice_tokens = choice_tokens;
+  ea.choice_probs = choice_probs;
+  ea.aux_loss = aux_loss;
+  ea.z_loss = z_loss;
+  hipError_t he = hipSuccess;
+  if (Ti > 0) {
+    RouterArgs ra{static_cast<const uint16_t*>(x), W_router, Ti, reinterpret_cast<float2*>(ws + L.f.partial),
+                  reinterpret_cast<uint16_t*>(ws + L.f.planes)};
+    he = launch_router_partial(ra, s);
+    if (he == hipSuccess) he = launch_ec_softmax(ea, s);
+  }
+  if (he == hipSuccess) he = launch_ec_choose(ea, s);   // T == 0: zero offsets for the weight gradients
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "routing launch: %s", hipGetErrorString(he));
+  const int32_t* perm = reinterpret_cast<const int32_t*>(ws + L.f.perm);
+  const int32_t* offsets = reinterpret_cast<const int32_t*>(ws + L.f.offsets);
+  if (Ti > 0) {
+    GemmArgs ga{Teff,
+                static_cast<const uint16_t*>(x),
+                static_cast<const uint16_t*>(W_gate),
+                static_cast<const uint16_t*>(W_up),
+                static_cast<const uint16_t*>(W_down),
+                perm, offsets,
+                reinterpret_cast<const int32_t*>(ws + L.f.tp_gu),
+                reinterpret_cast<const int32_t*>(ws + L.f.tp_dn),
+                reinterpret_cast<const int2*>(ws + L.f.tiles_gu),
+                reinterpret_cast<const int2*>(ws + L.f.tiles_dn),
+                reinterpret_cast<uint16_t*>(ws + L.f.h),
+                reinterpret_cast<uint16_t*>(ws + L.f.y),
+                reinterpret_cast<float*>(ws + B.gu)};
+    he = launch_gateup(ga, plan, s);
+    if (he == hipSuccess) he = launch_down(ga, plan, s);
+    if (he != hipSuccess) return fail(OLMOE_EHIP, "forward GEMM launch: %s", hipGetErrorString(he));
+  }
+  return OLMOE_OK;
+}
+
+// the expert-choice gradients from the state ec_bwd_forward_state left in B
+olmoe_status_t ec_bwd_gradients(const void* x, const float* W_router, const void* W_gate, const void* W_up,
+                                const void* W_down, int Ti, const void* dout, float g_aux, float g_z, float* dx,
+                                float* dW_router, float* dW_gate, float* dW_up, float* dW_down, char* ws,
+                                const EcBwdLayout& B, hipStream_t s) {
+  const EcLayout& L = B.c;
+  const int C = ec_capacity(Ti);
+  const int Teff = 8 * C;
+  const int32_t* perm = reinterpret_cast<const int32_t*>(ws + L.f.perm);
+  const int32_t* offsets = reinterpret_cast<const int32_t*>(ws + L.f.offsets);
+  hipError_t he = hipSuccess;
+  BwdSmallArgs ba{Ti, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dout), W_router, nullptr,
+                  reinterpret_cast<const float*>(ws + B.p_all), reinterpret_cast<const float*>(ws + L.lse),
+                  offsets, perm, nullptr,
+                  reinterpret_cast<const uint16_t*>(ws + L.f.y), g_aux, g_z,
+                  reinterpret_cast<float*>(ws + B.dlogits), reinterpret_cast<uint16_t*>(ws + B.xg),
+                  reinterpret_cast<uint16_t*>(ws + B.dg), reinterpret_cast<const float*>(ws + B.dxr), dx,
+                  reinterpret_cast<float*>(ws + B.dwr_part), dW_router, reinterpret_cast<uint16_t*>(ws + B.zero),
+                  reinterpret_cast<int32_t*>(ws + B.tp_bwd), reinterpret_cast<int2*>(ws + B.tiles_bwd),
+                  reinterpret_cast<const int32_t*>(ws + L.inv_ec), OLMOE_E * C};
+  he = launch_bwd_prepare(ba, s);
+  if (he == hipSuccess) he = launch_bwd_router(ba, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "backward routing launch: %s", hipGetErrorString(he));
+  const uint16_t* dgu = reinterpret_cast<const uint16_t*>(ws + B.dgu);
+  if (Ti > 0) {
+    BwdDgradArgs dh{reinterpret_cast<const uint16_t*>(ws + B.dg), nullptr, static_cast<const uint16_t*>(W_down),
+                    nullptr, OLMOE_F, (long)OLMOE_D * OLMOE_F, 2 * OLMOE_F,
+                    reinterpret_cast<const int32_t*>(ws + B.tp_bwd) + OLMOE_E,
+                    reinterpret_cast<const int2*>(ws + B.tiles_bwd),
+                    reinterpret_cast<const float*>(ws + L.row_w), reinterpret_cast<const float*>(ws + B.gu),
+                    reinterpret_cast<uint16_t*>(ws + B.dgu), reinterpret_cast<uint16_t*>(ws + B.hw), nullptr};
+    BwdDgradArgs dxa{dgu, nullptr, static_cast<const uint16_t*>(W_gate), static_cast<const uint16_t*>(W_up),
+                     OLMOE_D, (long)OLMOE_F * OLMOE_D, OLMOE_F,
+                     reinterpret_cast<const int32_t*>(ws + B.tp_bwd) + OLMOE_E,
+                     reinterpret_cast<const int2*>(ws + B.tiles_bwd), nullptr, nullptr, nullptr, nullptr,
+                     reinterpret_cast<float*>(ws + B.dxr)};
+    he = launch_dgrad(dh, Teff, true, s);
+    if (he == hipSuccess) he = launch_dgrad(dxa, Teff, false, s);
+    if (he != hipSuccess) return fail(OLMOE_EHIP, "dgrad launch: %s", hipGetErrorString(he));
+  }
+  BwdWgradArgs wd{reinterpret_cast<const uint16_t*>(ws + B.dg), OLMOE_D, reinterpret_cast<const uint16_t*>(ws + B.hw),
+                  OLMOE_F, offsets, reinterpret_cast<const uint16_t*>(ws + B.zero), OLMOE_D, OLMOE_F, dW_down, dW_down,
+                  OLMOE_D, (long)OLMOE_D * OLMOE_F};
+  BwdWgradArgs wgu{dgu, 2 * OLMOE_F, reinterpret_cast<const uint16_t*>(ws + B.xg), OLMOE_D, offsets,
+                   reinterpret_cast<const uint16_t*>(ws + B.zero), 2 * OLMOE_F, OLMOE_D, dW_gate, dW_up, OLMOE_F,
+                   (long)OLMOE_F * OLMOE_D};
+  he = launch_wgrad(wd, s);
+  if (he == hipSuccess) he = launch_wgrad(wgu, s);
+  if (he == hipSuccess) he = launch_bwd_finish(ba, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "weight-gradient launch: %s", hipGetErrorString(he));
+  return ok();
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -814,103 +933,91 @@ olmoe_status_t olmoe_moe_backward_expert_choice(const void* x, const float* W_ro
   olmoe_status_t st = backward_checks(x, W_router, W_gate, W_up, W_down, T, dout, g_aux, g_z, dx, dW_router, dW_gate,
                                       dW_up, dW_down, workspace, workspace_bytes, B.total);
   if (st != OLMOE_OK) return st;
-
   // ---- launches: recompute the expert-choice forward (keeping p, lse, G, U, Y), then the gradients
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  const EcLayout& L = B.c;
+  st = ec_bwd_forward_state(x, W_router, W_gate, W_up, W_down, static_cast<int>(T), ws, B, nullptr, nullptr, nullptr,
+                            nullptr, s);
+  if (st != OLMOE_OK) return st;
+  return ec_bwd_gradients(x, W_router, W_gate, W_up, W_down, static_cast<int>(T), dout, g_aux, g_z, dx, dW_router,
+                          dW_gate, dW_up, dW_down, ws, B, s);
+}
+
+size_t olmoe_moe_ec_saved_bytes(int64_t T) { return olmoe_moe_ec_backward_workspace_bytes(T); }
+
+olmoe_status_t olmoe_moe_forward_expert_choice_train(const void* x, const float* W_router, const void* W_gate,
+                                                     const void* W_up, const void* W_down, int64_t T, void* out,
+                                                     int32_t* choice_tokens, float* choice_probs,
+                                                     int32_t* token_counts, float* aux_loss, float* z_loss,
+                                                     void* saved, size_t saved_bytes, void* stream) {
+  // ---- host-side checks; nothing is enqueued unless all pass
+  if (T < 0 || T > OLMOE_EC_MAX_TOKENS)
+    return fail(OLMOE_EINVAL, "T=%lld out of range [0, %lld]", (long long)T, (long long)OLMOE_EC_MAX_TOKENS);
+  if (!W_router || !W_gate || !W_up || !W_down) return fail(OLMOE_EINVAL, "a weight pointer is NULL");
+  if (T > 0 && (!x || !out)) return fail(OLMOE_EINVAL, "x or out is NULL");
+  const void* ptrs[] = {x, W_router, W_gate, W_up, W_down, out, choice_tokens, choice_probs, token_counts};
+  const char* names[] = {"x", "W_router", "W_gate", "W_up", "W_down", "out", "choice_tokens", "choice_probs",
+                         "token_counts"};
+  for (int i = 0; i < 9; ++i)
+    if (ptrs[i] && misaligned(ptrs[i])) return fail(OLMOE_EINVAL, "%s is not 16-byte aligned", names[i]);
+  if ((aux_loss && misaligned(aux_loss, 4)) || (z_loss && misaligned(z_loss, 4)))
+    return fail(OLMOE_EINVAL, "aux_loss / z_loss not 4-byte aligned");
+  const EcBwdLayout B = make_ec_bwd_layout(T);
+  if (!saved) return fail(OLMOE_EWORKSPACE, "saved is NULL");
+  if (misaligned(saved, 256)) return fail(OLMOE_EINVAL, "saved is not 256-byte aligned");
+  if (saved_bytes < B.total)
+    return fail(OLMOE_EWORKSPACE, "saved has %zu bytes, %zu needed for T=%lld", saved_bytes, B.total, (long long)T);
   const int Ti = static_cast<int>(T);
   const int C = ec_capacity(Ti);
-  const int Teff = 8 * C;
-  const GemmPlan plan = plan_gemm(Teff);
+  const size_t act = static_cast<size_t>(T) * OLMOE_D * 2;
+  const size_t wexp = static_cast<size_t>(OLMOE_E) * OLMOE_F * OLMOE_D * 2;
+  const size_t wr_bytes = (size_t)OLMOE_E * OLMOE_D * 4;
+  const size_t choice_n = static_cast<size_t>(C) * OLMOE_E * 4;
+  const void* ins[] = {x, W_router, W_gate, W_up, W_down};
+  const size_t in_n[] = {act, wr_bytes, wexp, wexp, wexp};
+  void* outs[] = {out, choice_tokens, choice_probs, token_counts, aux_loss, z_loss};
+  const size_t out_n[] = {act, choice_n, choice_n, static_cast<size_t>(T) * 4, 4, 4};
+  for (int o = 0; o < 6; ++o) {
+    for (int i = 0; i < 5; ++i)
+      if (overlaps(outs[o], out_n[o], ins[i], in_n[i])) return fail(OLMOE_EINVAL, "an output overlaps an input");
+    for (int q = o + 1; q < 6; ++q)
+      if (overlaps(outs[o], out_n[o], outs[q], out_n[q])) return fail(OLMOE_EINVAL, "two outputs overlap");
+    if (overlaps(outs[o], out_n[o], saved, B.total)) return fail(OLMOE_EINVAL, "an output overlaps saved");
+  }
+  olmoe_status_t st = check_device();
+  if (st != OLMOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(saved);
+  st = ec_bwd_forward_state(x, W_router, W_gate, W_up, W_down, Ti, ws, B, choice_tokens, choice_probs, aux_loss,
+                            z_loss, s);
+  if (st != OLMOE_OK || Ti == 0) return st == OLMOE_OK ? ok() : st;
+  const EcLayout& L = B.c;
   EcArgs ea{};
   ea.T = Ti;
   ea.C = C;
-  ea.partial = reinterpret_cast<const float2*>(ws + L.f.partial);
-  ea.pT = reinterpret_cast<float*>(ws + L.pT);
-  ea.lse = reinterpret_cast<float*>(ws + L.lse);
   ea.inv_ec = reinterpret_cast<int32_t*>(ws + L.inv_ec);
-  ea.perm = reinterpret_cast<int32_t*>(ws + L.f.perm);
   ea.row_w = reinterpret_cast<float*>(ws + L.row_w);
-  ea.blk_psum = reinterpret_cast<float*>(ws + L.f.blk_psum);
-  ea.blk_lse2 = reinterpret_cast<float*>(ws + L.f.blk_lse2);
-  ea.offsets = reinterpret_cast<int32_t*>(ws + L.f.offsets);
-  ea.tile_prefix_gu = reinterpret_cast<int32_t*>(ws + L.f.tp_gu);
-  ea.tiles_gu = reinterpret_cast<int2*>(ws + L.f.tiles_gu);
-  ea.bm_gu = plan.bm_gu;
-  ea.tile_prefix_dn = reinterpret_cast<int32_t*>(ws + L.f.tp_dn);
-  ea.tiles_dn = reinterpret_cast<int2*>(ws + L.f.tiles_dn);
-  ea.bm_dn = plan.bm_dn;
-  ea.p_all = reinterpret_cast<float*>(ws + B.p_all);
-  hipError_t he = hipSuccess;
-  if (Ti > 0) {
-    RouterArgs ra{static_cast<const uint16_t*>(x), W_router, Ti, reinterpret_cast<float2*>(ws + L.f.partial),
-                  reinterpret_cast<uint16_t*>(ws + L.f.planes)};
-    he = launch_router_partial(ra, s);
-    if (he == hipSuccess) he = launch_ec_softmax(ea, s);
-  }
-  if (he == hipSuccess) he = launch_ec_choose(ea, s);   // T == 0: zero offsets for the weight gradients
-  if (he != hipSuccess) return fail(OLMOE_EHIP, "routing launch: %s", hipGetErrorString(he));
-  const int32_t* perm = reinterpret_cast<const int32_t*>(ws + L.f.perm);
-  const int32_t* offsets = reinterpret_cast<const int32_t*>(ws + L.f.offsets);
-  if (Ti > 0) {
-    GemmArgs ga{Teff,
-                static_cast<const uint16_t*>(x),
-                static_cast<const uint16_t*>(W_gate),
-                static_cast<const uint16_t*>(W_up),
-                static_cast<const uint16_t*>(W_down),
-                perm, offsets,
-                reinterpret_cast<const int32_t*>(ws + L.f.tp_gu),
-                reinterpret_cast<const int32_t*>(ws + L.f.tp_dn),
-                reinterpret_cast<const int2*>(ws + L.f.tiles_gu),
-                reinterpret_cast<const int2*>(ws + L.f.tiles_dn),
-                reinterpret_cast<uint16_t*>(ws + L.f.h),
-                reinterpret_cast<uint16_t*>(ws + L.f.y),
-                reinterpret_cast<float*>(ws + B.gu)};
-    he = launch_gateup(ga, plan, s);
-    if (he == hipSuccess) he = launch_down(ga, plan, s);
-    if (he != hipSuccess) return fail(OLMOE_EHIP, "forward GEMM launch: %s", hipGetErrorString(he));
-  }
-  BwdSmallArgs ba{Ti, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dout), W_router, nullptr,
-                  reinterpret_cast<const float*>(ws + B.p_all), reinterpret_cast<const float*>(ws + L.lse),
-                  offsets, perm, nullptr,
-                  reinterpret_cast<const uint16_t*>(ws + L.f.y), g_aux, g_z,
-                  reinterpret_cast<float*>(ws + B.dlogits), reinterpret_cast<uint16_t*>(ws + B.xg),
-                  reinterpret_cast<uint16_t*>(ws + B.dg), reinterpret_cast<const float*>(ws + B.dxr), dx,
-                  reinterpret_cast<float*>(ws + B.dwr_part), dW_router, reinterpret_cast<uint16_t*>(ws + B.zero),
-                  reinterpret_cast<int32_t*>(ws + B.tp_bwd), reinterpret_cast<int2*>(ws + B.tiles_bwd),
-                  reinterpret_cast<const int32_t*>(ws + L.inv_ec), OLMOE_E * C};
-  he = launch_bwd_prepare(ba, s);
-  if (he == hipSuccess) he = launch_bwd_router(ba, s);
-  if (he != hipSuccess) return fail(OLMOE_EHIP, "backward routing launch: %s", hipGetErrorString(he));
-  const uint16_t* dgu = reinterpret_cast<const uint16_t*>(ws + B.dgu);
-  if (Ti > 0) {
-    BwdDgradArgs dh{reinterpret_cast<const uint16_t*>(ws + B.dg), nullptr, static_cast<const uint16_t*>(W_down),
-                    nullptr, OLMOE_F, (long)OLMOE_D * OLMOE_F, 2 * OLMOE_F,
-                    reinterpret_cast<const int32_t*>(ws + B.tp_bwd) + OLMOE_E,
-                    reinterpret_cast<const int2*>(ws + B.tiles_bwd),
-                    reinterpret_cast<const float*>(ws + L.row_w), reinterpret_cast<const float*>(ws + B.gu),
-                    reinterpret_cast<uint16_t*>(ws + B.dgu), reinterpret_cast<uint16_t*>(ws + B.hw), nullptr};
-    BwdDgradArgs dxa{dgu, nullptr, static_cast<const uint16_t*>(W_gate), static_cast<const uint16_t*>(W_up),
-                     OLMOE_D, (long)OLMOE_F * OLMOE_D, OLMOE_F,
-                     reinterpret_cast<const int32_t*>(ws + B.tp_bwd) + OLMOE_E,
-                     reinterpret_cast<const int2*>(ws + B.tiles_bwd), nullptr, nullptr, nullptr, nullptr,
-                     reinterpret_cast<float*>(ws + B.dxr)};
-    he = launch_dgrad(dh, Teff, true, s);
-    if (he == hipSuccess) he = launch_dgrad(dxa, Teff, false, s);
-    if (he != hipSuccess) return fail(OLMOE_EHIP, "dgrad launch: %s", hipGetErrorString(he));
-  }
-  BwdWgradArgs wd{reinterpret_cast<const uint16_t*>(ws + B.dg), OLMOE_D, reinterpret_cast<const uint16_t*>(ws + B.hw),
-                  OLMOE_F, offsets, reinterpret_cast<const uint16_t*>(ws + B.zero), OLMOE_D, OLMOE_F, dW_down, dW_down,
-                  OLMOE_D, (long)OLMOE_D * OLMOE_F};
-  BwdWgradArgs wgu{dgu, 2 * OLMOE_F, reinterpret_cast<const uint16_t*>(ws + B.xg), OLMOE_D, offsets,
-                   reinterpret_cast<const uint16_t*>(ws + B.zero), 2 * OLMOE_F, OLMOE_D, dW_gate, dW_up, OLMOE_F,
-                   (long)OLMOE_F * OLMOE_D};
-  he = launch_wgrad(wd, s);
-  if (he == hipSuccess) he = launch_wgrad(wgu, s);
-  if (he == hipSuccess) he = launch_bwd_finish(ba, s);
-  if (he != hipSuccess) return fail(OLMOE_EHIP, "weight-gradient launch: %s", hipGetErrorString(he));
+  ea.y = reinterpret_cast<const uint16_t*>(ws + L.f.y);
+  ea.out = static_cast<uint16_t*>(out);
+  ea.token_counts = token_counts;
+  const hipError_t he = launch_ec_combine(ea, s);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "combine launch: %s", hipGetErrorString(he));
   return ok();
+}
+
+olmoe_status_t olmoe_moe_backward_expert_choice_saved(const void* x, const float* W_router, const void* W_gate,
+                                                      const void* W_up, const void* W_down, int64_t T,
+                                                      const void* dout, float g_aux, float g_z, float* dx,
+                                                      float* dW_router, float* dW_gate, float* dW_up, float* dW_down,
+                                                      void* saved, size_t saved_bytes, void* stream) {
+  if (T < 0 || T > OLMOE_EC_MAX_TOKENS)
+    return fail(OLMOE_EINVAL, "T=%lld out of range [0, %lld]", (long long)T, (long long)OLMOE_EC_MAX_TOKENS);
+  const EcBwdLayout B = make_ec_bwd_layout(T);
+  olmoe_status_t st = backward_checks(x, W_router, W_gate, W_up, W_down, T, dout, g_aux, g_z, dx, dW_router, dW_gate,
+                                      dW_up, dW_down, saved, saved_bytes, B.total);
+  if (st != OLMOE_OK) return st;
+  return ec_bwd_gradients(x, W_router, W_gate, W_up, W_down, static_cast<int>(T), dout, g_aux, g_z, dx, dW_router,
+                          dW_gate, dW_up, dW_down, static_cast<char*>(saved), B, static_cast<hipStream_t>(stream));
 }
 
 olmoe_status_t olmoe_rmsnorm_bf16(const float* h, float eps, int64_t T, void* x_out, void* stream) {

@@ -229,6 +229,31 @@ def test_training_pair_checks_arguments_first(L):
     assert bs(dx=(8 << 36) + 256) == binding.EINVAL
 
 
+def test_expert_choice_training_pair_checks_arguments_first(L):
+    vp = ctypes.c_void_p
+    T = 64
+    sb = binding.ec_saved_bytes(T)
+    assert sb == binding.ec_backward_workspace_bytes(T) and binding.ec_saved_bytes(binding.EC_MAX_TOKENS + 1) == 0
+
+    def ft(out=4 << 20, saved=8 << 36, nbytes=sb, t=T):
+        return L.olmoe_moe_forward_expert_choice_train(vp(1 << 20), vp(2 << 20), vp(1 << 32), vp(2 << 32),
+                                                       vp(3 << 32), t, vp(out), None, None, None, None, None,
+                                                       vp(saved), nbytes, None)
+    assert ft(t=binding.EC_MAX_TOKENS + 1) == binding.EINVAL
+    assert ft(out=0) == binding.EINVAL
+    assert ft(saved=0) == binding.EWORKSPACE
+    assert ft(nbytes=1000) == binding.EWORKSPACE
+    assert ft(out=(8 << 36) + 512) == binding.EINVAL
+
+    def bs(dx=5 << 20, nbytes=sb):
+        return L.olmoe_moe_backward_expert_choice_saved(vp(1 << 20), vp(2 << 20), vp(1 << 32), vp(2 << 32),
+                                                        vp(3 << 32), T, vp(4 << 20), ctypes.c_float(1.0),
+                                                        ctypes.c_float(1.0), vp(dx), vp(6 << 20), vp(1 << 34),
+                                                        vp(2 << 34), vp(3 << 34), vp(8 << 36), nbytes, None)
+    assert bs(dx=0) == binding.EINVAL
+    assert bs(nbytes=1000) == binding.EWORKSPACE
+
+
 def test_glue_entry_points_reject_bad_arguments(L):
     vp = ctypes.c_void_p
     assert L.olmoe_rmsnorm_bf16(vp(1 << 20), ctypes.c_float(0.0), 4, vp(1 << 30), None) == binding.EINVAL

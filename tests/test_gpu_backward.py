@@ -201,3 +201,29 @@ def test_training_pair_equals_stateless_calls(weights, T):
     torch.cuda.synchronize()
     for k in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down"):
         assert torch.equal(b[k], b_ref[k]), k
+
+
+@pytest.mark.parametrize("T", [0, 1, 200, 700, 4096])
+def test_expert_choice_training_pair_equals_stateless_calls(weights, T):
+    w, _ = weights
+    _log(f"EC training pair T={T}")
+    x = inputs.device_x(T, seed=70 + T, workload="parity")
+    dout = inputs.device_x(T, seed=80 + T, workload="parity")
+    C = binding.ec_capacity(T)
+    i32, f32 = torch.int32, torch.float32
+    ref = binding.moe_forward_expert_choice(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"])
+    got = dict(choice_tokens=torch.empty((64, C), dtype=i32, device="cuda"),
+               choice_probs=torch.empty((64, C), dtype=f32, device="cuda"),
+               token_counts=torch.empty(T, dtype=i32, device="cuda"),
+               aux_loss=torch.empty(1, dtype=f32, device="cuda"), z_loss=torch.empty(1, dtype=f32, device="cuda"))
+    tr = binding.moe_forward_expert_choice_train(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], **got)
+    torch.cuda.synchronize()
+    for k in ("out", "choice_tokens", "choice_probs", "token_counts", "aux_loss", "z_loss"):
+        assert torch.equal(tr[k], ref[k]), k
+    b_ref = binding.moe_backward_expert_choice(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], dout,
+                                               g_aux=2.0, g_z=0.5)
+    b = binding.moe_backward_expert_choice_saved(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], dout,
+                                                 tr["saved"], g_aux=2.0, g_z=0.5)
+    torch.cuda.synchronize()
+    for k in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down"):
+        assert torch.equal(b[k], b_ref[k]), k
