@@ -169,6 +169,16 @@ def measure(workload, steps, warmup, seed=0, tokens=None):
     dom_sum, dom_calls = binding.timing_read()
     binding.timing_enable(False)
     dom_ms = dom_sum[dom] / dom_calls
+    # per-call distribution: events around each call on the stream the layer runs on
+    n_dist = min(steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_dist)]
+    for a, b in evs:
+        a.record()
+        step()
+        b.record()
+    sync()
+    per_call = sorted(a.elapsed_time(b) for a, b in evs)
+    pick = lambda q: per_call[min(len(per_call) - 1, int(q * len(per_call)))]
 
     L = wl.layers
     touched = sum(touched_per_layer) / len(touched_per_layer)      # per layer call
@@ -197,6 +207,8 @@ def measure(workload, steps, warmup, seed=0, tokens=None):
         "layer_mfma_frac": flop / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         "experts_touched": touched, "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "roofline": roof, "host_inputs": None,
+        "per_call_ms": {"calls": n_dist, "p10": round(pick(0.1), 5), "median": round(pick(0.5), 5),
+                        "p90": round(pick(0.9), 5)},
     }
     if wl.layers == 1:
         res["host_inputs"] = d
@@ -532,7 +544,7 @@ def stats_summary(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode-256")
     ap.add_argument("--seed", type=int, default=0)
@@ -541,6 +553,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--no-expert-choice", action="store_true", help="skip the expert-choice forward timing")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the 32-token, skewed 16384-token and 16-layer stack measurements")
     ap.add_argument("--copy-probe", action="store_true", help="run the counter-calibration copy and exit")
     ap.add_argument("--traffic-summary", action="store_true", help="summarise --pmc runs into profiles/")
     ap.add_argument("--stats-summary", metavar="DIR", dest="stats_dir", help="summarise a --stats run")
@@ -598,6 +612,7 @@ def main():
         "layer_mfma_frac": round(main_res["layer_mfma_frac"], 4),
         "experts_touched": main_res["experts_touched"],
         "stage_ms": main_res["stage_ms"],
+        "per_call_ms": main_res["per_call_ms"],
         "roofline": main_res["roofline"],
     }
     d = main_res.pop("host_inputs")
@@ -610,7 +625,8 @@ def main():
                              "unit": "tokens/s", "ms_per_step": round(s["sec"] * 1e3, 5),
                              "ms_per_step_without_events": round(s["sec_plain"] * 1e3, 5),
                              "tflops": round(s["tflops"], 2), "layer_mfma_frac": round(s["layer_mfma_frac"], 4),
-                             "stage_ms": s["stage_ms"], "roofline": s["roofline"]}
+                             "stage_ms": s["stage_ms"], "per_call_ms": s["per_call_ms"],
+                             "layer_hbm_frac": round(s["layer_hbm_frac"], 4), "roofline": s["roofline"]}
         d = None
     if not args.no_backward and wl_layers_of(args.workload) == 1:
         wls = [args.workload] + ([] if args.no_secondary or args.workload == "prefill-4096" else ["prefill-4096"])
@@ -621,6 +637,19 @@ def main():
         wls = [args.workload] + ([] if args.no_secondary or args.workload == "prefill-4096" else ["prefill-4096"])
         torch.cuda.empty_cache()
         line["expert_choice"] = [measure_expert_choice(w, args.steps, min(args.warmup, 5), args.seed) for w in wls]
+    if not args.no_other_configs and args.workload == "decode-256":
+        torch.cuda.empty_cache()
+        others = []
+        for w in ("tiny-32", "skew-16384", "stack-16x8192"):
+            r = measure(w, min(args.steps, 20), min(args.warmup, 3), args.seed)
+            r.pop("host_inputs")
+            others.append({"workload": w, "tokens": r["tokens"], "layers": r["layers"],
+                           "ms_per_step": round(r["sec"] * 1e3, 5), "tokens_per_s": round(r["tokens_per_s"], 1),
+                           "tflops": round(r["tflops"], 2), "layer_hbm_frac": round(r["layer_hbm_frac"], 4),
+                           "layer_mfma_frac": round(r["layer_mfma_frac"], 4), "experts_touched": r["experts_touched"],
+                           "per_call_ms": r["per_call_ms"], "roofline": r["roofline"]})
+            torch.cuda.empty_cache()
+        line["other_configs"] = others
     if not args.no_cpu:
         if d is None:
             from sparse_mixture_experts_expert_amd import inputs
