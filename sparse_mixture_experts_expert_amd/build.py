@@ -70,5 +70,26 @@ def build(verbose: bool = True, extra: list[str] | None = None) -> str:
     return LIB
 
 
+C_CALLER_SRC = os.path.join(ROOT, "tests", "c", "forward_c.c")
+C_CALLER = os.path.join(ROOT, "tests", "c", "forward_c")
+
+
+def build_c_caller(verbose: bool = True) -> str:
+    """The plain-C test program that drives olmoe_moe_forward through the HIP runtime's C API
+    (gcc; the HIP headers need the platform macro that hipcc would define)."""
+    rocm = os.path.dirname(os.path.dirname(hipcc()))
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"),
+           "-I", os.path.join(ROOT, "include"), C_CALLER_SRC, "-L", PKG, "-lolmoe_moe",
+           "-Wl,-rpath,$ORIGIN/../../sparse_mixture_experts_expert_amd", "-L", os.path.join(rocm, "lib"),
+           "-lamdhip64", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}", "-o", C_CALLER]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C caller build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {C_CALLER}")
+    return C_CALLER
+
+
 if __name__ == "__main__":
     build()
+    build_c_caller()
