@@ -408,6 +408,12 @@ __global__ __launch_bounds__(C::NT) void wgrad_kernel(BwdWgradArgs a) {
 
 using DgDH = DCfg<128, 128, 2, 2, 3, EPI_DH>;
 using DgDX = DCfg<128, 128, 2, 2, 3, EPI_F32>;
+// small batches (an expert's rows fit one 64-row tile): 64x256 tiles on 8 waves, three stages, so
+// less of each staged tile is padding rows and more weight bytes are in flight per CU (at 256
+// tokens 104 + 65 us against 110 + 73 us for the two products)
+using DgDHS = DCfg<64, 256, 2, 4, 3, EPI_DH>;
+using DgDXS = DCfg<64, 256, 2, 4, 3, EPI_F32>;
+constexpr int DGRAD_SMALL_TOKENS = 320;
 // large batches: 256x256 tiles on 8 waves (4% off the backward at 4096 tokens; at 256 tokens, with
 // one partly filled row tile per expert, the 128-row tiles are faster)
 using DgDHL = DCfg<256, 256, 4, 2, 2, EPI_DH>;
@@ -420,7 +426,9 @@ using WgCfg = WCfg<256, 256, 4, 2, 2>;
 
 }  // namespace
 
-int bwd_tile_rows(int T) { return T > DGRAD_LARGE_TOKENS ? DgDHL::BM : DgDH::BM; }
+int bwd_tile_rows(int T) {
+  return T > DGRAD_LARGE_TOKENS ? DgDHL::BM : T > DGRAD_SMALL_TOKENS ? DgDH::BM : DgDHS::BM;
+}
 
 template <class C>
 hipError_t launch_dgrad_cfg(const BwdDgradArgs& a, int T, hipStream_t stream) {
@@ -431,9 +439,12 @@ hipError_t launch_dgrad_cfg(const BwdDgradArgs& a, int T, hipStream_t stream) {
 
 hipError_t launch_dgrad(const BwdDgradArgs& a, int T, bool dh, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  static_assert(DgDH::BM == DgDX::BM && DgDHL::BM == DgDXL::BM, "both dgrad products share the tile list");
+  static_assert(DgDH::BM == DgDX::BM && DgDHL::BM == DgDXL::BM && DgDHS::BM == DgDXS::BM,
+                "both dgrad products share the tile list");
+  static_assert(DgDHS::BM >= MIN_TILE_ROWS, "tile lists are sized for MIN_TILE_ROWS");
   if (T > DGRAD_LARGE_TOKENS) return dh ? launch_dgrad_cfg<DgDHL>(a, T, stream) : launch_dgrad_cfg<DgDXL>(a, T, stream);
-  return dh ? launch_dgrad_cfg<DgDH>(a, T, stream) : launch_dgrad_cfg<DgDX>(a, T, stream);
+  if (T > DGRAD_SMALL_TOKENS) return dh ? launch_dgrad_cfg<DgDH>(a, T, stream) : launch_dgrad_cfg<DgDX>(a, T, stream);
+  return dh ? launch_dgrad_cfg<DgDHS>(a, T, stream) : launch_dgrad_cfg<DgDXS>(a, T, stream);
 }
 
 hipError_t launch_wgrad(const BwdWgradArgs& a, hipStream_t stream) {

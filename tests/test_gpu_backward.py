@@ -88,7 +88,7 @@ def run_backward(w, hw, T, seed, g_aux, g_z):
 
 
 @pytest.mark.parametrize("T,g_aux,g_z", [(1, 1.0, 1.0), (33, 1.0, 1.0), (200, 0.0, 0.0), (200, 5.0, -3.0),
-                                         (700, 1.0, 1.0), (2100, 1.0, 1.0), (4096, 1.0, 1.0)])
+                                         (400, 1.0, 1.0), (700, 1.0, 1.0), (2100, 1.0, 1.0), (4096, 1.0, 1.0)])
 def test_backward_matches_oracle(weights, T, g_aux, g_z):
     w, hw = weights
     _log(f"backward T={T}")
@@ -146,7 +146,7 @@ def run_ec_backward(w, hw, T, seed, g_aux, g_z):
 
 
 @pytest.mark.parametrize("T,g_aux,g_z", [(1, 1.0, 1.0), (9, 1.0, 1.0), (200, 0.0, 0.0), (200, 5.0, -3.0),
-                                         (700, 1.0, 1.0), (2100, 1.0, 1.0), (4096, 1.0, 1.0)])
+                                         (400, 1.0, 1.0), (700, 1.0, 1.0), (2100, 1.0, 1.0), (4096, 1.0, 1.0)])
 def test_expert_choice_backward_matches_oracle(weights, T, g_aux, g_z):
     w, hw = weights
     _log(f"EC backward T={T}")
