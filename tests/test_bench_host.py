@@ -7,7 +7,6 @@ import shutil
 import subprocess
 import sys
 
-import numpy as np
 import pytest
 
 import bench
