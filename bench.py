@@ -574,7 +574,7 @@ def main():
         stats_summary(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share: this build runs on a single MI355X "
+        print("bench.py measures one GPU's share: the library runs on a single MI355X "
               "(the data-parallel shard needs no communication); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 

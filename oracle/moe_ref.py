@@ -509,7 +509,7 @@ def moe_stack_ref(h0, layers, k=8, teacher_inputs=None, eps=RMS_EPS):
 
     layers: list of dicts with w_router / w_gate / w_up / w_down.
     teacher_inputs: optional per-layer bf16 inputs to use instead of RMSNorm(h)
-    (runs each layer on given inputs, so every layer can be judged alone).
+    (runs each layer on given inputs, so every layer can be checked alone).
     Returns (h_final, per-layer list of dicts: x_in (bf16 bits), out, ids,
     counts, aux, z, gap)."""
     h = np.asarray(h0, dtype=np.float64).copy()

@@ -244,7 +244,7 @@ def test_stack_teacher_forced_and_free_running(fused):
     torch.cuda.synchronize()
     xs = [parity.bf16_tensor_to_bits(x) for x in r["inputs"]]
     states = [h0_host.astype(np.float64)] + [st.cpu().numpy().astype(np.float64) for st in r["states"]]
-    # teacher forcing: each layer judged on the GPU's own input and its own residual update
+    # teacher forcing: each layer checked on the GPU's own input and its own residual update
     for l in range(L):
         ids = r["route_ids"][l].cpu().numpy()
         ref = oracle.moe_layer_ref(xs[l], hw[l]["w_router"], hw[l]["w_gate"], hw[l]["w_up"], hw[l]["w_down"], 8,
@@ -258,7 +258,7 @@ def test_stack_teacher_forced_and_free_running(fused):
             assert (np.abs(got - want) <= np.abs(want) * 2.0 ** -7 + 1e-30).all()
     # free running against the oracle's own stack.  A token whose top-8 flips at a near tie
     # (either routing is correct) follows a different path from then on, so the update is
-    # judged on the tokens routed identically at every layer; the flipped ones must be few.
+    # checked on the tokens routed identically at every layer; the flipped ones must be few.
     h_ref, per_ref = oracle.moe_stack_ref(h0_host, hw, k=8)
     hg = r["h"].cpu().numpy().astype(np.float64)
     rel = np.linalg.norm(hg - h_ref) / np.linalg.norm(h_ref)
