@@ -89,6 +89,7 @@ def traffic_from_profiles(workload, stage):
 
 
 N_WEIGHT_SETS = 4   # single-layer steps cycle through distinct weight sets (3.2 GB, far above the 256 MB MALL)
+EVENT_EVERY = 8     # the dominant kernel's events are recorded on one timed step in this many
 
 
 def wl_layers_of(workload):
@@ -158,8 +159,10 @@ def measure(workload, steps, warmup, seed=0, tokens=None):
         step()
     sync()
     sec_plain = (time.perf_counter() - t0) / steps
-    # timed region: K steps with the dominant kernel bracketed by HIP events on its launch stream
+    # timed region: K steps with the dominant kernel bracketed by HIP events on its launch stream,
+    # on every EVENT_EVERY-th step (events on every call cost the step a few microseconds)
     binding.timing_enable([dom])
+    binding.timing_every(EVENT_EVERY)
     sync()
     t0 = time.perf_counter()
     for _ in range(steps):

@@ -47,7 +47,7 @@ extern "C" {
 #define OLMOE_API
 #endif
 
-#define OLMOE_ABI_VERSION 7
+#define OLMOE_ABI_VERSION 8
 
 #define OLMOE_D 2048 /* hidden size */
 #define OLMOE_F 1024 /* expert width (SwiGLU intermediate size) */
@@ -340,10 +340,15 @@ OLMOE_API olmoe_status_t olmoe_moe_backward(const void* x, const float* W_router
  * milliseconds (0 for stages outside the mask), writes the number of timed
  * calls to *calls, and returns the number of stages (or -1 on error).  Names
  * of the stages: olmoe_timing_stage_name(i).  Each recorded boundary costs
- * the stream a little time, so bracket only the stages of interest. */
+ * the stream a little time, so bracket only the stages of interest, and
+ * olmoe_timing_every(n) (n >= 1, else OLMOE_EINVAL) brackets only every n-th
+ * call on this thread from then on (the first call after it is bracketed;
+ * olmoe_timing_enable resets n to 1), so a long run can be timed on a sample
+ * of its calls. */
 #define OLMOE_TIMING_ALL 0x1F
 OLMOE_API olmoe_status_t olmoe_timing_enable(int stage_mask);
 OLMOE_API int olmoe_timing_read(double* stage_ms, int max_stages, int* calls);
+OLMOE_API olmoe_status_t olmoe_timing_every(int n);
 OLMOE_API const char* olmoe_timing_stage_name(int stage);
 
 #ifdef __cplusplus

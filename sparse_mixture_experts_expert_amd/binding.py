@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
     L.olmoe_timing_enable.argtypes = [i32]
     L.olmoe_timing_read.restype = i32
     L.olmoe_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), i32, ctypes.POINTER(i32)]
+    L.olmoe_timing_every.restype = i32
+    L.olmoe_timing_every.argtypes = [i32]
     L.olmoe_timing_stage_name.restype = ctypes.c_char_p
     L.olmoe_timing_stage_name.argtypes = [i32]
     _lib = L
@@ -521,6 +523,11 @@ def timing_enable(stages=True):
 
 
 _timing_mask = 0
+
+
+def timing_every(n):
+    """Bracket only every n-th later forward call (the next one first); timing_enable resets it to 1."""
+    _check(lib().olmoe_timing_every(int(n)))
 
 
 def timing_read():

@@ -172,6 +172,8 @@ const char* kStageNames[N_STAGES] = {"router", "dispatch", "gateup", "down", "co
 
 struct TimingState {
   int mask = 0;   // bit i: bracket stage i with events
+  int every = 1;  // bracket every n-th call
+  long long calls = 0;   // calls seen since the mask or the sampling step was set
   std::vector<std::vector<hipEvent_t>> pending;  // one set of N_STAGES+1 boundary events per call
 };
 thread_local TimingState g_timing;
@@ -187,6 +189,7 @@ struct StageRecorder {
   int next = 0;
   explicit StageRecorder(hipStream_t st) : s(st) {
     if (!g_timing.mask || g_timing.pending.size() >= 65536) return;
+    if (g_timing.calls++ % g_timing.every != 0) return;
     g_timing.pending.emplace_back(N_STAGES + 1, nullptr);
     ev = &g_timing.pending.back();
     for (int b = 0; b <= N_STAGES; ++b)
@@ -1059,6 +1062,15 @@ olmoe_status_t olmoe_timing_enable(int stage_mask) {
       if (e) (void)hipEventDestroy(e);
   g_timing.pending.clear();
   g_timing.mask = stage_mask;
+  g_timing.every = 1;
+  g_timing.calls = 0;
+  return ok();
+}
+
+olmoe_status_t olmoe_timing_every(int n) {
+  if (n < 1) return fail(OLMOE_EINVAL, "timing sample step %d is below 1", n);
+  g_timing.every = n;
+  g_timing.calls = 0;
   return ok();
 }
 

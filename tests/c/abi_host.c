@@ -35,6 +35,9 @@ int main(void) {
                           (void*)(uintptr_t)(4u << 20), NULL, NULL, NULL, NULL, NULL,
                           (void*)((uintptr_t)8 << 36), 1000, NULL) == OLMOE_EWORKSPACE);
   CHECK(olmoe_timing_enable(1 << 5) == OLMOE_EINVAL);
+  CHECK(olmoe_timing_every(0) == OLMOE_EINVAL);
+  CHECK(olmoe_timing_every(4) == OLMOE_OK);
+  CHECK(olmoe_timing_enable(0) == OLMOE_OK);
   printf("C ABI host checks passed (ABI %d)\n", olmoe_abi_version());
   return 0;
 }

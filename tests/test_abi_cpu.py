@@ -282,6 +282,10 @@ def test_timing_stage_names(L):
     assert set(stats) == set(names)
     assert L.olmoe_timing_enable(1 << 5) == binding.EINVAL
     assert L.olmoe_timing_enable(-1) == binding.EINVAL
+    assert L.olmoe_timing_every(0) == binding.EINVAL
+    assert L.olmoe_timing_every(-3) == binding.EINVAL
+    assert L.olmoe_timing_every(8) == binding.OK
+    assert L.olmoe_timing_every(1) == binding.OK
     binding.timing_enable(False)
 
 

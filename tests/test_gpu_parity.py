@@ -361,3 +361,18 @@ def test_full_size_stack():
                                      forced_ids=ids[rows])
         rel, mx = parity.check_out(oracle.to_f64(out[rows]), ref_o["out"], f"stack layer {l}")
         _log(f"stack layer {l}: ties={ntie} sampled relL2={rel:.2e} ({time.time() - t0:.1f}s)")
+
+
+def test_stage_timing_on_a_sample_of_calls(weights):
+    """olmoe_timing_every(n) brackets calls 0, n, 2n, ... of those that follow it."""
+    w, _ = weights
+    x = inputs.device_x(64, seed=11, workload="parity")
+    binding.timing_enable(["gateup", "down"])
+    binding.timing_every(3)
+    for _ in range(7):
+        binding.moe_forward(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"])
+    torch.cuda.synchronize()
+    stats, calls = binding.timing_read()
+    binding.timing_enable(False)
+    assert calls == 3
+    assert set(stats) == {"gateup", "down"} and stats["gateup"] > 0 and stats["down"] > 0
