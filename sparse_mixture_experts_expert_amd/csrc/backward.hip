@@ -19,7 +19,8 @@ namespace olmoe {
 
 namespace {
 
-constexpr int WR_SPLIT_TOKENS = 32;    // tokens per partial sum of dW_router
+constexpr int WR_SPLIT_TOKENS = 32;    // tokens per load batch of the dW_router partial kernel
+constexpr int WR_MAX_SPLITS = 32;      // dW_router partial sums at most (16: 80 + 6 us at 4096 tokens, 32: 48 + 10, 128: 46 + 33)
 
 // workgroup 0: zero row and the dgrad row-tile list; the others: x and dout rows in
 // expert order (one row per workgroup)
@@ -108,37 +109,45 @@ __global__ __launch_bounds__(256) void bwd_router_kernel(BwdSmallArgs a) {
       p * (dp - s) + a.g_z * static_cast<float>(Z_BETA) * 2.0f * a.lse[t] / Tf * p;
 }
 
-// dW_router partial sums over WR_SPLIT_TOKENS tokens: thread (column, 16 experts)
+// dW_router partial sums, one per gridDim.y token range (whole batches of WR_SPLIT_TOKENS tokens,
+// summed in token order): thread (column, 16 experts).  The 16 experts are the same for the whole
+// wavefront, so their dlogits go through scalar loads (one per wave) rather than a vector load
+// that every lane repeats.
 __global__ __launch_bounds__(256) void bwd_wrouter_partial_kernel(BwdSmallArgs a) {
   const int col = blockIdx.x * 64 + (threadIdx.x & 63);
-  const int e0 = (threadIdx.x >> 6) * 16;
-  const int t0 = blockIdx.y * WR_SPLIT_TOKENS;
-  const int t1 = min(a.T, t0 + WR_SPLIT_TOKENS);
+  const int e0 = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) * 16);
+  const int batches = (a.T + WR_SPLIT_TOKENS - 1) / WR_SPLIT_TOKENS;
+  const int per = (batches + gridDim.y - 1) / gridDim.y * WR_SPLIT_TOKENS;   // tokens per range
+  const int r0 = blockIdx.y * per;
+  const int r1 = min(a.T, r0 + per);
   float acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  if (t1 - t0 == WR_SPLIT_TOKENS) {   // full split: every load issued before the FMAs
-    float xv[WR_SPLIT_TOKENS];
+  for (int t0 = r0; t0 < r1; t0 += WR_SPLIT_TOKENS) {
+    const int t1 = min(r1, t0 + WR_SPLIT_TOKENS);
+    if (t1 - t0 == WR_SPLIT_TOKENS) {   // full batch: every load issued before the FMAs
+      float xv[WR_SPLIT_TOKENS];
 #pragma unroll
-    for (int q = 0; q < WR_SPLIT_TOKENS; ++q) xv[q] = bf16_to_f32(a.x[(size_t)(t0 + q) * D + col]);
+      for (int q = 0; q < WR_SPLIT_TOKENS; ++q) xv[q] = bf16_to_f32(a.x[(size_t)(t0 + q) * D + col]);
 #pragma unroll 4
-    for (int q = 0; q < WR_SPLIT_TOKENS; ++q) {
-      const float4* dl = reinterpret_cast<const float4*>(a.dlogits + (size_t)(t0 + q) * E + e0);
+      for (int q = 0; q < WR_SPLIT_TOKENS; ++q) {
+        const float4* dl = reinterpret_cast<const float4*>(a.dlogits + (size_t)(t0 + q) * E + e0);
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const float4 d4 = dl[i4];
-        acc[4 * i4] = fmaf(d4.x, xv[q], acc[4 * i4]);
-        acc[4 * i4 + 1] = fmaf(d4.y, xv[q], acc[4 * i4 + 1]);
-        acc[4 * i4 + 2] = fmaf(d4.z, xv[q], acc[4 * i4 + 2]);
-        acc[4 * i4 + 3] = fmaf(d4.w, xv[q], acc[4 * i4 + 3]);
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const float4 d4 = dl[i4];
+          acc[4 * i4] = fmaf(d4.x, xv[q], acc[4 * i4]);
+          acc[4 * i4 + 1] = fmaf(d4.y, xv[q], acc[4 * i4 + 1]);
+          acc[4 * i4 + 2] = fmaf(d4.z, xv[q], acc[4 * i4 + 2]);
+          acc[4 * i4 + 3] = fmaf(d4.w, xv[q], acc[4 * i4 + 3]);
+        }
       }
-    }
-  } else {
-    for (int t = t0; t < t1; ++t) {
-      const float xv = bf16_to_f32(a.x[(size_t)t * D + col]);
-      const float* dl = a.dlogits + (size_t)t * E + e0;
+    } else {
+      for (int t = t0; t < t1; ++t) {
+        const float xv = bf16_to_f32(a.x[(size_t)t * D + col]);
+        const float* dl = a.dlogits + (size_t)t * E + e0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = fmaf(dl[i], xv, acc[i]);
+        for (int i = 0; i < 16; ++i) acc[i] = fmaf(dl[i], xv, acc[i]);
+      }
     }
   }
 #pragma unroll
@@ -210,7 +219,7 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(BwdSmallArgs a) {
 
 }  // namespace
 
-int bwd_router_splits(int T) { return (T + WR_SPLIT_TOKENS - 1) / WR_SPLIT_TOKENS; }
+int bwd_router_splits(int T) { return min(WR_MAX_SPLITS, (T + WR_SPLIT_TOKENS - 1) / WR_SPLIT_TOKENS); }
 
 hipError_t launch_bwd_prepare(const BwdSmallArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(bwd_prepare_kernel, dim3(1 + (a.rows ? a.rows : K * a.T)), dim3(256), 0, stream, a,
