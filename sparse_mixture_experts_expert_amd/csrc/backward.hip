@@ -203,9 +203,17 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(BwdSmallArgs a) {
   for (int tk = 0; tk < DX_TOK; ++tk) {
     const int t = t0 + tk;
     if (t >= a.T) break;
-    if constexpr (EC) {
+    if constexpr (EC) {   // a varying count of rows: loaded eight at a time, added in order
       const int n = scnt[tk];
-      for (int j = 0; j < n; ++j) acc[tk] += a.dxr[(size_t)srow[tk][j] * D + col];
+      for (int j0 = 0; j0 < n; j0 += 8) {
+        float r[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          r[jj] = j0 + jj < n ? a.dxr[(size_t)srow[tk][j0 + jj] * D + col] : 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          if (j0 + jj < n) acc[tk] += r[jj];
+      }
     } else {
       float r[K];
 #pragma unroll
