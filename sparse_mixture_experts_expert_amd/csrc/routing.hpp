@@ -242,6 +242,8 @@ __device__ __forceinline__ void scan_block(const ScanArgs& a, ScanLds& L) {
 
   int c = 0;
   double ps = 0.0;
+  // unrolled so that several blocks' loads are in flight before the first add (same order)
+#pragma unroll 8
   for (int b = b0; b < b1; ++b) {
     c += a.blk_counts[b * E + e];
     ps += static_cast<double>(a.blk_psum[b * E + e]);
@@ -297,6 +299,7 @@ __device__ __forceinline__ void scan_block(const ScanArgs& a, ScanLds& L) {
   __syncthreads();
 
   int base = L.soff[e] + L.sc[s][e];
+#pragma unroll 8
   for (int b = b0; b < b1; ++b) {
     a.blk_base[b * E + e] = base;
     base += a.blk_counts[b * E + e];
