@@ -69,38 +69,56 @@ __global__ __launch_bounds__(256) void bwd_router_kernel(BwdSmallArgs a) {
       g[c][2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
     }
   }
-  // <dout[t], Y row>, the same on every lane
-  auto dot_row = [&](int row) {
-    const uint16_t* yr = a.y + (size_t)row * D;
-    float s = 0.f;
+  // <dout[t], Y row> for up to 8 rows (row < 0: none), the same on every lane.  Every row's
+  // loads are issued before the first product, so the rows' memory latencies overlap.
+  auto dot_rows = [&](const int* rows, float* out) __attribute__((always_inline)) {
+    u32x4 v[K][NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(yr + (c * 64 + lane) * 8);
+    for (int j = 0; j < K; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s = fmaf(g[c][2 * i], f16_to_f32(static_cast<uint16_t>(v[i] & 0xFFFFu)), s);
-        s = fmaf(g[c][2 * i + 1], f16_to_f32(static_cast<uint16_t>(v[i] >> 16)), s);
-      }
+      for (int c = 0; c < NC; ++c)
+        v[j][c] = rows[j] >= 0 ? *reinterpret_cast<const u32x4*>(a.y + (size_t)rows[j] * D + (c * 64 + lane) * 8)
+                               : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s = fmaf(g[c][2 * i], f16_to_f32(static_cast<uint16_t>(v[j][c][i] & 0xFFFFu)), s);
+          s = fmaf(g[c][2 * i + 1], f16_to_f32(static_cast<uint16_t>(v[j][c][i] >> 16)), s);
+        }
+      out[j] = wave_sum(s);
     }
-    return wave_sum(s);
   };
   const float p = a.p_all[(size_t)t * E + lane];
   const float cnt = static_cast<float>(a.offsets[lane + 1] - a.offsets[lane]);
   const float Tf = static_cast<float>(a.T);
   float dp = a.g_aux * static_cast<float>(LB_ALPHA * E) * (cnt / (K * Tf)) / Tf;
-  if constexpr (EC) {
+  if constexpr (EC) {   // the experts that took the token, eight at a time in ascending order
     const int myrow = a.inv_ec[(size_t)t * E + lane];
     float dwl = 0.f;
-    for (uint64_t m = __ballot(myrow >= 0); m; m &= m - 1) {
-      const int ej = __builtin_ctzll(m);
-      const float d = dot_row(__shfl(myrow, ej));
-      dwl = lane == ej ? d : dwl;
+    for (uint64_t m = __ballot(myrow >= 0); m;) {
+      int rows[K], ej[K];
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        ej[j] = m ? __builtin_ctzll(m) : -1;
+        rows[j] = m ? __shfl(myrow, ej[j]) : -1;
+        m &= m - 1;
+      }
+      float d[K];
+      dot_rows(rows, d);
+#pragma unroll
+      for (int j = 0; j < K; ++j) dwl = lane == ej[j] ? d[j] : dwl;
     }
     dp += dwl;
   } else {
-    float dw[K];
+    int rows[K];
 #pragma unroll
-    for (int j = 0; j < K; ++j) dw[j] = dot_row(a.inv[t * K + j]);
+    for (int j = 0; j < K; ++j) rows[j] = a.inv[t * K + j];
+    float dw[K];
+    dot_rows(rows, dw);
 #pragma unroll
     for (int j = 0; j < K; ++j) dp += a.ids[t * K + j] == lane ? dw[j] : 0.f;
   }
