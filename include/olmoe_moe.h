@@ -188,7 +188,7 @@ OLMOE_API olmoe_status_t olmoe_moe_forward_residual(const void* x, const float* 
  * weights and T; the caller keeps that pairing (the library cannot detect a
  * mismatch, and results are then meaningless).  saved is used as the backward's
  * workspace, so its forward state is consumed: run olmoe_moe_forward_train again
- * before another olmoe_moe_backward_saved.
+ * before another olmoe_moe_backward_saved.  Internal streams as olmoe_moe_backward.
  * Errors: as olmoe_moe_forward / olmoe_moe_backward (EWORKSPACE for a NULL or
  * short `saved`). */
 OLMOE_API size_t olmoe_moe_saved_bytes(int64_t T);   /* 0 for T out of range; host only */
@@ -246,7 +246,7 @@ OLMOE_API olmoe_status_t olmoe_moe_forward_expert_choice(const void* x, const fl
  * probabilities of the pairs the experts took).  Which tokens each expert takes
  * and the shares f_e = C / (8T) are piecewise constant and carry no gradient.
  * The forward is recomputed inside.  Arguments, outputs (fp32, overwritten),
- * precisions and errors as olmoe_moe_backward, with 0 <= T <=
+ * precisions, internal streams and errors as olmoe_moe_backward, with 0 <= T <=
  * OLMOE_EC_MAX_TOKENS and a workspace of olmoe_moe_ec_backward_workspace_bytes(T). */
 OLMOE_API size_t olmoe_moe_ec_backward_workspace_bytes(int64_t T);   /* 0 for T out of range; host only */
 OLMOE_API olmoe_status_t olmoe_moe_backward_expert_choice(const void* x, const float* W_router,
@@ -318,10 +318,17 @@ OLMOE_API olmoe_status_t olmoe_residual_add(float* h, const void* y, int64_t T, 
  * bf16 operands are the upstream gradient, the weights, the gathered inputs,
  * dG / dU and w*H (rounded to nearest even); G and U are kept in fp32; the
  * router gradient and the sums into dx run in fp32 in a fixed order.
+ * Streams: the two weight-gradient GEMMs run on two internal streams of the
+ * calling thread (one pair per device, default priority, created on the first
+ * backward call and kept until the process ends), ordered after the earlier
+ * work of this call on `stream` and joined back into `stream` with events, so
+ * `stream` still passes the call only when all of it is done (also under
+ * graph capture).  Backward calls from one thread share that pair.
  * Errors: OLMOE_EINVAL for NULL / misaligned pointers, T out of range,
  * non-finite g_aux / g_z, outputs overlapping an input, each other or the
  * workspace; OLMOE_EWORKSPACE for a NULL or short workspace; OLMOE_ENODEVICE /
- * OLMOE_EHIP as olmoe_moe_forward. */
+ * OLMOE_EHIP as olmoe_moe_forward (also when the internal streams cannot be
+ * created). */
 OLMOE_API size_t olmoe_moe_backward_workspace_bytes(int64_t T);
 OLMOE_API olmoe_status_t olmoe_moe_backward(const void* x, const float* W_router, const void* W_gate,
                                   const void* W_up, const void* W_down, int64_t T, const void* dout,

@@ -163,6 +163,66 @@ olmoe_status_t check_device() {
   return OLMOE_OK;
 }
 
+// ---------------------------------------------------------------- side streams
+
+// After the dH dgrad, the backward's two weight-gradient GEMMs depend on nothing the dX dgrad
+// writes, and the weight gradients are mostly stores of fp32 results while the dgrad is mostly
+// MFMA work: the two run on side streams of the calling thread (created once per device, default
+// priority, not synchronising with the null stream), forked from the caller's stream after the
+// dH dgrad and joined back into it at the end, so the caller's stream still orders all of a
+// call's work.  Calls from one thread share its side streams, which serialises their weight
+// gradients but keeps each call's order.  The streams live until the process ends.
+struct SideStreams {
+  hipStream_t s[2] = {nullptr, nullptr};
+  hipEvent_t fork = nullptr;
+  hipEvent_t join[2] = {nullptr, nullptr};
+};
+thread_local std::vector<SideStreams> g_side;   // per device, for this thread
+
+hipError_t side_streams(SideStreams** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if ((int)g_side.size() <= dev) g_side.resize(dev + 1);
+  SideStreams& ss = g_side[dev];
+  if (!ss.fork) {
+    SideStreams n;
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+      e = hipStreamCreateWithFlags(&n.s[i], hipStreamNonBlocking);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join[i], hipEventDisableTiming);
+    }
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      for (int i = 0; i < 2; ++i) {
+        if (n.s[i]) (void)hipStreamDestroy(n.s[i]);
+        if (n.join[i]) (void)hipEventDestroy(n.join[i]);
+      }
+      return e;
+    }
+    ss = n;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
+
+// the weight-gradient GEMMs wd and wgu on the side streams, after everything issued on s so far
+hipError_t fork_wgrads(const BwdWgradArgs& wd, const BwdWgradArgs& wgu, hipStream_t s, SideStreams& ss) {
+  hipError_t e = hipEventRecord(ss.fork, s);
+  for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+    e = hipStreamWaitEvent(ss.s[i], ss.fork, 0);
+    if (e == hipSuccess) e = launch_wgrad(i == 0 ? wd : wgu, ss.s[i]);
+    if (e == hipSuccess) e = hipEventRecord(ss.join[i], ss.s[i]);
+  }
+  return e;
+}
+
+// s waits for the side streams' work
+hipError_t join_wgrads(hipStream_t s, SideStreams& ss) {
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipStreamWaitEvent(s, ss.join[i], 0);
+  return e;
+}
+
 // ---------------------------------------------------------------- stage timing
 
 // router: logits and top-8 selection; dispatch: scan and permutation; then the
@@ -515,6 +575,15 @@ olmoe_status_t bwd_gradients(const void* x, const float* W_router, const void* W
   if (he == hipSuccess) he = launch_bwd_router(ba, s);
   if (he != hipSuccess) return fail(OLMOE_EHIP, "backward routing launch: %s", hipGetErrorString(he));
   const uint16_t* dgu = reinterpret_cast<const uint16_t*>(ws + B.dgu);
+  BwdWgradArgs wd{reinterpret_cast<const uint16_t*>(ws + B.dg), OLMOE_D, reinterpret_cast<const uint16_t*>(ws + B.hw),
+                  OLMOE_F, offsets, reinterpret_cast<const uint16_t*>(ws + B.zero), OLMOE_D, OLMOE_F, dW_down, dW_down,
+                  OLMOE_D, (long)OLMOE_D * OLMOE_F};
+  BwdWgradArgs wgu{dgu, 2 * OLMOE_F, reinterpret_cast<const uint16_t*>(ws + B.xg), OLMOE_D, offsets,
+                   reinterpret_cast<const uint16_t*>(ws + B.zero), 2 * OLMOE_F, OLMOE_D, dW_gate, dW_up, OLMOE_F,
+                   (long)OLMOE_F * OLMOE_D};
+  SideStreams* ss = nullptr;
+  he = side_streams(&ss);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "side streams: %s", hipGetErrorString(he));
   if (Ti > 0) {
     BwdDgradArgs dh{reinterpret_cast<const uint16_t*>(ws + B.dg), nullptr, static_cast<const uint16_t*>(W_down),
                     nullptr, OLMOE_F, (long)OLMOE_D * OLMOE_F, 2 * OLMOE_F,
@@ -528,19 +597,16 @@ olmoe_status_t bwd_gradients(const void* x, const float* W_router, const void* W
                      reinterpret_cast<const int2*>(ws + B.tiles_bwd), nullptr, nullptr, nullptr, nullptr,
                      reinterpret_cast<float*>(ws + B.dxr)};
     he = launch_dgrad(dh, Ti, true, s);
+    if (he == hipSuccess) he = fork_wgrads(wd, wgu, s, *ss);   // they need dH's outputs only
     if (he == hipSuccess) he = launch_dgrad(dxa, Ti, false, s);
-    if (he != hipSuccess) return fail(OLMOE_EHIP, "dgrad launch: %s", hipGetErrorString(he));
+    if (he != hipSuccess) return fail(OLMOE_EHIP, "gradient launch: %s", hipGetErrorString(he));
+  } else {
+    he = fork_wgrads(wd, wgu, s, *ss);
+    if (he != hipSuccess) return fail(OLMOE_EHIP, "weight-gradient launch: %s", hipGetErrorString(he));
   }
-  BwdWgradArgs wd{reinterpret_cast<const uint16_t*>(ws + B.dg), OLMOE_D, reinterpret_cast<const uint16_t*>(ws + B.hw),
-                  OLMOE_F, offsets, reinterpret_cast<const uint16_t*>(ws + B.zero), OLMOE_D, OLMOE_F, dW_down, dW_down,
-                  OLMOE_D, (long)OLMOE_D * OLMOE_F};
-  BwdWgradArgs wgu{dgu, 2 * OLMOE_F, reinterpret_cast<const uint16_t*>(ws + B.xg), OLMOE_D, offsets,
-                   reinterpret_cast<const uint16_t*>(ws + B.zero), 2 * OLMOE_F, OLMOE_D, dW_gate, dW_up, OLMOE_F,
-                   (long)OLMOE_F * OLMOE_D};
-  he = launch_wgrad(wd, s);
-  if (he == hipSuccess) he = launch_wgrad(wgu, s);
-  if (he == hipSuccess) he = launch_bwd_finish(ba, s);
-  if (he != hipSuccess) return fail(OLMOE_EHIP, "weight-gradient launch: %s", hipGetErrorString(he));
+  he = launch_bwd_finish(ba, s);
+  if (he == hipSuccess) he = join_wgrads(s, *ss);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "router-gradient launch: %s", hipGetErrorString(he));
   return ok();
 }
 
@@ -666,6 +732,15 @@ olmoe_status_t ec_bwd_gradients(const void* x, const float* W_router, const void
   if (he == hipSuccess) he = launch_bwd_router(ba, s);
   if (he != hipSuccess) return fail(OLMOE_EHIP, "backward routing launch: %s", hipGetErrorString(he));
   const uint16_t* dgu = reinterpret_cast<const uint16_t*>(ws + B.dgu);
+  BwdWgradArgs wd{reinterpret_cast<const uint16_t*>(ws + B.dg), OLMOE_D, reinterpret_cast<const uint16_t*>(ws + B.hw),
+                  OLMOE_F, offsets, reinterpret_cast<const uint16_t*>(ws + B.zero), OLMOE_D, OLMOE_F, dW_down, dW_down,
+                  OLMOE_D, (long)OLMOE_D * OLMOE_F};
+  BwdWgradArgs wgu{dgu, 2 * OLMOE_F, reinterpret_cast<const uint16_t*>(ws + B.xg), OLMOE_D, offsets,
+                   reinterpret_cast<const uint16_t*>(ws + B.zero), 2 * OLMOE_F, OLMOE_D, dW_gate, dW_up, OLMOE_F,
+                   (long)OLMOE_F * OLMOE_D};
+  SideStreams* ss = nullptr;
+  he = side_streams(&ss);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "side streams: %s", hipGetErrorString(he));
   if (Ti > 0) {
     BwdDgradArgs dh{reinterpret_cast<const uint16_t*>(ws + B.dg), nullptr, static_cast<const uint16_t*>(W_down),
                     nullptr, OLMOE_F, (long)OLMOE_D * OLMOE_F, 2 * OLMOE_F,
@@ -679,19 +754,16 @@ olmoe_status_t ec_bwd_gradients(const void* x, const float* W_router, const void
                      reinterpret_cast<const int2*>(ws + B.tiles_bwd), nullptr, nullptr, nullptr, nullptr,
                      reinterpret_cast<float*>(ws + B.dxr)};
     he = launch_dgrad(dh, Teff, true, s);
+    if (he == hipSuccess) he = fork_wgrads(wd, wgu, s, *ss);   // they need dH's outputs only
     if (he == hipSuccess) he = launch_dgrad(dxa, Teff, false, s);
-    if (he != hipSuccess) return fail(OLMOE_EHIP, "dgrad launch: %s", hipGetErrorString(he));
+    if (he != hipSuccess) return fail(OLMOE_EHIP, "gradient launch: %s", hipGetErrorString(he));
+  } else {
+    he = fork_wgrads(wd, wgu, s, *ss);
+    if (he != hipSuccess) return fail(OLMOE_EHIP, "weight-gradient launch: %s", hipGetErrorString(he));
   }
-  BwdWgradArgs wd{reinterpret_cast<const uint16_t*>(ws + B.dg), OLMOE_D, reinterpret_cast<const uint16_t*>(ws + B.hw),
-                  OLMOE_F, offsets, reinterpret_cast<const uint16_t*>(ws + B.zero), OLMOE_D, OLMOE_F, dW_down, dW_down,
-                  OLMOE_D, (long)OLMOE_D * OLMOE_F};
-  BwdWgradArgs wgu{dgu, 2 * OLMOE_F, reinterpret_cast<const uint16_t*>(ws + B.xg), OLMOE_D, offsets,
-                   reinterpret_cast<const uint16_t*>(ws + B.zero), 2 * OLMOE_F, OLMOE_D, dW_gate, dW_up, OLMOE_F,
-                   (long)OLMOE_F * OLMOE_D};
-  he = launch_wgrad(wd, s);
-  if (he == hipSuccess) he = launch_wgrad(wgu, s);
-  if (he == hipSuccess) he = launch_bwd_finish(ba, s);
-  if (he != hipSuccess) return fail(OLMOE_EHIP, "weight-gradient launch: %s", hipGetErrorString(he));
+  he = launch_bwd_finish(ba, s);
+  if (he == hipSuccess) he = join_wgrads(s, *ss);
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "router-gradient launch: %s", hipGetErrorString(he));
   return ok();
 }
 
