@@ -323,7 +323,9 @@ OLMOE_API olmoe_status_t olmoe_residual_add(float* h, const void* y, int64_t T, 
  * backward call and kept until the process ends), ordered after the earlier
  * work of this call on `stream` and joined back into `stream` with events, so
  * `stream` still passes the call only when all of it is done (also under
- * graph capture).  Backward calls from one thread share that pair.
+ * graph capture, where the fork and join become graph edges; the thread's first
+ * backward call on a device creates the pair, so make it outside a capture).
+ * Backward calls from one thread share that pair.
  * Errors: OLMOE_EINVAL for NULL / misaligned pointers, T out of range,
  * non-finite g_aux / g_z, outputs overlapping an input, each other or the
  * workspace; OLMOE_EWORKSPACE for a NULL or short workspace; OLMOE_ENODEVICE /

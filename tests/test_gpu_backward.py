@@ -227,3 +227,33 @@ def test_expert_choice_training_pair_equals_stateless_calls(weights, T):
     torch.cuda.synchronize()
     for k in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down"):
         assert torch.equal(b[k], b_ref[k]), k
+
+
+def test_backward_captured_in_a_graph_replays_exactly(weights):
+    """The backward, with its fork of the weight gradients onto the side streams and the join
+    back, captured in a HIP graph: every replay gives the eager call's bits, with eager work and
+    synchronisations between the replays."""
+    w, _ = weights
+    T = 300
+    x = inputs.device_x(T, seed=51, workload="parity")
+    dout = inputs.device_x(T, seed=52, workload="parity")
+    wts = (w["w_router"], w["w_gate"], w["w_up"], w["w_down"])
+    names = ("dx", "dw_router", "dw_gate", "dw_up", "dw_down")
+    first = binding.moe_backward(x, *wts, dout)
+    torch.cuda.synchronize()
+    ref = {k: first[k].clone() for k in names}
+    bufs = {k: torch.empty_like(ref[k]) for k in names}
+    ws = torch.empty(max(binding.backward_workspace_bytes(T), 256), dtype=torch.uint8, device="cuda")
+    binding.moe_backward(x, *wts, dout, workspace=ws, **bufs)   # outside the capture first
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        binding.moe_backward(x, *wts, dout, workspace=ws, **bufs)
+    for rep in range(3):
+        for v in bufs.values():
+            v.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in names:
+            assert torch.equal(bufs[k], ref[k]), (rep, k)
