@@ -62,8 +62,8 @@ def check_grad(got, ref, name, mag=None):
     return rel, worst
 
 
-def run_backward(w, hw, T, seed, g_aux, g_z):
-    x = inputs.device_x(T, seed=seed, workload="parity")
+def run_backward(w, hw, T, seed, g_aux, g_z, x=None):
+    x = inputs.device_x(T, seed=seed, workload="parity") if x is None else x
     g = torch.Generator(device="cuda")
     g.manual_seed(seed + 100)
     dout = torch.randn((T, 2048), generator=g, device="cuda").to(torch.bfloat16)
@@ -119,8 +119,8 @@ def test_backward_bitwise_reproducible(weights):
 # ------------------------------------------------------------------ expert choice
 
 
-def run_ec_backward(w, hw, T, seed, g_aux, g_z):
-    x = inputs.device_x(T, seed=seed, workload="parity")
+def run_ec_backward(w, hw, T, seed, g_aux, g_z, x=None):
+    x = inputs.device_x(T, seed=seed, workload="parity") if x is None else x
     g = torch.Generator(device="cuda")
     g.manual_seed(seed + 100)
     dout = torch.randn((T, 2048), generator=g, device="cuda").to(torch.bfloat16)
@@ -257,3 +257,22 @@ def test_backward_captured_in_a_graph_replays_exactly(weights):
         torch.cuda.synchronize()
         for k in names:
             assert torch.equal(bufs[k], ref[k]), (rep, k)
+
+
+@pytest.mark.parametrize("routing", ["token", "expert"])
+def test_backward_with_skewed_routing(weights, routing):
+    """The skewed workload's router (a few experts take several times the average row count, many
+    take few or none): unequal tile lists in the dgrad and long reductions in the weight gradients."""
+    w, hw = weights
+    sk = inputs.device_weights(seed=3, workload="skew-16384", skew=True)
+    w2 = dict(w, w_router=sk["w_router"])
+    hw2 = dict(hw, w_router=sk["w_router"].cpu().numpy())
+    T = 1000
+    x = inputs.device_x(T, seed=3, workload="skew-16384", skew=True)
+    _log(f"skewed backward ({routing}) T={T}")
+    if routing == "token":
+        counts = binding.moe_forward(x, *(w2[k] for k in ("w_router", "w_gate", "w_up", "w_down")))["expert_counts"]
+        assert counts.max().item() > 4 * (8 * T / 64)
+        run_backward(w2, hw2, T, seed=61, g_aux=1.0, g_z=1.0, x=x)
+    else:
+        run_ec_backward(w2, hw2, T, seed=61, g_aux=1.0, g_z=1.0, x=x)
