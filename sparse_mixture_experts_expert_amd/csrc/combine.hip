@@ -20,12 +20,12 @@ namespace olmoe {
 
 namespace {
 
-// one wavefront per token: 64 lanes x 32 columns (four 16-byte chunks per lane)
+// residual variant: one wavefront per token, 64 lanes x 32 columns (four 16-byte chunks per lane)
 constexpr int CMB_TOK_PER_WG = 4;
 
 template <bool RESIDUAL>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  const int t = blockIdx.x * CMB_TOK_PER_WG + (threadIdx.x >> 6);
+  const int t = RESIDUAL ? blockIdx.x * CMB_TOK_PER_WG + (threadIdx.x >> 6) : blockIdx.x;
   if (t >= a.T) return;
   const int lane = threadIdx.x & 63;
   int pos[K];
@@ -36,6 +36,30 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     p[j] = a.probs[t * K + j];
   }
   constexpr int NC = D / (64 * 8);   // 16-byte output chunks per lane
+  if constexpr (!RESIDUAL) {
+    // the plain layer output needs no whole-row step: wavefront w of the token's workgroup takes
+    // chunk w (four times the wavefronts in flight for the same loads and arithmetic)
+    static_assert(NC == 4, "a token's four chunks on the four wavefronts of its workgroup");
+    const int col = ((threadIdx.x >> 6) * 64 + lane) * 8;
+    u32x4 v[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) v[j] = *reinterpret_cast<const u32x4*>(a.y + (size_t)pos[j] * D + col);
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(p[j], f16_to_f32(static_cast<uint16_t>(v[j][i] & 0xFFFFu)), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(p[j], f16_to_f32(static_cast<uint16_t>(v[j][i] >> 16)), acc[2 * i + 1]);
+      }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+    *reinterpret_cast<u32x4*>(a.out + (size_t)t * D + col) = o;
+    return;
+  }
   float acc[NC][8];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -132,11 +156,11 @@ __global__ __launch_bounds__(256) void residual_add_kernel(float* __restrict__ h
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
-  const dim3 grid((a.T + CMB_TOK_PER_WG - 1) / CMB_TOK_PER_WG);
   if (a.h)
-    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(combine_kernel<true>, dim3((a.T + CMB_TOK_PER_WG - 1) / CMB_TOK_PER_WG), dim3(256), 0,
+                       stream, a);
+  else   // a workgroup per token
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(a.T), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
