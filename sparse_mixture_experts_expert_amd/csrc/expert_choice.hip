@@ -316,25 +316,26 @@ __global__ __launch_bounds__(NT) void ec_choose_kernel(EcArgs a) {
     a.tiles_dn[e * ndn + i] = make_int2(e * C + i * qdn, e | (min(qdn, C - i * qdn) << 8));
 }
 
-// One wavefront per token: lane e holds the row of (t, e) or -1; the chosen experts are taken
-// in ascending order, 8 rows per batch (a short batch repeats its first row with weight 0,
-// which adds exactly nothing), each lane summing 32 columns in fp32.
-constexpr int EC_CMB_TOK = 4;
+// Per token: lane e of each wavefront holds the row of (t, e) or -1; the chosen experts are
+// taken in ascending order, 8 rows per batch (a short batch repeats its first row with weight 0,
+// which adds exactly nothing), each lane summing 8 columns in fp32.
 
 __global__ __launch_bounds__(256) void ec_combine_kernel(EcArgs a) {
-  const int t = blockIdx.x * EC_CMB_TOK + (threadIdx.x >> 6);
+  // a workgroup per token, wavefront w on 512-column chunk w (four times the wavefronts in flight
+  // of one wavefront per token, for the same loads and arithmetic)
+  const int t = blockIdx.x;
   if (t >= a.T) return;
   const int lane = threadIdx.x & 63;
+  const int chunk = threadIdx.x >> 6;
+  static_assert(D / (64 * 8) == 4, "a token's four chunks on the four wavefronts of its workgroup");
   const int myrow = a.inv_ec[(size_t)t * E + lane];
   const float myw = myrow >= 0 ? a.row_w[myrow] : 0.f;
   uint64_t mask = __ballot(myrow >= 0);
-  if (a.token_counts && lane == 0) a.token_counts[t] = __popcll(mask);
-  constexpr int NC = D / (64 * 8);
-  float acc[NC][8];
+  if (a.token_counts && chunk == 0 && lane == 0) a.token_counts[t] = __popcll(mask);
+  const int col = (chunk * 64 + lane) * 8;
+  float acc[8];
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[c][i] = 0.f;
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   while (mask) {
     int pos[8];
     float wt[8];
@@ -345,28 +346,21 @@ __global__ __launch_bounds__(256) void ec_combine_kernel(EcArgs a) {
       pos[j] = ej >= 0 ? __shfl(myrow, ej) : pos[0];
       wt[j] = ej >= 0 ? __shfl(myw, ej) : 0.f;
     }
+    u32x4 v[8];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int col = (c * 64 + lane) * 8;
-      u32x4 v[8];
+    for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const u32x4*>(a.y + (size_t)pos[j] * D + col);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const u32x4*>(a.y + (size_t)pos[j] * D + col);
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[c][2 * i] = fmaf(wt[j], f16_to_f32(static_cast<uint16_t>(v[j][i] & 0xFFFFu)), acc[c][2 * i]);
-          acc[c][2 * i + 1] = fmaf(wt[j], f16_to_f32(static_cast<uint16_t>(v[j][i] >> 16)), acc[c][2 * i + 1]);
-        }
-    }
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(wt[j], f16_to_f32(static_cast<uint16_t>(v[j][i] & 0xFFFFu)), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(wt[j], f16_to_f32(static_cast<uint16_t>(v[j][i] >> 16)), acc[2 * i + 1]);
+      }
   }
+  u32x4 o;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    u32x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[c][2 * i], acc[c][2 * i + 1]);
-    *reinterpret_cast<u32x4*>(a.out + (size_t)t * D + (c * 64 + lane) * 8) = o;
-  }
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+  *reinterpret_cast<u32x4*>(a.out + (size_t)t * D + col) = o;
 }
 
 }  // namespace
@@ -401,7 +395,7 @@ hipError_t launch_ec_choose(const EcArgs& a, hipStream_t stream) {
 
 hipError_t launch_ec_combine(const EcArgs& a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(ec_combine_kernel, dim3((a.T + EC_CMB_TOK - 1) / EC_CMB_TOK), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(ec_combine_kernel, dim3(a.T), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
