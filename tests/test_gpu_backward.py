@@ -276,3 +276,43 @@ def test_backward_with_skewed_routing(weights, routing):
         run_backward(w2, hw2, T, seed=61, g_aux=1.0, g_z=1.0, x=x)
     else:
         run_ec_backward(w2, hw2, T, seed=61, g_aux=1.0, g_z=1.0, x=x)
+
+
+def test_backward_from_two_host_threads(weights):
+    """Two host threads each run a backward on their own stream and workspace at the same time
+    (each thread gets its own side streams): both give the bits of the same calls made alone."""
+    import threading
+    w, _ = weights
+    wts = (w["w_router"], w["w_gate"], w["w_up"], w["w_down"])
+    names = ("dx", "dw_router", "dw_gate", "dw_up", "dw_down")
+    cases = []
+    for T, seed in ((300, 71), (700, 72)):
+        x = inputs.device_x(T, seed=seed, workload="parity")
+        dout = inputs.device_x(T, seed=seed + 1, workload="parity")
+        r = binding.moe_backward(x, *wts, dout)
+        torch.cuda.synchronize()
+        bufs = {k: torch.empty_like(r[k]) for k in names}
+        ws = torch.empty(max(binding.backward_workspace_bytes(T), 256), dtype=torch.uint8, device="cuda")
+        cases.append((x, dout, {k: r[k].clone() for k in names}, bufs, ws, torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    errors = []
+
+    def run(case):
+        x, dout, _, bufs, ws, s = case
+        try:
+            for _ in range(3):
+                binding.moe_backward(x, *wts, dout, workspace=ws, stream=s, **bufs)
+            s.synchronize()
+        except Exception as e:   # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(c,)) for c in cases]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for x, dout, ref, bufs, ws, s in cases:
+        for k in names:
+            assert torch.equal(bufs[k], ref[k]), (x.shape[0], k)
