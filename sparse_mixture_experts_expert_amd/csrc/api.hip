@@ -68,7 +68,7 @@ Layout make_layout(int64_t T) {
   L.blk_psum = take(nblk * 64 * 4);
   L.blk_lse2 = take(nblk * 4);
   L.blk_base = take(nblk * 64 * 4);
-  L.perm = take(rows * 4);
+  L.perm = take((rows + 64) * 4);   // 64 spare entries: the weight-gradient kernel reads a stage's ids at once
   L.inv = take(rows * 4);
   L.h = take(rows * OLMOE_F * 2);
   L.y = take(rows * OLMOE_D * 2);
@@ -79,7 +79,7 @@ Layout make_layout(int64_t T) {
 // backward workspace: the forward's layout followed by the backward's own buffers
 struct BwdLayout {
   Layout f;
-  size_t p_all, lse, row_w, gu, xg, dg, dgu, hw, dxr, dlogits, dwr_part, zero, tp_bwd, tiles_bwd, total;
+  size_t p_all, lse, row_w, gu, dgu, hw, dxr, dlogits, dwr_part, zero, tp_bwd, tiles_bwd, total;
 };
 BwdLayout make_bwd_layout(int64_t T) {
   BwdLayout B{};
@@ -95,8 +95,6 @@ BwdLayout make_bwd_layout(int64_t T) {
   B.lse = take(t * 4);
   B.row_w = take(rows * 4);
   B.gu = take(rows * 2 * OLMOE_F * 4);
-  B.xg = take(rows * OLMOE_D * 2);
-  B.dg = take(rows * OLMOE_D * 2);
   B.dgu = take(rows * 2 * OLMOE_F * 2);
   B.hw = take(rows * OLMOE_F * 2);
   B.dxr = take(rows * OLMOE_D * 4);
@@ -567,25 +565,25 @@ olmoe_status_t bwd_gradients(const void* x, const float* W_router, const void* W
                   reinterpret_cast<const float*>(ws + B.p_all), reinterpret_cast<const float*>(ws + B.lse),
                   offsets, perm, reinterpret_cast<const int32_t*>(ws + L.inv),
                   reinterpret_cast<const uint16_t*>(ws + L.y), g_aux, g_z,
-                  reinterpret_cast<float*>(ws + B.dlogits), reinterpret_cast<uint16_t*>(ws + B.xg),
-                  reinterpret_cast<uint16_t*>(ws + B.dg), reinterpret_cast<const float*>(ws + B.dxr), dx,
+                  reinterpret_cast<float*>(ws + B.dlogits), reinterpret_cast<const float*>(ws + B.dxr), dx,
                   reinterpret_cast<float*>(ws + B.dwr_part), dW_router, reinterpret_cast<uint16_t*>(ws + B.zero),
                   reinterpret_cast<int32_t*>(ws + B.tp_bwd), reinterpret_cast<int2*>(ws + B.tiles_bwd)};
   he = launch_bwd_prepare(ba, s);
   if (he == hipSuccess) he = launch_bwd_router(ba, s);
   if (he != hipSuccess) return fail(OLMOE_EHIP, "backward routing launch: %s", hipGetErrorString(he));
   const uint16_t* dgu = reinterpret_cast<const uint16_t*>(ws + B.dgu);
-  BwdWgradArgs wd{reinterpret_cast<const uint16_t*>(ws + B.dg), OLMOE_D, reinterpret_cast<const uint16_t*>(ws + B.hw),
+  // dout and x rows are read through perm (expert order -> token) by the kernels that use them
+  BwdWgradArgs wd{static_cast<const uint16_t*>(dout), OLMOE_D, reinterpret_cast<const uint16_t*>(ws + B.hw),
                   OLMOE_F, offsets, reinterpret_cast<const uint16_t*>(ws + B.zero), OLMOE_D, OLMOE_F, dW_down, dW_down,
-                  OLMOE_D, (long)OLMOE_D * OLMOE_F};
-  BwdWgradArgs wgu{dgu, 2 * OLMOE_F, reinterpret_cast<const uint16_t*>(ws + B.xg), OLMOE_D, offsets,
+                  OLMOE_D, (long)OLMOE_D * OLMOE_F, perm, nullptr};
+  BwdWgradArgs wgu{dgu, 2 * OLMOE_F, static_cast<const uint16_t*>(x), OLMOE_D, offsets,
                    reinterpret_cast<const uint16_t*>(ws + B.zero), 2 * OLMOE_F, OLMOE_D, dW_gate, dW_up, OLMOE_F,
-                   (long)OLMOE_F * OLMOE_D};
+                   (long)OLMOE_F * OLMOE_D, nullptr, perm};
   SideStreams* ss = nullptr;
   he = side_streams(&ss);
   if (he != hipSuccess) return fail(OLMOE_EHIP, "side streams: %s", hipGetErrorString(he));
   if (Ti > 0) {
-    BwdDgradArgs dh{reinterpret_cast<const uint16_t*>(ws + B.dg), nullptr, static_cast<const uint16_t*>(W_down),
+    BwdDgradArgs dh{static_cast<const uint16_t*>(dout), perm, static_cast<const uint16_t*>(W_down),
                     nullptr, OLMOE_F, (long)OLMOE_D * OLMOE_F, 2 * OLMOE_F,
                     reinterpret_cast<const int32_t*>(ws + B.tp_bwd) + OLMOE_E,
                     reinterpret_cast<const int2*>(ws + B.tiles_bwd),
@@ -614,7 +612,7 @@ olmoe_status_t bwd_gradients(const void* x, const float* W_router, const void* W
 // for its 64C rows
 struct EcBwdLayout {
   EcLayout c;
-  size_t p_all, gu, xg, dg, dgu, hw, dxr, dlogits, dwr_part, zero, tp_bwd, tiles_bwd, total;
+  size_t p_all, gu, dgu, hw, dxr, dlogits, dwr_part, zero, tp_bwd, tiles_bwd, total;
 };
 EcBwdLayout make_ec_bwd_layout(int64_t T) {
   EcBwdLayout B{};
@@ -629,8 +627,6 @@ EcBwdLayout make_ec_bwd_layout(int64_t T) {
   const size_t t = static_cast<size_t>(T), rows = static_cast<size_t>(OLMOE_E) * C;
   B.p_all = take(t * OLMOE_E * 4);
   B.gu = take(rows * 2 * OLMOE_F * 4);
-  B.xg = take(rows * OLMOE_D * 2);
-  B.dg = take(rows * OLMOE_D * 2);
   B.dgu = take(rows * 2 * OLMOE_F * 2);
   B.hw = take(rows * OLMOE_F * 2);
   B.dxr = take(rows * OLMOE_D * 4);
@@ -723,8 +719,7 @@ olmoe_status_t ec_bwd_gradients(const void* x, const float* W_router, const void
                   reinterpret_cast<const float*>(ws + B.p_all), reinterpret_cast<const float*>(ws + L.lse),
                   offsets, perm, nullptr,
                   reinterpret_cast<const uint16_t*>(ws + L.f.y), g_aux, g_z,
-                  reinterpret_cast<float*>(ws + B.dlogits), reinterpret_cast<uint16_t*>(ws + B.xg),
-                  reinterpret_cast<uint16_t*>(ws + B.dg), reinterpret_cast<const float*>(ws + B.dxr), dx,
+                  reinterpret_cast<float*>(ws + B.dlogits), reinterpret_cast<const float*>(ws + B.dxr), dx,
                   reinterpret_cast<float*>(ws + B.dwr_part), dW_router, reinterpret_cast<uint16_t*>(ws + B.zero),
                   reinterpret_cast<int32_t*>(ws + B.tp_bwd), reinterpret_cast<int2*>(ws + B.tiles_bwd),
                   reinterpret_cast<const int32_t*>(ws + L.inv_ec), OLMOE_E * C};
@@ -732,17 +727,18 @@ olmoe_status_t ec_bwd_gradients(const void* x, const float* W_router, const void
   if (he == hipSuccess) he = launch_bwd_router(ba, s);
   if (he != hipSuccess) return fail(OLMOE_EHIP, "backward routing launch: %s", hipGetErrorString(he));
   const uint16_t* dgu = reinterpret_cast<const uint16_t*>(ws + B.dgu);
-  BwdWgradArgs wd{reinterpret_cast<const uint16_t*>(ws + B.dg), OLMOE_D, reinterpret_cast<const uint16_t*>(ws + B.hw),
+  // dout and x rows are read through perm (expert order -> token) by the kernels that use them
+  BwdWgradArgs wd{static_cast<const uint16_t*>(dout), OLMOE_D, reinterpret_cast<const uint16_t*>(ws + B.hw),
                   OLMOE_F, offsets, reinterpret_cast<const uint16_t*>(ws + B.zero), OLMOE_D, OLMOE_F, dW_down, dW_down,
-                  OLMOE_D, (long)OLMOE_D * OLMOE_F};
-  BwdWgradArgs wgu{dgu, 2 * OLMOE_F, reinterpret_cast<const uint16_t*>(ws + B.xg), OLMOE_D, offsets,
+                  OLMOE_D, (long)OLMOE_D * OLMOE_F, perm, nullptr};
+  BwdWgradArgs wgu{dgu, 2 * OLMOE_F, static_cast<const uint16_t*>(x), OLMOE_D, offsets,
                    reinterpret_cast<const uint16_t*>(ws + B.zero), 2 * OLMOE_F, OLMOE_D, dW_gate, dW_up, OLMOE_F,
-                   (long)OLMOE_F * OLMOE_D};
+                   (long)OLMOE_F * OLMOE_D, nullptr, perm};
   SideStreams* ss = nullptr;
   he = side_streams(&ss);
   if (he != hipSuccess) return fail(OLMOE_EHIP, "side streams: %s", hipGetErrorString(he));
   if (Ti > 0) {
-    BwdDgradArgs dh{reinterpret_cast<const uint16_t*>(ws + B.dg), nullptr, static_cast<const uint16_t*>(W_down),
+    BwdDgradArgs dh{static_cast<const uint16_t*>(dout), perm, static_cast<const uint16_t*>(W_down),
                     nullptr, OLMOE_F, (long)OLMOE_D * OLMOE_F, 2 * OLMOE_F,
                     reinterpret_cast<const int32_t*>(ws + B.tp_bwd) + OLMOE_E,
                     reinterpret_cast<const int2*>(ws + B.tiles_bwd),

@@ -22,33 +22,24 @@ namespace {
 constexpr int WR_SPLIT_TOKENS = 32;    // tokens per load batch of the dW_router partial kernel
 constexpr int WR_MAX_SPLITS = 32;      // dW_router partial sums at most (16: 80 + 6 us at 4096 tokens, 32: 48 + 10, 128: 46 + 33)
 
-// workgroup 0: zero row and the dgrad row-tile list; the others: x and dout rows in
-// expert order (one row per workgroup)
+// the zero row and the dgrad row-tile list (the GEMMs read x and dout rows through perm)
 __global__ __launch_bounds__(256) void bwd_prepare_kernel(BwdSmallArgs a, int bm) {
   const int tid = threadIdx.x;
-  if (blockIdx.x == 0) {
-    __shared__ int off[E + 1], tp[E + 1];
-    reinterpret_cast<u32x4*>(a.zero)[tid] = u32x4{0u, 0u, 0u, 0u};   // 4 KiB
-    if (tid <= E) off[tid] = a.offsets[tid];
-    __syncthreads();
-    if (tid == 0) {
-      int acc = 0;
-      for (int e = 0; e < E; ++e) {
-        tp[e] = acc;
-        acc += (off[e + 1] - off[e] + bm - 1) / bm;
-      }
-      tp[E] = acc;
+  __shared__ int off[E + 1], tp[E + 1];
+  reinterpret_cast<u32x4*>(a.zero)[tid] = u32x4{0u, 0u, 0u, 0u};   // 4 KiB
+  if (tid <= E) off[tid] = a.offsets[tid];
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int e = 0; e < E; ++e) {
+      tp[e] = acc;
+      acc += (off[e + 1] - off[e] + bm - 1) / bm;
     }
-    __syncthreads();
-    if (tid <= E) a.tp_bwd[tid] = tp[tid];
-    fill_tiles(tp, off, bm, a.tiles_bwd);
-    return;
+    tp[E] = acc;
   }
-  const int r = blockIdx.x - 1;
-  const int t = a.perm[r];
-  const int c = tid * 8;
-  *reinterpret_cast<u32x4*>(a.xg + (size_t)r * D + c) = *reinterpret_cast<const u32x4*>(a.x + (size_t)t * D + c);
-  *reinterpret_cast<u32x4*>(a.dg + (size_t)r * D + c) = *reinterpret_cast<const u32x4*>(a.dout + (size_t)t * D + c);
+  __syncthreads();
+  if (tid <= E) a.tp_bwd[tid] = tp[tid];
+  fill_tiles(tp, off, bm, a.tiles_bwd);
 }
 
 // one wavefront per token: dL/dw for its 8 rows (expert choice: for the rows of the experts that
@@ -248,7 +239,7 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(BwdSmallArgs a) {
 int bwd_router_splits(int T) { return min(WR_MAX_SPLITS, (T + WR_SPLIT_TOKENS - 1) / WR_SPLIT_TOKENS); }
 
 hipError_t launch_bwd_prepare(const BwdSmallArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(bwd_prepare_kernel, dim3(1 + (a.rows ? a.rows : K * a.T)), dim3(256), 0, stream, a,
+  hipLaunchKernelGGL(bwd_prepare_kernel, dim3(1), dim3(256), 0, stream, a,
                      bwd_tile_rows(a.rows ? a.rows / K : a.T));
   return hipGetLastError();
 }

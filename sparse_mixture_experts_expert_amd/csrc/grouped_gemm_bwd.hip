@@ -57,6 +57,12 @@ __device__ __forceinline__ int kout_off(int k, int col) {
 // element offset of chunk ch of row `row` in a K-inner tile of 64-element rows
 __device__ __forceinline__ int kin_off(int row, int ch) { return row * 64 + ((ch ^ (row & 7)) << 3); }
 
+// a table read through the constant address space: wave-uniform reads of it become scalar loads
+using cint_ptr = const __attribute__((address_space(4))) int*;
+__device__ __forceinline__ cint_ptr as_const(const int32_t* p) {
+  return (cint_ptr)reinterpret_cast<uintptr_t>(p);
+}
+
 // LDS byte address (offset in the LDS aperture) of element e of a K-outer tile
 __device__ __forceinline__ uint32_t lds_addr(const bf16_t* tile, int e) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const bf16_t*)(tile + e)));
@@ -320,32 +326,49 @@ __global__ __launch_bounds__(C::NT) void wgrad_kernel(BwdWgradArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv / C::WN, wn = wv % C::WN;
 
-  // both operands K-outer: load j fills k-rows (j*NW + wv)*RP + lane/CP, slot lane%CP
+  // both operands K-outer: load j of A fills k-rows (wv*IPA + j)*RPA + lane/CPA, slot lane%CPA (B
+  // alike), so a wave's loads of one stage cover KW consecutive k-rows of either operand
+  constexpr int KW = C::IPA * C::RPA;
+  static_assert(KW == C::IPB * C::RPB && C::RPA == 2 && C::RPB == 2, "a wave's k-rows of a stage");
   int ka[C::IPA], oa[C::IPA], kb[C::IPB], ob[C::IPB];
 #pragma unroll
   for (int j = 0; j < C::IPA; ++j) {
-    ka[j] = (j * C::NW + wv) * C::RPA + lane / C::CPA;
+    ka[j] = (wv * C::IPA + j) * C::RPA + lane / C::CPA;
     oa[j] = mt * C::BM + (((lane % C::CPA) ^ ((ka[j] & 3) << 1)) << 3);
   }
 #pragma unroll
   for (int j = 0; j < C::IPB; ++j) {
-    kb[j] = (j * C::NW + wv) * C::RPB + lane / C::CPB;
+    kb[j] = (wv * C::IPB + j) * C::RPB + lane / C::CPB;
     ob[j] = nt * C::BN + (((lane % C::CPB) ^ ((kb[j] & 3) << 1)) << 3);
   }
-  auto issue = [&](int kt, int sl, int j0, int j1) {
+  // a gathered operand reads row rows_x[r0 + k] for the expert's row k; the KW ids a wave needs
+  // for a stage come from one scalar load of the table (read through the constant address space,
+  // so the load is counted by lgkmcnt and leaves the vmcnt accounting of the LDS-DMA ring alone),
+  // fetched a stage before they are used.  The table is padded past its last row, so the ids of a
+  // stage's rows beyond the expert's count can be read (and are not used).
+  const bool gather = a.a_rows != nullptr || a.b_rows != nullptr;
+  const auto gtab = as_const(a.a_rows ? a.a_rows : a.b_rows);
+  auto load_ids = [&](int kt, int (&ids)[KW]) {
+    const int base = __builtin_amdgcn_readfirstlane(r0 + kt * BK + wv * KW);
+#pragma unroll
+    for (int i = 0; i < KW; ++i) ids[i] = gtab[base + i];
+  };
+  auto issue = [&](int kt, int sl, int j0, int j1, const int (&ids)[KW]) {
 #pragma unroll
     for (int j = 0; j < C::IPS; ++j) {
       if (j < j0 || j >= j1) continue;
       if (j < C::IPA) {
         const int k = kt * BK + ka[j];   // rows past the expert's count read zeros
-        const bf16_t* src = k < rows ? a.a + (size_t)(r0 + k) * a.lda + oa[j] : a.zero + (oa[j] - mt * C::BM);
-        __builtin_amdgcn_global_load_lds(GPTR(src), LPTR(&smem[sl][(j * C::NW + wv) * C::RPA * C::BM]), 16, 0, 0);
+        const int srow = a.a_rows ? ((lane >> 5) ? ids[2 * j + 1] : ids[2 * j]) : r0 + k;
+        const bf16_t* src = k < rows ? a.a + (size_t)srow * a.lda + oa[j] : a.zero + (oa[j] - mt * C::BM);
+        __builtin_amdgcn_global_load_lds(GPTR(src), LPTR(&smem[sl][(wv * C::IPA + j) * C::RPA * C::BM]), 16, 0, 0);
       } else {
         const int jb = j - C::IPA;
         const int k = kt * BK + kb[jb];
-        const bf16_t* src = k < rows ? a.b + (size_t)(r0 + k) * a.ldb + ob[jb] : a.zero + (ob[jb] - nt * C::BN);
+        const int srow = a.b_rows ? ((lane >> 5) ? ids[2 * jb + 1] : ids[2 * jb]) : r0 + k;
+        const bf16_t* src = k < rows ? a.b + (size_t)srow * a.ldb + ob[jb] : a.zero + (ob[jb] - nt * C::BN);
         __builtin_amdgcn_global_load_lds(GPTR(src),
-                                         LPTR(&smem[sl][C::A_ELEMS + (jb * C::NW + wv) * C::RPB * C::BN]), 16, 0, 0);
+                                         LPTR(&smem[sl][C::A_ELEMS + (wv * C::IPB + jb) * C::RPB * C::BN]), 16, 0, 0);
       }
     }
   };
@@ -358,11 +381,21 @@ __global__ __launch_bounds__(C::NT) void wgrad_kernel(BwdWgradArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-#pragma unroll
-  for (int s = 0; s < C::STAGES - 1; ++s)
-    if (s < KT) issue(s, s, 0, C::IPS);
+  // idn: ids of the next stage to issue; idf: of the one after it.  The first two stages' ids are
+  // waited for here, once, so that inside the loop only the one-stage-ahead load is in flight
+  static_assert(C::STAGES == 2, "the id prefetch assumes a two-stage ring");
+  int idn[KW] = {}, idf[KW] = {};
+  if (KT > 0) {
+    if (gather) {
+      load_ids(0, idf);
+      if (KT > 1) load_ids(1, idn);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt unconstrained
+    }
+    issue(0, 0, 0, C::IPS, idf);
+  }
   constexpr int NKK = BK / 16;
   for (int kt = 0; kt < KT; ++kt) {
+    if (gather && kt + C::STAGES < KT) load_ids(kt + C::STAGES, idf);
     wait_stage_b<C::STAGES - 2, C::IPS>(min(C::STAGES - 2, KT - 1 - kt));
     const bool more = kt + C::STAGES - 1 < KT;
     const int next_slot = (kt + C::STAGES - 1) % C::STAGES;
@@ -370,7 +403,7 @@ __global__ __launch_bounds__(C::NT) void wgrad_kernel(BwdWgradArgs a) {
     const bf16_t* Bs = As + C::A_ELEMS;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      if (more) issue(kt + C::STAGES - 1, next_slot, kk * C::IPS / NKK, (kk + 1) * C::IPS / NKK);
+      if (more) issue(kt + C::STAGES - 1, next_slot, kk * C::IPS / NKK, (kk + 1) * C::IPS / NKK, idn);
       bf16x8 af[C::FM], bfr[C::FN];
       static_assert(C::FM % 2 == 0 && C::FN % 2 == 0, "operands are read in pairs");
 #pragma unroll
@@ -387,6 +420,8 @@ __global__ __launch_bounds__(C::NT) void wgrad_kernel(BwdWgradArgs a) {
         for (int j = 0; j < C::FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
+#pragma unroll
+    for (int i = 0; i < KW; ++i) idn[i] = idf[i];
   }
 
   // output row m (of m_total) goes to out0 below m_split, out1 above; the gradients are not read

@@ -173,9 +173,9 @@ hipError_t launch_dgrad(const BwdDgradArgs& a, int T, bool dh, hipStream_t strea
 
 // wgrad: per expert, out[m][n] = sum over the expert's rows r of a[r][m] * b[r][n]
 struct BwdWgradArgs {
-  const uint16_t* a;          // bf16 [rows, lda], expert-contiguous
+  const uint16_t* a;          // bf16 [rows, lda], expert-contiguous (or gathered through a_rows)
   int lda;
-  const uint16_t* b;          // bf16 [rows, ldb]
+  const uint16_t* b;          // bf16 [rows, ldb] (or gathered through b_rows)
   int ldb;
   const int32_t* offsets;     // [65]
   const uint16_t* zero;       // at least 256 zero bytes (rows past an expert's count)
@@ -184,6 +184,10 @@ struct BwdWgradArgs {
   float* out1;                // rows m >= m_split (at m - m_split)
   int m_split;
   long out_stride;            // elements per expert in out0 / out1
+  // row -> source row of a / b (expert order -> token), or null (row itself); at most one of the
+  // two, and the table must stay readable 64 entries past its last row
+  const int32_t* a_rows = nullptr;
+  const int32_t* b_rows = nullptr;
 };
 hipError_t launch_wgrad(const BwdWgradArgs& a, hipStream_t stream);
 
@@ -201,8 +205,6 @@ struct BwdSmallArgs {
   const uint16_t* y;          // fp16 [8T,2048] expert outputs
   float g_aux, g_z;
   float* dlogits;             // fp32 [T,64]
-  uint16_t* xg;               // bf16 [8T,2048] x rows in expert order
-  uint16_t* dg;               // bf16 [8T,2048] dout rows in expert order
   const float* dxr;           // fp32 [8T,2048] per-row input gradients
   float* dx;                  // fp32 [T,2048]
   float* dwr_part;            // fp32 [nsplit,64,2048]
@@ -214,7 +216,7 @@ struct BwdSmallArgs {
   int rows = 0;                      // rows in expert order (0: 8T)
 };
 int bwd_router_splits(int T);
-hipError_t launch_bwd_prepare(const BwdSmallArgs& a, hipStream_t stream);   // zero row, tile list, gathers
+hipError_t launch_bwd_prepare(const BwdSmallArgs& a, hipStream_t stream);   // zero row, dgrad tile list
 hipError_t launch_bwd_router(const BwdSmallArgs& a, hipStream_t stream);    // dw and dlogits
 hipError_t launch_bwd_finish(const BwdSmallArgs& a, hipStream_t stream);    // dW_router and dx
 
