@@ -312,7 +312,7 @@ OLMOE_API olmoe_status_t olmoe_residual_add(float* h, const void* y, int64_t T, 
  *   dW_up      fp32 [64,1024,2048]
  *   dW_down    fp32 [64,2048,1024]
  *   workspace  device buffer of olmoe_moe_backward_workspace_bytes(T) bytes,
- *              256-byte aligned (about 290 KiB per token)
+ *              256-byte aligned (about 230 KiB per token)
  *
  * Arithmetic: the gradient GEMMs run on bf16 MFMA with fp32 accumulation; their
  * bf16 operands are the upstream gradient, the weights, the gathered inputs,
