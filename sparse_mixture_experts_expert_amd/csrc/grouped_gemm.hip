@@ -309,11 +309,20 @@ using GuTiny = Cfg<32, 64, 1, 2, true, 4, 64, 1, true>;
 using DnTiny = Cfg<32, 64, 1, 2, false, 4>;
 using GuSmall = Cfg<64, 128, 2, 4, true, 2, 64, 1, true>;
 using DnSmall = Cfg<64, 256, 2, 4, false, 2, 64, 1, true>;
+// a few hundred tokens up to about a thousand: experts hold 60-130 rows, so 64-row tiles would
+// stream most experts' weights twice and 256-row tiles leave most of each tile padding; 128-row
+// tiles in the small tiles' streaming style (two 64-k stages, non-temporal weights, rotated start)
+// stream each expert's weights about once (layer 0.183 against 0.206 ms at 416 tokens, 0.206
+// against 0.236 at 768, 0.237 against 0.247 at 832, and 0.269 against 0.243 at 896, where the
+// 256-row tiles take over; three 32-k stages instead were slower than both neighbours)
+using GuMed = Cfg<128, 128, 2, 4, true, 2, 64, 1, true>;
+using DnMed = Cfg<128, 256, 2, 4, false, 2, 64, 1, true>;
 using GuLarge = Cfg<256, 128, 4, 2, true, 3, 32, 0>;
 using DnLarge = Cfg<256, 256, 2, 4, false, 2, 64, 0>;
-// 64-row tiles stream an expert's weights once per tile, so they lose to the 256-row tiles as
-// soon as experts commonly hold more than 64 rows (measured crossover between 384 and 512 tokens)
-constexpr int SMALL_PLAN_TOKENS = 448;
+// 64-row tiles stream an expert's weights once per tile, so they lose as soon as experts commonly
+// hold more than 64 rows; the 128-row tiles likewise beyond about 128 rows
+constexpr int SMALL_PLAN_TOKENS = 384;
+constexpr int MEDIUM_PLAN_TOKENS = 832;
 
 template <class C>
 hipError_t launch_cfg(const bf16_t* A, const bf16_t* W0, const bf16_t* W1, const GemmArgs& a,
@@ -352,6 +361,10 @@ GemmPlan plan_gemm(int T) {
     p.variant = 1;
     p.bm_gu = GuSmall::BM;
     p.bm_dn = DnSmall::BM;
+  } else if (T <= MEDIUM_PLAN_TOKENS) {
+    p.variant = 3;
+    p.bm_gu = GuMed::BM;
+    p.bm_dn = DnMed::BM;
   } else {
     p.variant = 2;
     p.bm_gu = GuLarge::BM;
@@ -365,12 +378,14 @@ hipError_t launch_gateup(const GemmArgs& a, const GemmPlan& p, hipStream_t strea
     switch (p.variant) {
       case 0: return launch_cfg<SavingGU<GuTiny>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
       case 1: return launch_cfg<SavingGU<GuSmall>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
+      case 3: return launch_cfg<SavingGU<GuMed>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
       default: return launch_cfg<SavingGU<GuLarge>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
     }
   }
   switch (p.variant) {
     case 0: return launch_cfg<GuTiny>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
     case 1: return launch_cfg<GuSmall>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
+    case 3: return launch_cfg<GuMed>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
     default: return launch_cfg<GuLarge>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
   }
 }
@@ -379,6 +394,7 @@ hipError_t launch_down(const GemmArgs& a, const GemmPlan& p, hipStream_t stream)
   switch (p.variant) {
     case 0: return launch_cfg<DnTiny>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
     case 1: return launch_cfg<DnSmall>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
+    case 3: return launch_cfg<DnMed>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
     default: return launch_cfg<DnLarge>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
   }
 }
