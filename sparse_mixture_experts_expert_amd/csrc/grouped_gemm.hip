@@ -321,6 +321,10 @@ using DnMed = Cfg<128, 256, 2, 4, false, 2, 64, 1, true>;
 // tokens, 0.228 against 0.253 at 1024; 0.277 against 0.272 at 1280, where the 256-row tiles win)
 using GuMed192 = Cfg<192, 128, 2, 4, true, 2, 64, 1, true>;
 using DnMed192 = Cfg<192, 256, 2, 4, false, 2, 64, 1, true>;
+// 256-row tiles in that style still lead up to about 1500 tokens (0.255 against 0.273 ms at 1280,
+// 0.281 against 0.290 at 1536), level at 1792, and behind the MFMA-tuned large tiles from 2048
+using GuMed256 = Cfg<256, 128, 2, 4, true, 2, 64, 1, true>;
+using DnMed256 = Cfg<256, 256, 2, 4, false, 2, 64, 1, true>;
 using GuLarge = Cfg<256, 128, 4, 2, true, 3, 32, 0>;
 using DnLarge = Cfg<256, 256, 2, 4, false, 2, 64, 0>;
 // 64-row tiles stream an expert's weights once per tile, so they lose as soon as experts commonly
@@ -328,6 +332,7 @@ using DnLarge = Cfg<256, 256, 2, 4, false, 2, 64, 0>;
 constexpr int SMALL_PLAN_TOKENS = 384;
 constexpr int MEDIUM_PLAN_TOKENS = 832;
 constexpr int MEDIUM192_PLAN_TOKENS = 1024;
+constexpr int MEDIUM256_PLAN_TOKENS = 1536;
 
 template <class C>
 hipError_t launch_cfg(const bf16_t* A, const bf16_t* W0, const bf16_t* W1, const GemmArgs& a,
@@ -374,6 +379,10 @@ GemmPlan plan_gemm(int T) {
     p.variant = 4;
     p.bm_gu = GuMed192::BM;
     p.bm_dn = DnMed192::BM;
+  } else if (T <= MEDIUM256_PLAN_TOKENS) {
+    p.variant = 5;
+    p.bm_gu = GuMed256::BM;
+    p.bm_dn = DnMed256::BM;
   } else {
     p.variant = 2;
     p.bm_gu = GuLarge::BM;
@@ -389,6 +398,7 @@ hipError_t launch_gateup(const GemmArgs& a, const GemmPlan& p, hipStream_t strea
       case 1: return launch_cfg<SavingGU<GuSmall>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
       case 3: return launch_cfg<SavingGU<GuMed>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
       case 4: return launch_cfg<SavingGU<GuMed192>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
+      case 5: return launch_cfg<SavingGU<GuMed256>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
       default: return launch_cfg<SavingGU<GuLarge>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
     }
   }
@@ -397,6 +407,7 @@ hipError_t launch_gateup(const GemmArgs& a, const GemmPlan& p, hipStream_t strea
     case 1: return launch_cfg<GuSmall>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
     case 3: return launch_cfg<GuMed>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
     case 4: return launch_cfg<GuMed192>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
+    case 5: return launch_cfg<GuMed256>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
     default: return launch_cfg<GuLarge>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
   }
 }
@@ -407,6 +418,7 @@ hipError_t launch_down(const GemmArgs& a, const GemmPlan& p, hipStream_t stream)
     case 1: return launch_cfg<DnSmall>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
     case 3: return launch_cfg<DnMed>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
     case 4: return launch_cfg<DnMed192>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
+    case 5: return launch_cfg<DnMed256>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
     default: return launch_cfg<DnLarge>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
   }
 }
