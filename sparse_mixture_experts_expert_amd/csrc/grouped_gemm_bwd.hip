@@ -453,7 +453,9 @@ constexpr int DGRAD_SMALL_TOKENS = 320;
 // one partly filled row tile per expert, the 128-row tiles are faster)
 using DgDHL = DCfg<256, 256, 4, 2, 2, EPI_DH>;
 using DgDXL = DCfg<256, 256, 4, 2, 2, EPI_F32>;
-constexpr int DGRAD_LARGE_TOKENS = 448;
+// the 128-row tiles keep the lead while experts hold up to about 100 rows (backward 0.729 against
+// 0.757 ms at 512 tokens, 0.808 against 0.827 at 768; 0.918 against 0.904 at 1024)
+constexpr int DGRAD_LARGE_TOKENS = 768;
 // 256x256 tiles on 8 waves: each operand row is re-read half as often as with 128x128 tiles on 4
 // waves, and the fewer, larger units also write their fp32 gradients faster (measured 13% off the
 // whole backward at both 256 and 4096 tokens)

@@ -88,7 +88,8 @@ def run_backward(w, hw, T, seed, g_aux, g_z, x=None):
 
 
 @pytest.mark.parametrize("T,g_aux,g_z", [(1, 1.0, 1.0), (33, 1.0, 1.0), (200, 0.0, 0.0), (200, 5.0, -3.0),
-                                         (400, 1.0, 1.0), (700, 1.0, 1.0), (2100, 1.0, 1.0), (4096, 1.0, 1.0)])
+                                         (400, 1.0, 1.0), (700, 1.0, 1.0), (769, 1.0, 1.0), (2100, 1.0, 1.0),
+                                         (4096, 1.0, 1.0)])
 def test_backward_matches_oracle(weights, T, g_aux, g_z):
     w, hw = weights
     _log(f"backward T={T}")
