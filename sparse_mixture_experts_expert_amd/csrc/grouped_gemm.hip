@@ -325,6 +325,11 @@ using DnMed192 = Cfg<192, 256, 2, 4, false, 2, 64, 1, true>;
 // 0.281 against 0.290 at 1536), level at 1792, and behind the MFMA-tuned large tiles from 2048
 using GuMed256 = Cfg<256, 128, 2, 4, true, 2, 64, 1, true>;
 using DnMed256 = Cfg<256, 256, 2, 4, false, 2, 64, 1, true>;
+// and 384-row streaming tiles (three 32-k stages on 4 x 2 waves to fit LDS) up to about 2500
+// tokens: 0.339 against 0.379 ms at 1792, 0.364 against 0.389 at 2048, 0.383 against 0.400 at
+// 2560; at 3072 (0.568 against 0.442) experts commonly outgrow one tile
+using GuMed384 = Cfg<384, 128, 4, 2, true, 3, 32, 1, true>;
+using DnMed384 = Cfg<384, 256, 4, 2, false, 3, 32, 1, true>;
 using GuLarge = Cfg<256, 128, 4, 2, true, 3, 32, 0>;
 using DnLarge = Cfg<256, 256, 2, 4, false, 2, 64, 0>;
 // 64-row tiles stream an expert's weights once per tile, so they lose as soon as experts commonly
@@ -333,6 +338,7 @@ constexpr int SMALL_PLAN_TOKENS = 384;
 constexpr int MEDIUM_PLAN_TOKENS = 832;
 constexpr int MEDIUM192_PLAN_TOKENS = 1024;
 constexpr int MEDIUM256_PLAN_TOKENS = 1536;
+constexpr int MEDIUM384_PLAN_TOKENS = 2560;
 
 template <class C>
 hipError_t launch_cfg(const bf16_t* A, const bf16_t* W0, const bf16_t* W1, const GemmArgs& a,
@@ -383,6 +389,10 @@ GemmPlan plan_gemm(int T) {
     p.variant = 5;
     p.bm_gu = GuMed256::BM;
     p.bm_dn = DnMed256::BM;
+  } else if (T <= MEDIUM384_PLAN_TOKENS) {
+    p.variant = 6;
+    p.bm_gu = GuMed384::BM;
+    p.bm_dn = DnMed384::BM;
   } else {
     p.variant = 2;
     p.bm_gu = GuLarge::BM;
@@ -399,6 +409,7 @@ hipError_t launch_gateup(const GemmArgs& a, const GemmPlan& p, hipStream_t strea
       case 3: return launch_cfg<SavingGU<GuMed>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
       case 4: return launch_cfg<SavingGU<GuMed192>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
       case 5: return launch_cfg<SavingGU<GuMed256>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
+      case 6: return launch_cfg<SavingGU<GuMed384>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
       default: return launch_cfg<SavingGU<GuLarge>>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream, a.gu);
     }
   }
@@ -408,6 +419,7 @@ hipError_t launch_gateup(const GemmArgs& a, const GemmPlan& p, hipStream_t strea
     case 3: return launch_cfg<GuMed>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
     case 4: return launch_cfg<GuMed192>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
     case 5: return launch_cfg<GuMed256>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
+    case 6: return launch_cfg<GuMed384>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
     default: return launch_cfg<GuLarge>(a.x, a.w_gate, a.w_up, a, a.tile_prefix_gu, a.tiles_gu, a.h, stream);
   }
 }
@@ -419,6 +431,7 @@ hipError_t launch_down(const GemmArgs& a, const GemmPlan& p, hipStream_t stream)
     case 3: return launch_cfg<DnMed>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
     case 4: return launch_cfg<DnMed192>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
     case 5: return launch_cfg<DnMed256>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
+    case 6: return launch_cfg<DnMed384>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
     default: return launch_cfg<DnLarge>(a.h, a.w_down, nullptr, a, a.tile_prefix_dn, a.tiles_dn, a.y, stream);
   }
 }

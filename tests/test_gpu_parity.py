@@ -82,10 +82,10 @@ def test_layer_matches_oracle(weights, T):
     full_check(run_layer(x, w), hw, f"T={T}")
 
 
-@pytest.mark.parametrize("T", [449, 641, 832, 833, 1024, 1025, 1536, 1537, 2049, 2600])
+@pytest.mark.parametrize("T", [449, 641, 832, 833, 1024, 1025, 1536, 1537, 2049, 2560, 2561, 2600])
 def test_layer_matches_oracle_large_tile_plans(weights, T):
     """Batches served by the 128-row (385 to 832 tokens), 192-row (to 1024), streaming 256-row (to
-    1536) and MFMA-tuned 256-row tile plans, ragged tails included."""
+    1536), 384-row (to 2560) and MFMA-tuned 256-row tile plans, ragged tails included."""
     w, hw = weights
     _log(f"layer T={T}")
     x = inputs.device_x(T, seed=4, workload="parity")
