@@ -366,6 +366,84 @@ def test_stack_with_zero_down_is_identity_and_one_layer_matches_layer():
     np.testing.assert_array_equal(per[0]["x_in"], oracle.bf16_bits(xin))
 
 
+def _torch_block_stack(h0, layers, k, teacher=None, norm_from_h0=False, no_accumulate=False):
+    """The pre-norm residual stack ("Mixture-of-experts LLMs from scratch with OLMoE", section 3:
+    each block adds its MoE output to the float residual it normalised) written independently of
+    the oracle: torch float64, library rms_norm, a library top-k, and every expert run on every
+    token with the unchosen gates zero.  The two flags plant the mistakes the pin must catch:
+    normalising the first state at every layer, and adding each output to the first state."""
+    F_ = torch.nn.functional
+    hh = torch.from_numpy(np.asarray(h0, np.float64))
+    first = hh.clone()
+    outs = []
+    for l, w in enumerate(layers):
+        if teacher is not None:
+            x = torch.from_numpy(oracle.to_f64(teacher[l]))
+        else:
+            src = first if norm_from_h0 else hh
+            u = F_.rms_norm(src, (src.shape[1],), eps=1e-5)
+            x = u.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+        wr = torch.from_numpy(w["w_router"].astype(np.float64))
+        logits = x @ wr.T
+        p = torch.softmax(logits, dim=1)
+        top = torch.topk(logits, k, dim=1).indices
+        gate = torch.zeros_like(p).scatter(1, top, p.gather(1, top))
+        out = torch.zeros_like(x)
+        for e in range(wr.shape[0]):
+            wg = torch.from_numpy(oracle.to_f64(w["w_gate"][e]))
+            wu = torch.from_numpy(oracle.to_f64(w["w_up"][e]))
+            wd = torch.from_numpy(oracle.to_f64(w["w_down"][e]))
+            out += gate[:, e:e + 1] * ((F_.silu(x @ wg.T) * (x @ wu.T)) @ wd.T)
+        outs.append(out.numpy())
+        hh = (first if no_accumulate else hh) + out
+    return hh.numpy(), outs
+
+
+def test_stack_recursion_against_independent_block_stack():
+    """Three layers with non-zero outputs: the oracle's stack equals the independent torch
+    formulation, and both planted mistakes (RMSNorm of the first state fed to every layer; each
+    output added to the first state) move the result far outside the comparison's tolerance."""
+    T, D, F, E, k = 6, 32, 16, 8, 4
+    h0 = np.random.default_rng(21).standard_normal((T, D)).astype(np.float32)
+    layers = [inputs.host_layer(T, seed=40 + l, dims=(D, F, E), w_std=0.5) for l in range(3)]
+    h, per = oracle.moe_stack_ref(h0, layers, k=k)
+    want, outs = _torch_block_stack(h0, layers, k)
+    scale = np.abs(want).max()
+    np.testing.assert_allclose(h, want, rtol=0, atol=1e-12 * scale)
+    for l in range(3):
+        np.testing.assert_allclose(per[l]["out"], outs[l], rtol=0, atol=1e-12 * scale)
+    # every layer contributes, so the recursion is exercised
+    assert all(np.linalg.norm(o) > 0.2 * np.linalg.norm(h0) for o in outs)
+    for bug in (dict(norm_from_h0=True), dict(no_accumulate=True)):
+        wrong, _ = _torch_block_stack(h0, layers, k, **bug)
+        assert np.abs(wrong - h).max() > 1e-3 * scale, bug
+    # the same recursion unrolled by hand from the single-layer oracle
+    hh = h0.astype(np.float64)
+    for l, w in enumerate(layers):
+        xin = oracle.rmsnorm_bf16(hh)
+        np.testing.assert_array_equal(per[l]["x_in"], oracle.bf16_bits(xin))
+        hh = hh + oracle.moe_layer_ref(xin, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], k)["out"]
+    np.testing.assert_array_equal(h, hh)
+
+
+def test_stack_teacher_forced_inputs():
+    """teacher_inputs: every layer runs on its given bf16 input, and the residual is h0 plus the
+    sum of those outputs; fed the free-running stack's own inputs it reproduces that stack."""
+    T, D, F, E, k = 5, 32, 16, 8, 4
+    h0 = np.random.default_rng(22).standard_normal((T, D)).astype(np.float32)
+    layers = [inputs.host_layer(T, seed=50 + l, dims=(D, F, E), w_std=0.5) for l in range(3)]
+    teach = [inputs.host_layer(T, seed=60 + l, dims=(D, F, E))["x"] for l in range(3)]
+    h, per = oracle.moe_stack_ref(h0, layers, k=k, teacher_inputs=teach)
+    want, _ = _torch_block_stack(h0, layers, k, teacher=teach)
+    np.testing.assert_allclose(h, want, rtol=0, atol=1e-12 * np.abs(want).max())
+    for l in range(3):
+        np.testing.assert_array_equal(per[l]["x_in"], teach[l])
+    h_free, per_free = oracle.moe_stack_ref(h0, layers, k=k)
+    h_again, _ = oracle.moe_stack_ref(h0, layers, k=k, teacher_inputs=[p["x_in"] for p in per_free])
+    np.testing.assert_array_equal(h_again, h_free)
+    assert np.abs(h_free - h).max() > 1e-3
+
+
 # --------------------------------------------------------------------- backward
 
 
