@@ -460,14 +460,17 @@ def moe_forward_residual(x, w_router, w_gate, w_up, w_down, h, *, x_next=None, e
 
 
 def moe_stack_forward(h, layers, eps: float = 1e-5, keep_inputs: bool = False, keep_states: bool = False,
-                      workspace=None, stream=None, fused: bool = True):
+                      workspace=None, stream=None, fused: bool = True, keep_probs: bool = False,
+                      state_rows=None):
     """Residual stack h <- h + MoE_l(RMSNorm(h)) over `layers` (dicts of weight
     tensors), in place on the fp32 residual `h` [T,2048].  fused: each layer's
     combine also updates h and writes the next layer's input
     (olmoe_moe_forward_residual); otherwise RMSNorm, layer and residual add run
     as separate calls (the layer output then passes through bf16).  Returns h
     and, per layer, expert counts / aux / z / route ids, plus the bf16 layer
-    inputs (keep_inputs) and h after each layer (keep_states)."""
+    inputs (keep_inputs), h after each layer (keep_states; only the rows in
+    the index tensor state_rows when it is given, h itself is always whole) and
+    the route probabilities (keep_probs, as "route_probs" [L,T,8])."""
     import torch
     T = h.shape[0]
     dev = h.device
@@ -478,29 +481,31 @@ def moe_stack_forward(h, layers, eps: float = 1e-5, keep_inputs: bool = False, k
     aux = torch.empty(len(layers), dtype=torch.float32, device=dev)
     z = torch.empty(len(layers), dtype=torch.float32, device=dev)
     ids = torch.empty((len(layers), T, K), dtype=torch.int32, device=dev)
+    probs = torch.empty((len(layers), T, K), dtype=torch.float32, device=dev) if keep_probs else None
     inputs, states = [], []
     rmsnorm_bf16(h, eps, xbuf, stream)
     for l, w in enumerate(layers):
         if keep_inputs:
             inputs.append(xbuf.clone())
         last = l == len(layers) - 1
+        pl = probs[l] if keep_probs else None
         if fused:
             moe_forward_residual(xbuf, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], h,
-                                 x_next=None if last else xbuf, eps=eps, route_ids=ids[l],
+                                 x_next=None if last else xbuf, eps=eps, route_ids=ids[l], route_probs=pl,
                                  expert_counts=counts[l], aux_loss=aux[l:l + 1], z_loss=z[l:l + 1],
                                  workspace=workspace, stream=stream)
         else:
             moe_forward(xbuf, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], out=ybuf,
-                        route_ids=ids[l], route_probs=None, expert_counts=counts[l],
+                        route_ids=ids[l], route_probs=pl, expert_counts=counts[l],
                         aux_loss=aux[l:l + 1], z_loss=z[l:l + 1], workspace=workspace, stream=stream,
                         want_routing=False)
             residual_add(h, ybuf, stream)
             if not last:
                 rmsnorm_bf16(h, eps, xbuf, stream)
         if keep_states:
-            states.append(h.clone())
+            states.append(h.clone() if state_rows is None else h[state_rows].clone())
     return {"h": h, "expert_counts": counts, "aux_loss": aux, "z_loss": z, "route_ids": ids,
-            "inputs": inputs, "states": states}
+            "route_probs": probs, "inputs": inputs, "states": states}
 
 
 TIMING_STAGES = ("router", "dispatch", "gateup", "down", "combine")

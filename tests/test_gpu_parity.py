@@ -333,35 +333,51 @@ def test_largest_batch():
 
 
 def test_full_size_stack():
+    """The 16-layer stack at 8192 tokens through the fused path the bench times ("Mixture-of-experts
+    LLMs from scratch with OLMoE", section 3: h <- h + MoE(RMSNorm(h)), fp32 residual).  Per layer:
+    routing ids and probabilities of every token against the oracle run on the GPU's own input
+    x_l, counts and losses; on sampled rows, the fused residual update h_{l+1} - h_l against the
+    oracle layer on those rows (the GPU's ids forced), and x_{l+1} = bf16(RMSNorm(h_{l+1}))."""
     name = "stack-16x8192"
     _log("full size stack")
     t0 = time.time()
     d = inputs.device_workload(name, seed=0)
     T = d["h0"].shape[0]
-    r = binding.moe_stack_forward(d["h0"].clone(), d["layers"], keep_inputs=True)
-    torch.cuda.synchronize()
     rng = np.random.default_rng(2)
-    rows = rng.choice(T, size=16, replace=False)
+    rows = np.sort(rng.choice(T, size=24, replace=False))
+    rows_t = torch.from_numpy(rows).to("cuda")
+    h0_rows = d["h0"][rows_t].cpu().numpy().astype(np.float64)
+    r = binding.moe_stack_forward(d["h0"].clone(), d["layers"], keep_inputs=True, keep_states=True,
+                                  keep_probs=True, state_rows=rows_t)
+    torch.cuda.synchronize()
+    states = [h0_rows] + [st.cpu().numpy().astype(np.float64) for st in r["states"]]
+    np.testing.assert_array_equal(states[-1], r["h"][rows_t].cpu().numpy().astype(np.float64))
+    nl = len(d["layers"])
     for l, w in enumerate(d["layers"]):
         hw = {k: (w[k].cpu().numpy() if w[k].dtype == torch.float32 else parity.bf16_tensor_to_bits(w[k]))
               for k in ("w_router", "w_gate", "w_up", "w_down")}
         xb = parity.bf16_tensor_to_bits(r["inputs"][l])
         ids = r["route_ids"][l].cpu().numpy()
+        probs = r["route_probs"][l].cpu().numpy()
         ref = oracle_routing(xb, hw["w_router"])
-        ntie = parity.check_routing(ids, np.take_along_axis(ref["p_all"], ids, 1), ref, f"stack layer {l}")
+        ntie = parity.check_routing(ids, probs, ref, f"stack layer {l}")
         counts = np.bincount(ids.ravel(), minlength=64)
         np.testing.assert_array_equal(r["expert_counts"][l].cpu().numpy(), counts)
         aux, z = oracle.losses(ref["p_all"], counts, ref["lse"], 8)
         parity.check_losses(float(r["aux_loss"][l]), float(r["z_loss"][l]), aux, z, f"stack layer {l}")
-        # the layer's output on its own input, rerun alone (same kernels, same bits)
-        single = binding.moe_forward(r["inputs"][l], w["w_router"], w["w_gate"], w["w_up"], w["w_down"])
-        torch.cuda.synchronize()
-        np.testing.assert_array_equal(single["route_ids"].cpu().numpy(), ids)
-        out = parity.bf16_tensor_to_bits(single["out"])
+        # the fused epilogue's fp32 update of the residual on the sampled rows
         ref_o = oracle.moe_layer_ref(xb[rows], hw["w_router"], hw["w_gate"], hw["w_up"], hw["w_down"], 8,
                                      forced_ids=ids[rows])
-        rel, mx = parity.check_out(oracle.to_f64(out[rows]), ref_o["out"], f"stack layer {l}")
-        _log(f"stack layer {l}: ties={ntie} sampled relL2={rel:.2e} ({time.time() - t0:.1f}s)")
+        rel, mx = parity.check_out(states[l + 1] - states[l], ref_o["out"], f"stack layer {l} residual update")
+        if l == 0:   # the first input is RMSNorm of h0
+            want = oracle.rmsnorm_bf16(h0_rows, 1e-5)
+            assert (np.abs(oracle.to_f64(xb[rows]) - want) <= np.abs(want) * 2.0 ** -7 + 1e-30).all()
+        if l + 1 < nl:   # the next input, written by the same epilogue, is RMSNorm of this state
+            want = oracle.rmsnorm_bf16(states[l + 1], 1e-5)
+            got = oracle.to_f64(parity.bf16_tensor_to_bits(r["inputs"][l + 1])[rows])
+            assert (np.abs(got - want) <= np.abs(want) * 2.0 ** -7 + 1e-30).all(), f"layer {l + 1} input"
+            assert (got != want).mean() < 1e-2
+        _log(f"stack layer {l}: ties={ntie} update relL2={rel:.2e} maxabs/rms={mx:.2e} ({time.time() - t0:.1f}s)")
 
 
 def test_stage_timing_on_a_sample_of_calls(weights):
