@@ -120,7 +120,10 @@ OLMOE_API olmoe_status_t olmoe_moe_workspace_layout(int64_t T, size_t* perm_off,
  *
  * T == 0 is valid: expert_counts is zeroed and the losses are set to 0.
  * Errors: OLMOE_EINVAL for a NULL required pointer, T out of range,
- * a pointer not 16-byte aligned, or `out` overlapping x or a weight;
+ * a pointer not 16-byte aligned, `out` overlapping x, a weight or the
+ * workspace, or an optional output (route_ids T*8*4 bytes, route_probs
+ * T*8*4, expert_counts 256, aux_loss 4, z_loss 4) overlapping an input, the
+ * workspace, `out` or another optional output;
  * OLMOE_EWORKSPACE for a NULL or short workspace; OLMOE_ENODEVICE when the
  * current device is not gfx950; OLMOE_EHIP when a launch fails. */
 OLMOE_API olmoe_status_t olmoe_moe_forward(const void* x, const float* W_router, const void* W_gate,

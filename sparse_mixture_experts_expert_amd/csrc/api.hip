@@ -380,6 +380,26 @@ olmoe_status_t forward_impl(const void* x, const float* W_router, const void* W_
   if (overlaps(out, act, workspace, L.total) || overlaps(hres, act * 2, workspace, L.total) ||
       overlaps(x_next, act, workspace, L.total))
     return fail(OLMOE_EINVAL, "an output overlaps the workspace");
+  // the optional routing outputs: the kernels read ids and probs back while out / h are written,
+  // so none of them may share bytes with an input, the workspace, a main output or each other
+  {
+    const size_t pairs = static_cast<size_t>(T) * OLMOE_K * 4;
+    const void* ro[] = {route_ids, route_probs, expert_counts, aux_loss, z_loss};
+    const size_t ro_n[] = {pairs, pairs, OLMOE_E * 4, 4, 4};
+    const char* ro_name[] = {"route_ids", "route_probs", "expert_counts", "aux_loss", "z_loss"};
+    for (int i = 0; i < 5; ++i) {
+      if (!ro[i]) continue;
+      if (hits_inputs(ro[i], ro_n[i], false)) return fail(OLMOE_EINVAL, "%s overlaps an input", ro_name[i]);
+      if (overlaps(ro[i], ro_n[i], workspace, L.total))
+        return fail(OLMOE_EINVAL, "%s overlaps the workspace", ro_name[i]);
+      if (overlaps(ro[i], ro_n[i], out, act) || overlaps(ro[i], ro_n[i], hres, act * 2) ||
+          overlaps(ro[i], ro_n[i], x_next, act))
+        return fail(OLMOE_EINVAL, "%s overlaps out, h or x_next", ro_name[i]);
+      for (int q = i + 1; q < 5; ++q)
+        if (overlaps(ro[i], ro_n[i], ro[q], ro_n[q]))
+          return fail(OLMOE_EINVAL, "%s overlaps %s", ro_name[i], ro_name[q]);
+    }
+  }
   olmoe_status_t st = check_device();
   if (st != OLMOE_OK) return st;
 

@@ -54,11 +54,11 @@ def test_workspace_bytes_formula():
 
 
 def _fwd(L, x=1 << 20, wr=2 << 20, wg=3 << 20, wu=4 << 30, wd=5 << 30, T=4, out=6 << 34,
-         ws=8 << 36, wsb=None, ids=None):
+         ws=8 << 36, wsb=None, ids=None, probs=None, counts=None, aux=None, z=None):
     wsb = binding.workspace_bytes(T if T >= 0 else 0) if wsb is None else wsb
     vp = ctypes.c_void_p
-    st = L.olmoe_moe_forward(vp(x), vp(wr), vp(wg), vp(wu), vp(wd), T, vp(out), vp(ids), None, None,
-                             None, None, vp(ws), wsb, None)
+    st = L.olmoe_moe_forward(vp(x), vp(wr), vp(wg), vp(wu), vp(wd), T, vp(out), vp(ids), vp(probs), vp(counts),
+                             vp(aux), vp(z), vp(ws), wsb, None)
     return st, L.olmoe_last_error().decode()
 
 
@@ -83,6 +83,34 @@ def test_forward_rejects_bad_arguments_before_any_device_call(L):
     assert _fwd(L, ws=(8 << 36) + 16)[0] == binding.EINVAL
     # out overlapping the workspace
     assert _fwd(L, out=(8 << 36) + 256)[0] == binding.EINVAL
+
+
+def test_forward_routing_outputs_may_not_alias(L):
+    """route_ids, route_probs, expert_counts, aux_loss and z_loss are written by the routing
+    kernels and read back while out is written: each is checked against the inputs, the
+    workspace, out and the others (every case fails before any device call)."""
+    T = 64
+    R = 7 << 34   # a free region for the routing outputs
+    ok = dict(ids=R, probs=R + 8192, counts=R + 16384, aux=R + 20480, z=R + 20484)
+    bad = {
+        "route_ids over x": dict(ids=(1 << 20) + 64),
+        "route_probs over W_router": dict(probs=(2 << 20) + 1024),
+        "expert_counts over W_down": dict(counts=(5 << 30) + 4096),
+        "aux_loss over W_gate": dict(aux=(3 << 20) + 4),
+        "route_ids in the workspace": dict(ids=(8 << 36) + 4096),
+        "route_probs over out": dict(probs=(6 << 34) + 512),
+        "z_loss in the workspace": dict(z=(8 << 36) + 12),
+        "route_ids over route_probs": dict(ids=R + 8192 - 16),
+        "expert_counts over aux_loss": dict(counts=R + 20480 - 16),
+        "aux_loss is z_loss": dict(aux=R + 20484),
+    }
+    for label, change in bad.items():
+        st, msg = _fwd(L, T=T, **dict(ok, **change))
+        assert st == binding.EINVAL, f"{label}: status {st} ({msg})"
+        assert "overlaps" in msg, f"{label}: {msg}"
+    # the non-overlapping placement passes every check (and then finds no GPU here)
+    st, msg = _fwd(L, T=T, **ok)
+    assert st != binding.EINVAL, msg
 
 
 def test_router_variant_arguments_are_checked_first(L):
