@@ -47,7 +47,7 @@ extern "C" {
 #define OLMOE_API
 #endif
 
-#define OLMOE_ABI_VERSION 8
+#define OLMOE_ABI_VERSION 9
 
 #define OLMOE_D 2048 /* hidden size */
 #define OLMOE_F 1024 /* expert width (SwiGLU intermediate size) */
@@ -340,6 +340,25 @@ OLMOE_API olmoe_status_t olmoe_moe_backward(const void* x, const float* W_router
                                   float g_aux, float g_z, float* dx, float* dW_router, float* dW_gate,
                                   float* dW_up, float* dW_down, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the layer
+ * exactly as olmoe_moe_forward (same kernels, same results bit for bit), with
+ * the workspace in a device array of OLMOE_NOALLOC_SCRATCH_BYTES that the
+ * library owns, one per GPU, held until the process ends.  Enough for up to
+ * OLMOE_NOALLOC_MAX_TOKENS tokens; a larger T gives OLMOE_EINVAL.  The call
+ * allocates and frees nothing (its first call on a GPU looks the array's device
+ * address up once).  Every call on a GPU uses that GPU's one array, so calls
+ * that overlap on one GPU (two streams, two threads) race and give undefined
+ * results: serialise them.  Nothing in the array needs to start at zero.
+ * Arguments and errors otherwise as olmoe_moe_forward. */
+#define OLMOE_NOALLOC_MAX_TOKENS 1024
+#define OLMOE_NOALLOC_SCRATCH_BYTES ((size_t)60 << 20)
+OLMOE_API olmoe_status_t olmoe_moe_forward_noalloc(const void* x, const float* W_router, const void* W_gate,
+                                         const void* W_up, const void* W_down, int64_t T, void* out,
+                                         int32_t* route_ids, float* route_probs,
+                                         int32_t* expert_counts, float* aux_loss, float* z_loss,
+                                         void* stream);
 
 /* Per-stage timing of olmoe_moe_forward with HIP events recorded on the
  * caller's stream at the boundaries of its stages: 0 router (logits,

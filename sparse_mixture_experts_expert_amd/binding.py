@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
     L.olmoe_moe_forward_ex.restype = i32
     L.olmoe_moe_forward_ex.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp,
                                        ctypes.c_uint32, ctypes.c_uint64, vp, sz, vp]
+    L.olmoe_moe_forward_noalloc.restype = i32
+    L.olmoe_moe_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp]
     L.olmoe_moe_forward_residual.restype = i32
     L.olmoe_moe_forward_residual.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, ctypes.c_float, vp, vp, vp, vp,
                                              vp, ctypes.c_uint32, ctypes.c_uint64, vp, sz, vp]
@@ -196,6 +198,30 @@ def moe_forward(x, w_router, w_gate, w_up, w_down, *, out=None, route_ids=None, 
     return {"out": out, "route_ids": route_ids, "route_probs": route_probs,
             "expert_counts": expert_counts, "aux_loss": aux_loss, "z_loss": z_loss,
             "workspace": workspace}
+
+
+NOALLOC_MAX_TOKENS = 1024
+NOALLOC_SCRATCH_BYTES = 60 << 20
+
+
+def moe_forward_noalloc(x, w_router, w_gate, w_up, w_down, *, out=None, route_ids=None, route_probs=None,
+                        expert_counts=None, aux_loss=None, z_loss=None, stream=None):
+    """The layer with the library-owned scratch instead of a workspace
+    (olmoe_moe_forward_noalloc, at most NOALLOC_MAX_TOKENS tokens).  Missing
+    outputs are allocated here by torch, not by the library; pass them all to
+    make the call allocation-free.  Calls that overlap on one GPU race."""
+    import torch
+    T = x.shape[0]
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, D))
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    _check(lib().olmoe_moe_forward_noalloc(
+        _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), int(T), _ptr(out),
+        _ptr(route_ids), _ptr(route_probs), _ptr(expert_counts), _ptr(aux_loss), _ptr(z_loss),
+        _stream(stream)))
+    return {"out": out, "route_ids": route_ids, "route_probs": route_probs, "expert_counts": expert_counts,
+            "aux_loss": aux_loss, "z_loss": z_loss}
 
 
 def backward_workspace_bytes(T: int) -> int:

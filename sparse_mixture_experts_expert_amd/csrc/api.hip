@@ -272,6 +272,33 @@ olmoe_status_t forward_impl(const void* x, const float* W_router, const void* W_
                             float* z_loss, uint32_t route_flags, uint64_t keep_mask, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+// ---------------------------------------------------------------- library-owned scratch
+
+// The workspace of olmoe_moe_forward_noalloc: one array per GPU, held until the process ends.  In
+// host code the name below stands for the array but is not its device address; that address
+// comes from hipGetSymbolAddress with the GPU current, once per GPU, and only it is passed on.
+__device__ __align__(256) unsigned char scratch[OLMOE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;   // device address of `scratch` per device (null: not looked up)
+
+olmoe_status_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) return fail(OLMOE_ENODEVICE, "no HIP device: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(OLMOE_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return OLMOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -314,6 +341,26 @@ olmoe_status_t olmoe_moe_forward_ex(const void* x, const float* W_router, const 
   return forward_impl(x, W_router, W_gate, W_up, W_down, T, out, nullptr, nullptr, 0.f, route_ids,
                       route_probs, expert_counts, aux_loss, z_loss, route_flags, keep_mask, workspace,
                       workspace_bytes, stream);
+}
+
+olmoe_status_t olmoe_moe_forward_noalloc(const void* x, const float* W_router, const void* W_gate,
+                                         const void* W_up, const void* W_down, int64_t T, void* out,
+                                         int32_t* route_ids, float* route_probs, int32_t* expert_counts,
+                                         float* aux_loss, float* z_loss, void* stream) {
+  if (T < 0 || T > OLMOE_NOALLOC_MAX_TOKENS)
+    return fail(OLMOE_EINVAL, "T=%lld: the library-owned scratch holds at most %d tokens", (long long)T,
+                OLMOE_NOALLOC_MAX_TOKENS);
+  const size_t need = make_layout(T).total;
+  if (need > OLMOE_NOALLOC_SCRATCH_BYTES)   // a build inconsistency, not a caller error
+    return fail(OLMOE_EWORKSPACE, "scratch of %zu bytes below the %zu needed for T=%lld",
+                (size_t)OLMOE_NOALLOC_SCRATCH_BYTES, need, (long long)T);
+  olmoe_status_t st = check_device();
+  if (st != OLMOE_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != OLMOE_OK) return st;
+  return forward_impl(x, W_router, W_gate, W_up, W_down, T, out, nullptr, nullptr, 0.f, route_ids, route_probs,
+                      expert_counts, aux_loss, z_loss, 0u, OLMOE_KEEP_ALL, ws, OLMOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 olmoe_status_t olmoe_moe_forward_residual(const void* x, const float* W_router, const void* W_gate,

@@ -113,6 +113,19 @@ def test_forward_routing_outputs_may_not_alias(L):
     assert st != binding.EINVAL, msg
 
 
+def test_noalloc_forward_limits(L):
+    """The library-owned scratch covers the forward's workspace up to its token limit, and a larger
+    T is rejected before any device call."""
+    assert binding.workspace_bytes(binding.NOALLOC_MAX_TOKENS) <= binding.NOALLOC_SCRATCH_BYTES
+    vp = ctypes.c_void_p
+    st = L.olmoe_moe_forward_noalloc(vp(1 << 20), vp(2 << 20), vp(3 << 20), vp(4 << 30), vp(5 << 30),
+                                     binding.NOALLOC_MAX_TOKENS + 1, vp(6 << 34), None, None, None, None, None, None)
+    assert st == binding.EINVAL and "scratch" in L.olmoe_last_error().decode()
+    st = L.olmoe_moe_forward_noalloc(vp(1 << 20), vp(2 << 20), vp(3 << 20), vp(4 << 30), vp(5 << 30), -1,
+                                     vp(6 << 34), None, None, None, None, None, None)
+    assert st == binding.EINVAL
+
+
 def test_router_variant_arguments_are_checked_first(L):
     # every call here fails validation, so nothing reaches a device (fake pointers)
     vp = ctypes.c_void_p
