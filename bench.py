@@ -604,7 +604,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16+fp16",
+        "dtype_detail": "bf16 inputs, weights and output; gate/up GEMM on bf16 MFMA, down GEMM on f16 MFMA "
+                        "(fp16 SwiGLU activations, W_down converted to fp16); fp32 accumulation, router "
+                        "and softmax; fp16 expert outputs",
         "data": f"synthetic (seeded; N(0,1) tokens, N(0,0.02) weights, random init; "
                 f"{N_WEIGHT_SETS if main_res['layers'] == 1 else main_res['layers']} distinct weight sets cycled)",
         "config": {"workload": args.workload, "tokens": main_res["tokens"], "layers": main_res["layers"],

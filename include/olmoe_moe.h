@@ -69,6 +69,11 @@ OLMOE_API int olmoe_abi_version(void);
 /* Text of the last non-OK status on this thread ("" if none). */
 OLMOE_API const char* olmoe_last_error(void);
 
+/* Byte offset, in every workspace and `saved` buffer, of the int32 count of
+ * fp16 intermediates stored clipped by the last call that used it (see
+ * olmoe_moe_forward). */
+#define OLMOE_WORKSPACE_CLIP_COUNT_OFFSET 0
+
 /* Bytes of device workspace olmoe_moe_forward needs for T tokens (pure host
  * function, no device access).  Returns 0 for T < 0 or T > OLMOE_MAX_TOKENS.
  * Grows as about 8*T*(1024+2048)*2 bytes (the SwiGLU activations and the
@@ -112,11 +117,19 @@ OLMOE_API olmoe_status_t olmoe_moe_workspace_layout(int64_t T, size_t* perm_off,
  *
  * Arithmetic: router logits, softmax and losses in fp32 (the router is
  * evaluated exactly as an fp32 dot product of the bf16 inputs and fp32
- * weights); expert GEMMs on MFMA with fp32 accumulation (gate/up in bf16;
- * down in fp16, W_down converted exactly); the SwiGLU activation is formed in
- * fp32 and stored as fp16, expert outputs are stored as fp16 (both rounded to
- * nearest even, saturated at +-65504), and the weighted sum is accumulated in
- * fp32 over the 8 slots in route order and rounded once to bf16.
+ * weights); expert GEMMs on MFMA with fp32 accumulation (gate/up on bf16 MFMA;
+ * down on f16 MFMA, with W_down converted to fp16 after an exact scaling by
+ * 16 that the fp32 result undoes exactly: exact for 2^-18 <= |w| < 4096,
+ * rounded toward zero with an absolute error below 2^-28 under that, saturated
+ * above); the SwiGLU activation is formed in fp32 and stored as fp16, expert
+ * outputs are stored as fp16 (both rounded to nearest even), and the weighted
+ * sum is accumulated in fp32 over the 8 slots in route order and rounded once
+ * to bf16.  An activation or expert output outside fp16's range (|v| > 65504)
+ * or NaN is stored clipped to +-65504 and counted: the int32 at byte
+ * OLMOE_WORKSPACE_CLIP_COUNT_OFFSET of the workspace holds, once the call has
+ * completed on its stream, the number of such values (0 in normal use; the
+ * backward, expert-choice and training entry points keep the same count in
+ * their workspace or `saved` buffer).
  *
  * T == 0 is valid: expert_counts is zeroed and the losses are set to 0.
  * Errors: OLMOE_EINVAL for a NULL required pointer, T out of range,

@@ -434,6 +434,17 @@ def moe_backward_expert_choice(x, w_router, w_gate, w_up, w_down, dout, *, g_aux
             "workspace": workspace}
 
 
+CLIP_COUNT_OFFSET = 0
+
+
+def clip_count(workspace) -> int:
+    """Number of fp16 intermediates (SwiGLU activations and expert outputs) the last call that used
+    this workspace (or `saved` buffer) stored clipped to +-65504 because they were out of range or
+    NaN; 0 in normal use.  Synchronises with the device."""
+    import torch
+    return int(workspace[CLIP_COUNT_OFFSET:CLIP_COUNT_OFFSET + 4].view(torch.int32).item())
+
+
 def dispatch_tables(workspace, T: int):
     """Views of perm [8T], inv [T,8], offsets [65] inside a workspace after a call."""
     import torch

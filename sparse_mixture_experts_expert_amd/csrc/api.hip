@@ -37,8 +37,8 @@ olmoe_status_t ok() {
 }
 
 struct Layout {
-  size_t tiles_gu, tiles_dn, planes, partial, ids, probs, lrank, blk_counts, blk_psum, blk_lse2, blk_base, offsets,
-      tp_gu, tp_dn, perm, inv, h, y, total;
+  size_t clip, tiles_gu, tiles_dn, planes, partial, ids, probs, lrank, blk_counts, blk_psum, blk_lse2, blk_base,
+      offsets, tp_gu, tp_dn, perm, inv, h, y, total;
 };
 
 Layout make_layout(int64_t T) {
@@ -51,6 +51,9 @@ Layout make_layout(int64_t T) {
   };
   const size_t rows = 8 * static_cast<size_t>(T);
   const size_t nblk = static_cast<size_t>((T + 15) / 16);
+  // first, at offset 0 of every workspace (the backward and expert-choice layouts start with this
+  // one): the count of fp16 intermediates stored clipped, zeroed by each call's dispatch kernel
+  L.clip = take(4);
   L.offsets = take(65 * 4);
   L.tp_gu = take(65 * 4);
   L.tp_dn = take(65 * 4);
@@ -474,7 +477,7 @@ olmoe_status_t forward_impl(const void* x, const float* W_router, const void* W_
               reinterpret_cast<int32_t*>(ws + L.offsets),
               reinterpret_cast<int32_t*>(ws + L.tp_gu), reinterpret_cast<int2*>(ws + L.tiles_gu), plan.bm_gu,
               reinterpret_cast<int32_t*>(ws + L.tp_dn), reinterpret_cast<int2*>(ws + L.tiles_dn), plan.bm_dn,
-              expert_counts, aux_loss, z_loss};
+              expert_counts, aux_loss, z_loss, reinterpret_cast<int32_t*>(ws + L.clip)};
   PermuteArgs pa{Ti, ids, reinterpret_cast<const uint8_t*>(ws + L.lrank),
                  reinterpret_cast<const int32_t*>(ws + L.blk_base), reinterpret_cast<int32_t*>(ws + L.perm),
                  reinterpret_cast<int32_t*>(ws + L.inv)};
@@ -506,7 +509,9 @@ olmoe_status_t forward_impl(const void* x, const float* W_router, const void* W_
               reinterpret_cast<const int2*>(ws + L.tiles_gu),
               reinterpret_cast<const int2*>(ws + L.tiles_dn),
               reinterpret_cast<uint16_t*>(ws + L.h),
-              reinterpret_cast<uint16_t*>(ws + L.y)};
+              reinterpret_cast<uint16_t*>(ws + L.y),
+              nullptr,
+              reinterpret_cast<int32_t*>(ws + L.clip)};
   he = launch_gateup(ga, plan, s);
   if (he != hipSuccess) return fail(OLMOE_EHIP, "gate/up launch: %s", hipGetErrorString(he));
   rec.mark();
@@ -580,7 +585,7 @@ olmoe_status_t bwd_forward_state(const void* x, const float* W_router, const voi
               reinterpret_cast<int32_t*>(ws + L.offsets),
               reinterpret_cast<int32_t*>(ws + L.tp_gu), reinterpret_cast<int2*>(ws + L.tiles_gu), plan.bm_gu,
               reinterpret_cast<int32_t*>(ws + L.tp_dn), reinterpret_cast<int2*>(ws + L.tiles_dn), plan.bm_dn,
-              expert_counts, aux_loss, z_loss};
+              expert_counts, aux_loss, z_loss, reinterpret_cast<int32_t*>(ws + L.clip)};
   PermuteArgs pa{Ti, ids, reinterpret_cast<const uint8_t*>(ws + L.lrank),
                  reinterpret_cast<const int32_t*>(ws + L.blk_base), reinterpret_cast<int32_t*>(ws + L.perm),
                  reinterpret_cast<int32_t*>(ws + L.inv), probs, reinterpret_cast<float*>(ws + B.row_w)};
@@ -610,7 +615,8 @@ olmoe_status_t bwd_forward_state(const void* x, const float* W_router, const voi
                 reinterpret_cast<const int2*>(ws + L.tiles_dn),
                 reinterpret_cast<uint16_t*>(ws + L.h),
                 reinterpret_cast<uint16_t*>(ws + L.y),
-                reinterpret_cast<float*>(ws + B.gu)};
+                reinterpret_cast<float*>(ws + B.gu),
+                reinterpret_cast<int32_t*>(ws + L.clip)};
     he = launch_gateup(ga, plan, s);
     if (he == hipSuccess) he = launch_down(ga, plan, s);
     if (he != hipSuccess) return fail(OLMOE_EHIP, "forward GEMM launch: %s", hipGetErrorString(he));
@@ -739,6 +745,7 @@ olmoe_status_t ec_bwd_forward_state(const void* x, const float* W_router, const 
   ea.choice_probs = choice_probs;
   ea.aux_loss = aux_loss;
   ea.z_loss = z_loss;
+  ea.clip = reinterpret_cast<int32_t*>(ws + L.f.clip);
   hipError_t he = hipSuccess;
   if (Ti > 0) {
     RouterArgs ra{static_cast<const uint16_t*>(x), W_router, Ti, reinterpret_cast<float2*>(ws + L.f.partial),
@@ -763,7 +770,8 @@ olmoe_status_t ec_bwd_forward_state(const void* x, const float* W_router, const 
                 reinterpret_cast<const int2*>(ws + L.f.tiles_dn),
                 reinterpret_cast<uint16_t*>(ws + L.f.h),
                 reinterpret_cast<uint16_t*>(ws + L.f.y),
-                reinterpret_cast<float*>(ws + B.gu)};
+                reinterpret_cast<float*>(ws + B.gu),
+                reinterpret_cast<int32_t*>(ws + L.f.clip)};
     he = launch_gateup(ga, plan, s);
     if (he == hipSuccess) he = launch_down(ga, plan, s);
     if (he != hipSuccess) return fail(OLMOE_EHIP, "forward GEMM launch: %s", hipGetErrorString(he));
@@ -1014,6 +1022,7 @@ olmoe_status_t olmoe_moe_forward_expert_choice(const void* x, const float* W_rou
   ea.token_counts = token_counts;
   ea.aux_loss = aux_loss;
   ea.z_loss = z_loss;
+  ea.clip = reinterpret_cast<int32_t*>(ws + L.f.clip);
   hipError_t he = hipSuccess;
   if (Ti > 0) {
     RouterArgs ra{static_cast<const uint16_t*>(x), W_router, Ti, reinterpret_cast<float2*>(ws + L.f.partial),
@@ -1042,7 +1051,9 @@ olmoe_status_t olmoe_moe_forward_expert_choice(const void* x, const float* W_rou
               reinterpret_cast<const int2*>(ws + L.f.tiles_gu),
               reinterpret_cast<const int2*>(ws + L.f.tiles_dn),
               reinterpret_cast<uint16_t*>(ws + L.f.h),
-              reinterpret_cast<uint16_t*>(ws + L.f.y)};
+              reinterpret_cast<uint16_t*>(ws + L.f.y),
+              nullptr,
+              reinterpret_cast<int32_t*>(ws + L.f.clip)};
   he = launch_gateup(ga, plan, s);
   if (he != hipSuccess) return fail(OLMOE_EHIP, "gate/up launch: %s", hipGetErrorString(he));
   rec.mark();

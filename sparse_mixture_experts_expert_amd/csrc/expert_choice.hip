@@ -152,6 +152,7 @@ __global__ __launch_bounds__(NT) void ec_choose_kernel(EcArgs a) {
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int T = a.T, C = a.C;
+  if (e == 0 && tid == 0 && a.clip) *a.clip = 0;   // counted by the GEMMs after this launch
   if (e == E) {   // losses: wave s sums part s of the blocks, lane x for expert x
     const int nblk = (T + EC_SM_TOK - 1) / EC_SM_TOK;
     const int per = (nblk + NW - 1) / NW;

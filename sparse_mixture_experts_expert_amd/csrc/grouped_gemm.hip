@@ -30,12 +30,16 @@
 // after waiting only for the loads of the stage about to be used: S-1 stages
 // stay in flight while the MFMAs run.
 //
-// The intermediates H and Y are stored as fp16 (round to nearest even,
-// saturated at +-65504): same bytes as bf16 but 3 more significand bits, which
-// keeps their rounding well below the output's own bf16 rounding.  The down
-// GEMM therefore runs on f16 MFMA; W_down's bf16 values are converted to fp16
-// after the LDS read, exactly for every weight in fp16's normal range (weights
-// below 2^-14 in magnitude keep an absolute error under 2^-24).
+// The intermediates H and Y are stored as fp16 (round to nearest even): same
+// bytes as bf16 but 3 more significand bits, which keeps their rounding well
+// below the output's own bf16 rounding.  A value outside fp16's range (or NaN)
+// is stored clipped to +-65504 and counted in the workspace's clip counter, so
+// the caller learns of it.  The down GEMM therefore runs on f16 MFMA; W_down's
+// bf16 values are converted to fp16 after the LDS read, scaled by 16 on the way
+// (exact) and the products scaled back by 1/16 in fp32 (exact): every weight
+// with 2^-18 <= |w| < 4096 converts exactly, smaller ones round toward zero
+// with an absolute error under 2^-28, larger ones saturate.
+constexpr float W_DOWN_SCALE = 16.0f;
 #include <type_traits>
 
 #include "common.hpp"
@@ -139,7 +143,7 @@ template <class C>
 __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W0, const bf16_t* __restrict__ W1,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ tile_count, const int2* __restrict__ tiles,
-    int n_blocks, bf16_t* __restrict__ Cout, float* __restrict__ gu) {
+    int n_blocks, bf16_t* __restrict__ Cout, float* __restrict__ gu, int32_t* __restrict__ clip) {
   constexpr int BK = C::BK;
   __shared__ __align__(16) bf16_t smem[C::STAGES][C::ROWS * BK];
 
@@ -247,10 +251,11 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
       for (int j = 0; j < C::FN; ++j) {
         const int r = g * C::BN + wn * (C::BN / C::WN) + j * 32 + (lane & 31);
         u32x4 v = *reinterpret_cast<const u32x4*>(&Bs[swz<BK>(r, kc)]);
-        if constexpr (!C::GATEUP) {   // bf16 -> fp16 (exact in fp16's normal range)
+        if constexpr (!C::GATEUP) {   // bf16 -> fp16 of 16 w (exact for 2^-18 <= |w| < 4096)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v[q] << 16), __uint_as_float(v[q] & 0xFFFF0000u));
+            const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v[q] << 16) * W_DOWN_SCALE,
+                                                      __uint_as_float(v[q] & 0xFFFF0000u) * W_DOWN_SCALE);
             v[q] = __builtin_bit_cast(uint32_t, h);
           }
         }
@@ -300,6 +305,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
   else kloop(std::integral_constant<int, 0>{});
 
   // C layout of a 32x32 fragment: lane holds column lane%32, rows (v/4)*8 + (lane/32)*4 + v%4
+  int nclip = 0;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -311,7 +317,8 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
         if (r < valid) {
           float o;
           if constexpr (C::GATEUP) o = silu(acc[0][i][j][v]) * acc[1][i][j][v];
-          else o = acc[0][i][j][v];
+          else o = acc[0][i][j][v] * (1.0f / W_DOWN_SCALE);
+          nclip += !(fabsf(o) <= F16_MAX);   // out of range or NaN: stored clipped, counted
           Cout[(size_t)(row0 + r) * C::ND + c] = f32_to_f16_sat(o);
           if constexpr (C::SAVE_GU) {   // [rows, 2F]: G in columns 0..F-1, U in F..2F-1
             gu[(size_t)(row0 + r) * (2 * F) + c] = acc[0][i][j][v];
@@ -319,6 +326,8 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
           }
         }
       }
+  nclip = wave_sum_int(nclip);
+  if (nclip && lane == 0 && clip) atomicAdd(clip, nclip);   // an integer count: order does not matter
 }
 
 // tile sets by batch size (rows per expert ~ T/8), chosen by measurement on MI355X.  Up to a
@@ -374,7 +383,7 @@ hipError_t launch_cfg(const bf16_t* A, const bf16_t* W0, const bf16_t* W1, const
   const int n_blocks = C::ND / C::BN;
   const int grid = (max_tiles * n_blocks + 7) / 8 * 8;
   hipLaunchKernelGGL(grouped_gemm_kernel<C>, dim3(grid), dim3(C::NT), 0, stream, A, W0, W1, a.perm,
-                     tile_prefix + E, tiles, n_blocks, out, gu);
+                     tile_prefix + E, tiles, n_blocks, out, gu, a.clip);
   return hipGetLastError();
 }
 

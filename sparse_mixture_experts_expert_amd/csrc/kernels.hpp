@@ -55,6 +55,7 @@ struct ScanArgs {
   int32_t* expert_counts;   // [64] or null
   float* aux_loss;          // [1] or null
   float* z_loss;            // [1] or null
+  int32_t* clip = nullptr;  // [1] count of clipped fp16 intermediates: zeroed here, before the GEMMs
 };
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 
@@ -96,6 +97,7 @@ struct GemmArgs {
   uint16_t* h;              // fp16 [8T,1024] SwiGLU activations, expert-contiguous rows
   uint16_t* y;              // fp16 [8T,2048] expert outputs, expert-contiguous rows
   float* gu = nullptr;      // gate/up: also store fp32 G and U [8T, 2048] (backward recompute), or null
+  int32_t* clip = nullptr;  // [1] += values of H and Y outside fp16's range (or NaN), stored clipped
 };
 hipError_t launch_gateup(const GemmArgs& a, const GemmPlan& p, hipStream_t stream);
 hipError_t launch_down(const GemmArgs& a, const GemmPlan& p, hipStream_t stream);
@@ -142,6 +144,7 @@ struct EcArgs {
   float* aux_loss;            // [1] or null
   float* z_loss;              // [1] or null
   float* p_all = nullptr;     // fp32 [T,64] probabilities by token (backward pass), or null
+  int32_t* clip = nullptr;    // [1] count of clipped fp16 intermediates: zeroed by the selection
 };
 hipError_t launch_ec_softmax(const EcArgs& a, hipStream_t stream);   // p (transposed), lse, inv_ec = -1
 // top-C per expert and the tile lists (one workgroup per expert), aux and z (one more)

@@ -234,6 +234,7 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 // fixed order, so the results are reproducible bit for bit.
 __device__ __forceinline__ void scan_block(const ScanArgs& a, ScanLds& L) {
   const int tid = threadIdx.x;
+  if (tid == 0 && a.clip) *a.clip = 0;   // the GEMMs after this launch count their clipped values
   const int e = tid & 63;
   const int s = tid >> 6;
   const int nblk = (a.T + ROUTE_BLOCK - 1) / ROUTE_BLOCK;

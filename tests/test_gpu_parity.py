@@ -56,6 +56,7 @@ def run_layer(x, w, **variant):
     h = host_of(r)
     h.update({k: v.cpu().numpy() for k, v in tables.items()})
     h["x"] = parity.bf16_tensor_to_bits(x)
+    h["clip"] = binding.clip_count(r["workspace"])
     return h
 
 
@@ -70,6 +71,7 @@ def full_check(g, hw, label, renormalize=False, keep=None):
     parity.check_dispatch(g["route_ids"], g["expert_counts"], g["perm"], g["inv"], g["offsets"], label=label)
     rel, mx = parity.check_out(oracle.to_f64(g["out"]), ref["out"], label)
     parity.check_losses(float(g["aux_loss"][0]), float(g["z_loss"][0]), ref["aux"], ref["z"], label)
+    assert g["clip"] == 0, f"{label}: {g['clip']} intermediates clipped"
     _log(f"{label}: ties={ntie} relL2={rel:.2e} maxabs/rms={mx:.2e} aux={float(g['aux_loss'][0]):.6f}")
     return ref
 
@@ -156,6 +158,51 @@ def test_zero_router_ties_go_to_lower_ids(weights):
     assert g["z_loss"][0] == pytest.approx(0.001 * np.log(64) ** 2, rel=1e-5)
     ref = oracle.moe_layer_ref(g["x"], hw["w_router"] * 0, hw["w_gate"], hw["w_up"], hw["w_down"], 8)
     parity.check_out(oracle.to_f64(g["out"]), ref["out"], "zero router")
+
+
+@pytest.mark.filterwarnings("ignore:overflow encountered in exp")
+def test_activations_beyond_fp16_are_counted(weights):
+    """Tokens scaled x256 drive their SwiGLU activations and expert outputs past fp16's range: the
+    library stores them clipped and reports how many in the workspace's clip count instead of
+    clipping silently; every other token still matches the oracle, and the next call with normal
+    inputs on the same workspace reports 0."""
+    w, hw = weights
+    T = 64
+    x = inputs.device_x(T, seed=8, workload="parity")
+    big = [5, 17, 40]
+    x[big] = (x[big].float() * 256.0).to(torch.bfloat16)   # exact in bf16
+    ws = binding.make_workspace(T)
+    r = binding.moe_forward(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], workspace=ws)
+    torch.cuda.synchronize()
+    n = binding.clip_count(ws)
+    assert n > 0
+    g = host_of(r)
+    xb = parity.bf16_tensor_to_bits(x)
+    rows = np.setdiff1d(np.arange(T), big)
+    ref = oracle.moe_layer_ref(xb[rows], hw["w_router"], hw["w_gate"], hw["w_up"], hw["w_down"], 8,
+                               forced_ids=g["route_ids"][rows])
+    rel, mx = parity.check_out(oracle.to_f64(g["out"][rows]), ref["out"], "unscaled tokens beside clipped ones")
+    # the scaled tokens' exact outputs lie far outside fp16
+    ref_big = oracle.moe_layer_ref(xb[big], hw["w_router"], hw["w_gate"], hw["w_up"], hw["w_down"], 8,
+                                   forced_ids=g["route_ids"][big], keep_y=True)
+    assert np.abs(ref_big["y"]).max() > 65504
+    x2 = inputs.device_x(T, seed=9, workload="parity")
+    binding.moe_forward(x2, w["w_router"], w["w_gate"], w["w_up"], w["w_down"], workspace=ws)
+    torch.cuda.synchronize()
+    assert binding.clip_count(ws) == 0
+    _log(f"clipped intermediates counted: {n}; other tokens relL2={rel:.2e} maxabs/rms={mx:.2e}")
+
+
+def test_small_down_weights_convert_exactly(weights):
+    """W_down scaled by 2^-12 puts most weights below fp16's normal range (2^-14): the down GEMM's
+    scaled conversion keeps them exact down to 2^-18, so the layer still matches the oracle."""
+    w, hw = weights
+    T = 100
+    wd = (w["w_down"].float() * 2.0 ** -12).to(torch.bfloat16)   # exact in bf16
+    assert (wd.float().abs() < 2.0 ** -14).float().mean().item() > 0.9
+    x = inputs.device_x(T, seed=10, workload="parity")
+    g = run_layer(x, dict(w, w_down=wd))
+    full_check(g, dict(hw, w_down=parity.bf16_tensor_to_bits(wd)), "W_down x 2^-12")
 
 
 def test_zero_tokens(weights):
@@ -303,6 +350,7 @@ def full_size_layer(name, tokens=None):
     ref = oracle_routing(g["x"], hw["w_router"])
     ntie = parity.check_routing(g["route_ids"], g["route_probs"], ref, name)
     parity.check_dispatch(g["route_ids"], g["expert_counts"], g["perm"], g["inv"], g["offsets"], label=name)
+    assert g["clip"] == 0, f"{name}: {g['clip']} intermediates clipped"
     counts = np.bincount(g["route_ids"].ravel(), minlength=64)
     aux, z = oracle.losses(ref["p_all"], counts, ref["lse"], 8)
     parity.check_losses(float(g["aux_loss"][0]), float(g["z_loss"][0]), aux, z, name)
