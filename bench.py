@@ -511,6 +511,83 @@ def traffic_summary(args):
     print("\n".join(lines))
 
 
+MFMA_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_BUSY_CU_CYCLES")
+N_XCD, N_SIMD = 8, 1024          # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+PEAK_CLOCK_GHZ = 2.4             # the clock the published MFMA peak assumes
+FLOP_PER_MOP = 512               # SQ_INSTS_VALU_MFMA_MOPS_* count matrix work in units of 512 FLOP
+
+
+def _durations_us(d, select):
+    import csv
+    import glob
+    out = {}
+    for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if select(r["Kernel_Name"]):
+                out[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    return out
+
+
+def mfma_summary(args):
+    """Turn one rocprofv3 --kernel-trace --pmc run over MFMA_COUNTERS into the matrix-core
+    utilisation of the grouped GEMMs: per dispatch, the average shader clock (GRBM_GUI_ACTIVE
+    summed over the XCDs / duration), the fraction of SIMD cycles the MFMA unit was busy, the
+    matrix work counted by the hardware against the algorithmic FLOP, and the duration-based
+    fraction of the 2.5 PFLOP/s bf16 peak (medians over dispatches).  At full MFMA rate a busy
+    cycle does peak/(SIMDs x 2.4 GHz) of work, so busy fraction x clock / 2.4 GHz should match the
+    duration-based fraction."""
+    from sparse_mixture_experts_expert_amd import inputs
+    import statistics
+    wl = args.workload
+    T = inputs.WORKLOADS[wl].tokens
+    rows = _counter_rows(args.mfma_dir)
+    lines = [f"# Matrix-core utilisation of the grouped GEMMs, {wl}", "",
+             "rocprofv3 --kernel-trace --pmc " + " ".join(MFMA_COUNTERS) + "; medians over dispatches.",
+             f"clock = GRBM_GUI_ACTIVE / {N_XCD} XCDs / duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /"
+             f" ({N_SIMD} SIMDs x clock cycles); counted FLOP = MOPS x {FLOP_PER_MOP};",
+             "roofline = algorithmic FLOP / duration / 2.5 PFLOP/s; busy x clock/2.4 GHz is the same",
+             "fraction seen from the counters.", "",
+             "| stage | dispatches | duration us | clock GHz | MFMA busy | busy x clock/2.4 | roofline (duration) | "
+             "counted / algorithmic FLOP | source hash |", "|---|---|---|---|---|---|---|---|---|"]
+    for stage in ("gateup", "down"):
+        sel = lambda n, st=stage: _stage_of(n) == st
+        dur = _durations_us(args.mfma_dir, sel)
+        per = {}
+        for r in rows:
+            if sel(r["Kernel_Name"]):
+                per.setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+                per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        ids = [i for i in dur if all(i in per.get(c, {}) for c in MFMA_COUNTERS[:2])]
+        if not ids:
+            continue
+        clk, busy, frac, mops = [], [], [], []
+        flop_alg, _ = stage_model(stage, T, args.touched)
+        for i in ids:
+            cycles = per["GRBM_GUI_ACTIVE"][i] / N_XCD
+            clk.append(cycles / dur[i] / 1e3)
+            busy.append(per["SQ_VALU_MFMA_BUSY_CYCLES"][i] / (N_SIMD * cycles))
+            frac.append(flop_alg / (dur[i] * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+            mops.append(per.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", {}).get(i, 0.0) +
+                        per.get("SQ_INSTS_VALU_MFMA_MOPS_F16", {}).get(i, 0.0))
+        med = statistics.median
+        rec = {"workload": wl, "stage": stage, "dispatches": len(ids), "duration_us": round(med(dur[i] for i in ids), 2),
+               "clock_ghz": round(med(clk), 3), "mfma_busy": round(med(busy), 4),
+               "busy_x_clock_over_peak_clock": round(med(busy) * med(clk) / PEAK_CLOCK_GHZ, 4),
+               "roofline_frac_duration": round(med(frac), 4),
+               "counted_flop": med(mops) * FLOP_PER_MOP, "algorithmic_flop": flop_alg,
+               "source_hash": kernel_source_hash(stage)}
+        lines.append(f"| {stage} | {len(ids)} | {rec['duration_us']:.1f} | {rec['clock_ghz']:.2f} | "
+                     f"{rec['mfma_busy']:.3f} | {rec['busy_x_clock_over_peak_clock']:.3f} | "
+                     f"{rec['roofline_frac_duration']:.3f} | {rec['counted_flop'] / flop_alg:.3f} | {rec['source_hash']} |")
+        with open(os.path.join(ROOT, "profiles", f"mfma_{stage}_{wl}.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+    lines += ["", "Commands (from the repository root, TMPDIR=/tmp):", "", "```"] + args.commands + ["```", ""]
+    with open(os.path.join(ROOT, "profiles", f"mfma_{wl}.md"), "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def stats_summary(args):
     """Short text summary of a rocprofv3 --kernel-trace --stats run."""
     import csv
@@ -560,6 +637,8 @@ def main():
                     help="skip the 32-token, skewed 16384-token and 16-layer stack measurements")
     ap.add_argument("--copy-probe", action="store_true", help="run the counter-calibration copy and exit")
     ap.add_argument("--traffic-summary", action="store_true", help="summarise --pmc runs into profiles/")
+    ap.add_argument("--mfma-summary", metavar="DIR", dest="mfma_dir",
+                    help="summarise a --kernel-trace --pmc run over the MFMA counters into profiles/")
     ap.add_argument("--stats-summary", metavar="DIR", dest="stats_dir", help="summarise a --stats run")
     ap.add_argument("--profile-label", default="", help="extra word in the kernel summary's file name")
     ap.add_argument("--fetch-dir")
@@ -570,6 +649,9 @@ def main():
     ap.add_argument("--command", dest="commands", action="append", default=[],
                     help="command line recorded in a summary (repeatable)")
     args = ap.parse_args()
+    if args.mfma_dir:
+        mfma_summary(args)
+        return
     if args.traffic_summary:
         traffic_summary(args)
         return
