@@ -404,8 +404,22 @@ def cpu_baseline(d, workload, budget_s=20.0):
             break
     el = time.perf_counter() - t0
     return {"value": round(done / el, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"{runs} oracle call(s) of {n} tokens of {workload} (first {n} rows), "
                       f"{el:.1f} s, float64 NumPy"}
+
+
+def _cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 # ---------------------------------------------------------------------------
