@@ -316,6 +316,17 @@ def measure_backward(workload, steps, warmup, seed=0, routing="token"):
                                        g_aux=1.0, g_z=1.0, **outs)
         sec_pair = timed([fwd_train, bwd_saved])
         extra = {"train_step_saved_ms": round(sec_pair * 1e3, 5), "train_saved_tokens_per_s": round(T / sec_pair, 1)}
+    # the same backward with the expert weight gradients returned in bf16 (OLMOE_BWD_GRAD_BF16)
+    bf = torch.bfloat16
+    outs16 = dict(outs, dw_gate=torch.empty((E, F, D), dtype=bf, device=dev),
+                  dw_up=torch.empty((E, F, D), dtype=bf, device=dev), dw_down=torch.empty((E, D, F), dtype=bf, device=dev))
+    flags16 = binding.BWD_GRAD_BF16 | (binding.BWD_EXPERT_CHOICE if routing == "expert" else 0)
+
+    def bwd16(w):
+        binding.moe_backward_ex(d["x"], w["w_router"], w["w_gate"], w["w_up"], w["w_down"], dout, flags=flags16,
+                                g_aux=1.0, g_z=1.0, workspace=bws, **outs16)
+    sec16 = timed([bwd16])
+    extra.update({"grad_bf16_ms": round(sec16 * 1e3, 5), "grad_bf16_tokens_per_s": round(T / sec16, 1)})
     return {"routing": routing, "workload": workload, "tokens": T, "ms_per_step": round(sec * 1e3, 5), **extra,
             "tokens_per_s": round(T / sec, 1),
             "tflops": round(BWD_FLOP_PER_TOKEN * T / sec / 1e12, 2),
@@ -323,7 +334,8 @@ def measure_backward(workload, steps, warmup, seed=0, routing="token"):
             "train_step_ms": round(sec_train * 1e3, 5), "train_tokens_per_s": round(T / sec_train, 1),
             "note": "backward: gradients of x and all weights, the forward recompute inside timed, not counted "
                     "in tflops; train step: one forward call + one backward call; train step saved: the "
-                    "training pair (forward keeping its state + backward from it, no recompute)"}
+                    "training pair (forward keeping its state + backward from it, no recompute); grad bf16: "
+                    "the backward with the expert weight gradients written in bf16"}
 
 
 def measure_expert_choice(workload, steps, warmup, seed=0):

@@ -47,7 +47,7 @@ extern "C" {
 #define OLMOE_API
 #endif
 
-#define OLMOE_ABI_VERSION 9
+#define OLMOE_ABI_VERSION 10
 
 #define OLMOE_D 2048 /* hidden size */
 #define OLMOE_F 1024 /* expert width (SwiGLU intermediate size) */
@@ -353,6 +353,43 @@ OLMOE_API olmoe_status_t olmoe_moe_backward(const void* x, const float* W_router
                                   float g_aux, float g_z, float* dx, float* dW_router, float* dW_gate,
                                   float* dW_up, float* dW_down, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* One entry point for every backward variant, with one more choice: the
+ * expert weight gradients in the weights' own type.  The model was trained in
+ * bf16 ("OLMoE: Open Mixture-of-Experts Language Models", Additional
+ * Experiments, Figure 27; "OLMoE Guide", item 3 speaks of the backward in
+ * FP16/BF16), so a caller may want bf16 weight gradients: OLMOE_BWD_GRAD_BF16
+ * returns the fp32 gradients rounded to bf16, in half the bytes.
+ *
+ * flags (any other bit set is OLMOE_EINVAL):
+ *   OLMOE_BWD_SAVED          workspace is the `saved` buffer of the matching
+ *                            training forward (olmoe_moe_forward_train, or
+ *                            olmoe_moe_forward_expert_choice_train with the next
+ *                            flag) for the same x, weights and T; its state is
+ *                            consumed; else the forward is recomputed inside
+ *   OLMOE_BWD_EXPERT_CHOICE  the expert-choice layer (0 <= T <=
+ *                            OLMOE_EC_MAX_TOKENS; workspace of
+ *                            olmoe_moe_ec_backward_workspace_bytes(T)), else
+ *                            token choice (olmoe_moe_backward_workspace_bytes(T))
+ *   OLMOE_BWD_GRAD_BF16      dW_gate, dW_up and dW_down are bf16 (same shapes):
+ *                            each value is the fp32 gradient the call computes
+ *                            without this flag, rounded to nearest even (the
+ *                            same bits as rounding that call's outputs); dx and
+ *                            dW_router stay fp32
+ * With flags 0, OLMOE_BWD_SAVED, OLMOE_BWD_EXPERT_CHOICE and both, the call is
+ * olmoe_moe_backward, olmoe_moe_backward_saved,
+ * olmoe_moe_backward_expert_choice and
+ * olmoe_moe_backward_expert_choice_saved (bit for bit).  Arguments, internal
+ * streams and errors as those, with the output sizes of the chosen gradient
+ * type in the overlap checks. */
+#define OLMOE_BWD_SAVED ((uint32_t)1 << 0)
+#define OLMOE_BWD_EXPERT_CHOICE ((uint32_t)1 << 1)
+#define OLMOE_BWD_GRAD_BF16 ((uint32_t)1 << 2)
+OLMOE_API olmoe_status_t olmoe_moe_backward_ex(const void* x, const float* W_router, const void* W_gate,
+                                     const void* W_up, const void* W_down, int64_t T, const void* dout,
+                                     float g_aux, float g_z, float* dx, float* dW_router, void* dW_gate,
+                                     void* dW_up, void* dW_down, void* workspace,
+                                     size_t workspace_bytes, uint32_t flags, void* stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the layer

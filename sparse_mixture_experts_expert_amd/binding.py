@@ -84,6 +84,9 @@ def lib() -> ctypes.CDLL:
     L.olmoe_moe_backward_expert_choice_saved.restype = i32
     L.olmoe_moe_backward_expert_choice_saved.argtypes = [vp, vp, vp, vp, vp, i64, vp, ctypes.c_float, ctypes.c_float,
                                                          vp, vp, vp, vp, vp, vp, sz, vp]
+    L.olmoe_moe_backward_ex.restype = i32
+    L.olmoe_moe_backward_ex.argtypes = [vp, vp, vp, vp, vp, i64, vp, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp,
+                                        vp, vp, sz, ctypes.c_uint32, vp]
     L.olmoe_rmsnorm_bf16.restype = i32
     L.olmoe_rmsnorm_bf16.argtypes = [vp, ctypes.c_float, i64, vp, vp]
     L.olmoe_residual_add.restype = i32
@@ -430,6 +433,43 @@ def moe_backward_expert_choice(x, w_router, w_gate, w_up, w_down, dout, *, g_aux
         _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), int(T), _ptr(dout),
         ctypes.c_float(g_aux), ctypes.c_float(g_z), _ptr(dx), _ptr(dw_router), _ptr(dw_gate), _ptr(dw_up),
         _ptr(dw_down), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return {"dx": dx, "dw_router": dw_router, "dw_gate": dw_gate, "dw_up": dw_up, "dw_down": dw_down,
+            "workspace": workspace}
+
+
+BWD_SAVED = 1 << 0            # OLMOE_BWD_SAVED: workspace is the training forward's saved state
+BWD_EXPERT_CHOICE = 1 << 1    # OLMOE_BWD_EXPERT_CHOICE: the expert-choice layer
+BWD_GRAD_BF16 = 1 << 2        # OLMOE_BWD_GRAD_BF16: dW_gate / dW_up / dW_down in bf16
+
+
+def moe_backward_ex(x, w_router, w_gate, w_up, w_down, dout, *, flags: int = 0, g_aux: float = 1.0,
+                    g_z: float = 1.0, dx=None, dw_router=None, dw_gate=None, dw_up=None, dw_down=None,
+                    workspace=None, stream=None):
+    """olmoe_moe_backward_ex: any backward variant chosen by `flags` (BWD_SAVED, BWD_EXPERT_CHOICE,
+    BWD_GRAD_BF16).  The expert weight gradients are bf16 with BWD_GRAD_BF16, else fp32; dx and
+    dw_router are fp32.  With BWD_SAVED, `workspace` is the training forward's `saved` buffer;
+    otherwise it is allocated when missing."""
+    import torch
+    T = x.shape[0]
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, D))
+    _need(dout, "dout", torch.bfloat16, (T, D))
+    f32 = torch.float32
+    wg = torch.bfloat16 if flags & BWD_GRAD_BF16 else f32
+    dx = dx if dx is not None else torch.empty((T, D), dtype=f32, device=dev)
+    dw_router = dw_router if dw_router is not None else torch.empty((E, D), dtype=f32, device=dev)
+    dw_gate = dw_gate if dw_gate is not None else torch.empty((E, F, D), dtype=wg, device=dev)
+    dw_up = dw_up if dw_up is not None else torch.empty((E, F, D), dtype=wg, device=dev)
+    dw_down = dw_down if dw_down is not None else torch.empty((E, D, F), dtype=wg, device=dev)
+    if workspace is None:
+        if flags & BWD_SAVED:
+            raise ValueError("BWD_SAVED needs the saved buffer of the training forward as workspace")
+        nbytes = ec_backward_workspace_bytes(T) if flags & BWD_EXPERT_CHOICE else backward_workspace_bytes(T)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    _check(lib().olmoe_moe_backward_ex(
+        _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), int(T), _ptr(dout),
+        ctypes.c_float(g_aux), ctypes.c_float(g_z), _ptr(dx), _ptr(dw_router), _ptr(dw_gate), _ptr(dw_up),
+        _ptr(dw_down), _ptr(workspace), workspace.numel(), ctypes.c_uint32(flags), _stream(stream)))
     return {"dx": dx, "dw_router": dw_router, "dw_gate": dw_gate, "dw_up": dw_up, "dw_down": dw_down,
             "workspace": workspace}
 

@@ -529,8 +529,8 @@ olmoe_status_t forward_impl(const void* x, const float* W_router, const void* W_
 // argument checks shared by the backward entry points (T already range-checked)
 olmoe_status_t backward_checks(const void* x, const float* W_router, const void* W_gate, const void* W_up,
                                const void* W_down, int64_t T, const void* dout, float g_aux, float g_z, float* dx,
-                               float* dW_router, float* dW_gate, float* dW_up, float* dW_down, void* workspace,
-                               size_t workspace_bytes, size_t needed) {
+                               float* dW_router, void* dW_gate, void* dW_up, void* dW_down, void* workspace,
+                               size_t workspace_bytes, size_t needed, size_t wgrad_elem = 4) {
   if (!W_router || !W_gate || !W_up || !W_down) return fail(OLMOE_EINVAL, "a weight pointer is NULL");
   if (!dW_router || !dW_gate || !dW_up || !dW_down) return fail(OLMOE_EINVAL, "a weight-gradient pointer is NULL");
   if (T > 0 && (!x || !dout || !dx)) return fail(OLMOE_EINVAL, "x, dout or dx is NULL");
@@ -546,7 +546,8 @@ olmoe_status_t backward_checks(const void* x, const float* W_router, const void*
   const void* ins[] = {x, dout, W_router, W_gate, W_up, W_down};
   const size_t in_n[] = {act, act, wr_bytes, wexp, wexp, wexp};
   void* outs[] = {dx, dW_router, dW_gate, dW_up, dW_down};
-  const size_t out_n[] = {act * 2, wr_bytes, wexp * 2, wexp * 2, wexp * 2};
+  const size_t wg = wexp / 2 * wgrad_elem;
+  const size_t out_n[] = {act * 2, wr_bytes, wg, wg, wg};
   if (!workspace) return fail(OLMOE_EWORKSPACE, "workspace is NULL");
   if (misaligned(workspace, 256)) return fail(OLMOE_EINVAL, "workspace is not 256-byte aligned");
   if (workspace_bytes < needed)
@@ -627,8 +628,8 @@ olmoe_status_t bwd_forward_state(const void* x, const float* W_router, const voi
 // the gradients from the state bwd_forward_state left in B
 olmoe_status_t bwd_gradients(const void* x, const float* W_router, const void* W_gate, const void* W_up,
                              const void* W_down, int Ti, const void* dout, float g_aux, float g_z, float* dx,
-                             float* dW_router, float* dW_gate, float* dW_up, float* dW_down, char* ws,
-                             const BwdLayout& B, hipStream_t s) {
+                             float* dW_router, void* dW_gate, void* dW_up, void* dW_down, char* ws,
+                             const BwdLayout& B, hipStream_t s, bool grad_bf16 = false) {
   const Layout& L = B.f;
   int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
   const int32_t* perm = reinterpret_cast<const int32_t*>(ws + L.perm);
@@ -648,10 +649,10 @@ olmoe_status_t bwd_gradients(const void* x, const float* W_router, const void* W
   // dout and x rows are read through perm (expert order -> token) by the kernels that use them
   BwdWgradArgs wd{static_cast<const uint16_t*>(dout), OLMOE_D, reinterpret_cast<const uint16_t*>(ws + B.hw),
                   OLMOE_F, offsets, reinterpret_cast<const uint16_t*>(ws + B.zero), OLMOE_D, OLMOE_F, dW_down, dW_down,
-                  OLMOE_D, (long)OLMOE_D * OLMOE_F, perm, nullptr};
+                  OLMOE_D, (long)OLMOE_D * OLMOE_F, perm, nullptr, grad_bf16};
   BwdWgradArgs wgu{dgu, 2 * OLMOE_F, static_cast<const uint16_t*>(x), OLMOE_D, offsets,
                    reinterpret_cast<const uint16_t*>(ws + B.zero), 2 * OLMOE_F, OLMOE_D, dW_gate, dW_up, OLMOE_F,
-                   (long)OLMOE_F * OLMOE_D, nullptr, perm};
+                   (long)OLMOE_F * OLMOE_D, nullptr, perm, grad_bf16};
   SideStreams* ss = nullptr;
   he = side_streams(&ss);
   if (he != hipSuccess) return fail(OLMOE_EHIP, "side streams: %s", hipGetErrorString(he));
@@ -782,8 +783,8 @@ olmoe_status_t ec_bwd_forward_state(const void* x, const float* W_router, const 
 // the expert-choice gradients from the state ec_bwd_forward_state left in B
 olmoe_status_t ec_bwd_gradients(const void* x, const float* W_router, const void* W_gate, const void* W_up,
                                 const void* W_down, int Ti, const void* dout, float g_aux, float g_z, float* dx,
-                                float* dW_router, float* dW_gate, float* dW_up, float* dW_down, char* ws,
-                                const EcBwdLayout& B, hipStream_t s) {
+                                float* dW_router, void* dW_gate, void* dW_up, void* dW_down, char* ws,
+                                const EcBwdLayout& B, hipStream_t s, bool grad_bf16 = false) {
   const EcLayout& L = B.c;
   const int C = ec_capacity(Ti);
   const int Teff = 8 * C;
@@ -805,10 +806,10 @@ olmoe_status_t ec_bwd_gradients(const void* x, const float* W_router, const void
   // dout and x rows are read through perm (expert order -> token) by the kernels that use them
   BwdWgradArgs wd{static_cast<const uint16_t*>(dout), OLMOE_D, reinterpret_cast<const uint16_t*>(ws + B.hw),
                   OLMOE_F, offsets, reinterpret_cast<const uint16_t*>(ws + B.zero), OLMOE_D, OLMOE_F, dW_down, dW_down,
-                  OLMOE_D, (long)OLMOE_D * OLMOE_F, perm, nullptr};
+                  OLMOE_D, (long)OLMOE_D * OLMOE_F, perm, nullptr, grad_bf16};
   BwdWgradArgs wgu{dgu, 2 * OLMOE_F, static_cast<const uint16_t*>(x), OLMOE_D, offsets,
                    reinterpret_cast<const uint16_t*>(ws + B.zero), 2 * OLMOE_F, OLMOE_D, dW_gate, dW_up, OLMOE_F,
-                   (long)OLMOE_F * OLMOE_D, nullptr, perm};
+                   (long)OLMOE_F * OLMOE_D, nullptr, perm, grad_bf16};
   SideStreams* ss = nullptr;
   he = side_streams(&ss);
   if (he != hipSuccess) return fail(OLMOE_EHIP, "side streams: %s", hipGetErrorString(he));
@@ -852,20 +853,8 @@ olmoe_status_t olmoe_moe_backward(const void* x, const float* W_router, const vo
                                   const void* W_down, int64_t T, const void* dout, float g_aux, float g_z,
                                   float* dx, float* dW_router, float* dW_gate, float* dW_up, float* dW_down,
                                   void* workspace, size_t workspace_bytes, void* stream) {
-  // ---- host-side checks; nothing is enqueued unless all pass
-  if (T < 0 || T > OLMOE_MAX_TOKENS)
-    return fail(OLMOE_EINVAL, "T=%lld out of range [0, %lld]", (long long)T, (long long)OLMOE_MAX_TOKENS);
-  const BwdLayout B = make_bwd_layout(T);
-  olmoe_status_t st = backward_checks(x, W_router, W_gate, W_up, W_down, T, dout, g_aux, g_z, dx, dW_router, dW_gate,
-                                      dW_up, dW_down, workspace, workspace_bytes, B.total);
-  if (st != OLMOE_OK) return st;
-  // ---- launches: recompute the forward (keeping p, lse, G, U, Y), then the gradients
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  st = bwd_forward_state(x, W_router, W_gate, W_up, W_down, static_cast<int>(T), ws, B, nullptr, nullptr, nullptr, s);
-  if (st != OLMOE_OK) return st;
-  return bwd_gradients(x, W_router, W_gate, W_up, W_down, static_cast<int>(T), dout, g_aux, g_z, dx, dW_router,
-                       dW_gate, dW_up, dW_down, ws, B, s);
+  return olmoe_moe_backward_ex(x, W_router, W_gate, W_up, W_down, T, dout, g_aux, g_z, dx, dW_router, dW_gate, dW_up,
+                               dW_down, workspace, workspace_bytes, 0u, stream);
 }
 
 size_t olmoe_moe_saved_bytes(int64_t T) { return olmoe_moe_backward_workspace_bytes(T); }
@@ -932,14 +921,8 @@ olmoe_status_t olmoe_moe_backward_saved(const void* x, const float* W_router, co
                                         const void* W_down, int64_t T, const void* dout, float g_aux, float g_z,
                                         float* dx, float* dW_router, float* dW_gate, float* dW_up, float* dW_down,
                                         void* saved, size_t saved_bytes, void* stream) {
-  if (T < 0 || T > OLMOE_MAX_TOKENS)
-    return fail(OLMOE_EINVAL, "T=%lld out of range [0, %lld]", (long long)T, (long long)OLMOE_MAX_TOKENS);
-  const BwdLayout B = make_bwd_layout(T);
-  olmoe_status_t st = backward_checks(x, W_router, W_gate, W_up, W_down, T, dout, g_aux, g_z, dx, dW_router, dW_gate,
-                                      dW_up, dW_down, saved, saved_bytes, B.total);
-  if (st != OLMOE_OK) return st;
-  return bwd_gradients(x, W_router, W_gate, W_up, W_down, static_cast<int>(T), dout, g_aux, g_z, dx, dW_router,
-                       dW_gate, dW_up, dW_down, static_cast<char*>(saved), B, static_cast<hipStream_t>(stream));
+  return olmoe_moe_backward_ex(x, W_router, W_gate, W_up, W_down, T, dout, g_aux, g_z, dx, dW_router, dW_gate, dW_up,
+                               dW_down, saved, saved_bytes, OLMOE_BWD_SAVED, stream);
 }
 
 size_t olmoe_moe_ec_workspace_bytes(int64_t T) {
@@ -1076,20 +1059,8 @@ olmoe_status_t olmoe_moe_backward_expert_choice(const void* x, const float* W_ro
                                                 float g_aux, float g_z, float* dx, float* dW_router, float* dW_gate,
                                                 float* dW_up, float* dW_down, void* workspace, size_t workspace_bytes,
                                                 void* stream) {
-  if (T < 0 || T > OLMOE_EC_MAX_TOKENS)
-    return fail(OLMOE_EINVAL, "T=%lld out of range [0, %lld]", (long long)T, (long long)OLMOE_EC_MAX_TOKENS);
-  const EcBwdLayout B = make_ec_bwd_layout(T);
-  olmoe_status_t st = backward_checks(x, W_router, W_gate, W_up, W_down, T, dout, g_aux, g_z, dx, dW_router, dW_gate,
-                                      dW_up, dW_down, workspace, workspace_bytes, B.total);
-  if (st != OLMOE_OK) return st;
-  // ---- launches: recompute the expert-choice forward (keeping p, lse, G, U, Y), then the gradients
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  st = ec_bwd_forward_state(x, W_router, W_gate, W_up, W_down, static_cast<int>(T), ws, B, nullptr, nullptr, nullptr,
-                            nullptr, s);
-  if (st != OLMOE_OK) return st;
-  return ec_bwd_gradients(x, W_router, W_gate, W_up, W_down, static_cast<int>(T), dout, g_aux, g_z, dx, dW_router,
-                          dW_gate, dW_up, dW_down, ws, B, s);
+  return olmoe_moe_backward_ex(x, W_router, W_gate, W_up, W_down, T, dout, g_aux, g_z, dx, dW_router, dW_gate, dW_up,
+                               dW_down, workspace, workspace_bytes, OLMOE_BWD_EXPERT_CHOICE, stream);
 }
 
 size_t olmoe_moe_ec_saved_bytes(int64_t T) { return olmoe_moe_ec_backward_workspace_bytes(T); }
@@ -1159,14 +1130,47 @@ olmoe_status_t olmoe_moe_backward_expert_choice_saved(const void* x, const float
                                                       const void* dout, float g_aux, float g_z, float* dx,
                                                       float* dW_router, float* dW_gate, float* dW_up, float* dW_down,
                                                       void* saved, size_t saved_bytes, void* stream) {
-  if (T < 0 || T > OLMOE_EC_MAX_TOKENS)
-    return fail(OLMOE_EINVAL, "T=%lld out of range [0, %lld]", (long long)T, (long long)OLMOE_EC_MAX_TOKENS);
-  const EcBwdLayout B = make_ec_bwd_layout(T);
-  olmoe_status_t st = backward_checks(x, W_router, W_gate, W_up, W_down, T, dout, g_aux, g_z, dx, dW_router, dW_gate,
-                                      dW_up, dW_down, saved, saved_bytes, B.total);
+  return olmoe_moe_backward_ex(x, W_router, W_gate, W_up, W_down, T, dout, g_aux, g_z, dx, dW_router, dW_gate, dW_up,
+                               dW_down, saved, saved_bytes, OLMOE_BWD_EXPERT_CHOICE | OLMOE_BWD_SAVED, stream);
+}
+
+olmoe_status_t olmoe_moe_backward_ex(const void* x, const float* W_router, const void* W_gate, const void* W_up,
+                                     const void* W_down, int64_t T, const void* dout, float g_aux, float g_z,
+                                     float* dx, float* dW_router, void* dW_gate, void* dW_up, void* dW_down,
+                                     void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+  // ---- host-side checks; nothing is enqueued unless all pass
+  if (flags & ~(OLMOE_BWD_SAVED | OLMOE_BWD_EXPERT_CHOICE | OLMOE_BWD_GRAD_BF16))
+    return fail(OLMOE_EINVAL, "unknown backward flags 0x%x", flags);
+  const bool ec = flags & OLMOE_BWD_EXPERT_CHOICE;
+  const bool from_saved = flags & OLMOE_BWD_SAVED;
+  const bool grad_bf16 = flags & OLMOE_BWD_GRAD_BF16;
+  const int64_t t_max = ec ? OLMOE_EC_MAX_TOKENS : OLMOE_MAX_TOKENS;
+  if (T < 0 || T > t_max) return fail(OLMOE_EINVAL, "T=%lld out of range [0, %lld]", (long long)T, (long long)t_max);
+  const size_t wgrad_elem = grad_bf16 ? 2 : 4;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int Ti = static_cast<int>(T);
+  olmoe_status_t st = OLMOE_OK;
+  // ---- launches: recompute the forward (keeping p, lse, G, U, Y) unless the state was saved, then
+  // the gradients
+  if (ec) {
+    const EcBwdLayout B = make_ec_bwd_layout(T);
+    st = backward_checks(x, W_router, W_gate, W_up, W_down, T, dout, g_aux, g_z, dx, dW_router, dW_gate, dW_up,
+                         dW_down, workspace, workspace_bytes, B.total, wgrad_elem);
+    if (st == OLMOE_OK && !from_saved)
+      st = ec_bwd_forward_state(x, W_router, W_gate, W_up, W_down, Ti, ws, B, nullptr, nullptr, nullptr, nullptr, s);
+    if (st != OLMOE_OK) return st;
+    return ec_bwd_gradients(x, W_router, W_gate, W_up, W_down, Ti, dout, g_aux, g_z, dx, dW_router, dW_gate, dW_up,
+                            dW_down, ws, B, s, grad_bf16);
+  }
+  const BwdLayout B = make_bwd_layout(T);
+  st = backward_checks(x, W_router, W_gate, W_up, W_down, T, dout, g_aux, g_z, dx, dW_router, dW_gate, dW_up, dW_down,
+                       workspace, workspace_bytes, B.total, wgrad_elem);
+  if (st == OLMOE_OK && !from_saved)
+    st = bwd_forward_state(x, W_router, W_gate, W_up, W_down, Ti, ws, B, nullptr, nullptr, nullptr, s);
   if (st != OLMOE_OK) return st;
-  return ec_bwd_gradients(x, W_router, W_gate, W_up, W_down, static_cast<int>(T), dout, g_aux, g_z, dx, dW_router,
-                          dW_gate, dW_up, dW_down, static_cast<char*>(saved), B, static_cast<hipStream_t>(stream));
+  return bwd_gradients(x, W_router, W_gate, W_up, W_down, Ti, dout, g_aux, g_z, dx, dW_router, dW_gate, dW_up,
+                       dW_down, ws, B, s, grad_bf16);
 }
 
 olmoe_status_t olmoe_rmsnorm_bf16(const float* h, float eps, int64_t T, void* x_out, void* stream) {

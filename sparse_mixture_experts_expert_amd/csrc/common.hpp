@@ -47,6 +47,15 @@ __device__ __forceinline__ float f16_to_f32(uint16_t v) {
   return static_cast<float>(__builtin_bit_cast(_Float16, v));
 }
 
+// two fp32 values rounded to nearest even into one packed bf16 pair (gfx950 converts a pair in one
+// instruction; NaN stays NaN)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }

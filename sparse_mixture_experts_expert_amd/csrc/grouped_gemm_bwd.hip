@@ -304,7 +304,7 @@ struct WCfg {
   static_assert(STAGES >= 2 && IPS * (STAGES - 2) <= 63, "pipeline");
 };
 
-template <class C>
+template <class C, bool BF16_OUT>
 __global__ __launch_bounds__(C::NT) void wgrad_kernel(BwdWgradArgs a) {
   __shared__ __align__(16) bf16_t smem[C::STAGES][C::A_ELEMS + C::B_ELEMS];
 
@@ -427,18 +427,46 @@ __global__ __launch_bounds__(C::NT) void wgrad_kernel(BwdWgradArgs a) {
   // output row m (of m_total) goes to out0 below m_split, out1 above; the gradients are not read
   // again here, so the stores are non-temporal (staging the tile through LDS for wider stores
   // measured slower: the extra barrier and LDS pass cost more than the coalescing gains)
+  const int m_base = mt * C::BM + wm * (C::BM / C::WM);
+  const int n_base = nt * C::BN + wn * (C::BN / C::WN);
+  if constexpr (!BF16_OUT) {
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i)
+    for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
+      for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = mt * C::BM + wm * (C::BM / C::WM) + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-        const int n = nt * C::BN + wn * (C::BN / C::WN) + j * 32 + (lane & 31);
-        float* o = m < a.m_split ? a.out0 + (size_t)e * a.out_stride + (size_t)m * a.n_total
-                                 : a.out1 + (size_t)e * a.out_stride + (size_t)(m - a.m_split) * a.n_total;
-        __builtin_nontemporal_store(acc[i][j][v], &o[n]);
-      }
+        for (int v = 0; v < 16; ++v) {
+          const int m = m_base + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+          const int n = n_base + j * 32 + (lane & 31);
+          float* o = m < a.m_split ? static_cast<float*>(a.out0) + (size_t)e * a.out_stride + (size_t)m * a.n_total
+                                   : static_cast<float*>(a.out1) + (size_t)e * a.out_stride +
+                                         (size_t)(m - a.m_split) * a.n_total;
+          __builtin_nontemporal_store(acc[i][j][v], &o[n]);
+        }
+  } else {
+    // bf16: lanes 2c and 2c+1 hold columns 2c and 2c+1 of the same rows, so each pair trades one
+    // value (DPP swap of neighbours) and each lane stores one packed pair of one row: the even lane
+    // row (v even), the odd lane row (v odd); half the store instructions of 2-byte stores
+    const int odd = lane & 1;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float mine_lo = acc[i][j][2 * u], mine_hi = acc[i][j][2 * u + 1];
+          const float send = odd ? mine_lo : mine_hi;
+          const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, true));
+          const float lo = odd ? recv : mine_lo, hi = odd ? mine_hi : recv;
+          const int v = 2 * u + odd;
+          const int m = m_base + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+          const int n = n_base + j * 32 + (lane & 30);
+          uint16_t* o = m < a.m_split ? static_cast<uint16_t*>(a.out0) + (size_t)e * a.out_stride + (size_t)m * a.n_total
+                                      : static_cast<uint16_t*>(a.out1) + (size_t)e * a.out_stride +
+                                            (size_t)(m - a.m_split) * a.n_total;
+          __builtin_nontemporal_store(cvt_bf16x2(lo, hi), reinterpret_cast<uint32_t*>(o + n));
+        }
+  }
 }
 
 using DgDH = DCfg<128, 128, 2, 2, 3, EPI_DH>;
@@ -487,7 +515,10 @@ hipError_t launch_dgrad(const BwdDgradArgs& a, int T, bool dh, hipStream_t strea
 hipError_t launch_wgrad(const BwdWgradArgs& a, hipStream_t stream) {
   const int units = E * (a.m_total / WgCfg::BM) * (a.n_total / WgCfg::BN);
   const int grid = (units + 7) / 8 * 8;
-  hipLaunchKernelGGL(wgrad_kernel<WgCfg>, dim3(grid), dim3(WgCfg::NT), 0, stream, a);
+  if (a.out_bf16)
+    hipLaunchKernelGGL((wgrad_kernel<WgCfg, true>), dim3(grid), dim3(WgCfg::NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((wgrad_kernel<WgCfg, false>), dim3(grid), dim3(WgCfg::NT), 0, stream, a);
   return hipGetLastError();
 }
 

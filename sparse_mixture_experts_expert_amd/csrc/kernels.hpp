@@ -183,14 +183,15 @@ struct BwdWgradArgs {
   const int32_t* offsets;     // [65]
   const uint16_t* zero;       // at least 256 zero bytes (rows past an expert's count)
   int m_total, n_total;       // output rows / columns per expert
-  float* out0;                // rows m < m_split
-  float* out1;                // rows m >= m_split (at m - m_split)
+  void* out0;                 // rows m < m_split
+  void* out1;                 // rows m >= m_split (at m - m_split)
   int m_split;
   long out_stride;            // elements per expert in out0 / out1
   // row -> source row of a / b (expert order -> token), or null (row itself); at most one of the
   // two, and the table must stay readable 64 entries past its last row
   const int32_t* a_rows = nullptr;
   const int32_t* b_rows = nullptr;
+  bool out_bf16 = false;      // out0 / out1 hold bf16 (the fp32 sums rounded to nearest even), else fp32
 };
 hipError_t launch_wgrad(const BwdWgradArgs& a, hipStream_t stream);
 

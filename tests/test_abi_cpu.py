@@ -25,6 +25,12 @@ def L():
     return binding.lib()
 
 
+def _no_device():
+    """True when no GPU is visible (counting devices does not initialise one)."""
+    import torch
+    return torch.cuda.device_count() == 0
+
+
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert len(names) >= 10
@@ -108,9 +114,11 @@ def test_forward_routing_outputs_may_not_alias(L):
         st, msg = _fwd(L, T=T, **dict(ok, **change))
         assert st == binding.EINVAL, f"{label}: status {st} ({msg})"
         assert "overlaps" in msg, f"{label}: {msg}"
-    # the non-overlapping placement passes every check (and then finds no GPU here)
-    st, msg = _fwd(L, T=T, **ok)
-    assert st != binding.EINVAL, msg
+    # the non-overlapping placement passes every check (and then finds no GPU here; with a device
+    # the call would launch on the fake pointers, so it is made only without one)
+    if _no_device():
+        st, msg = _fwd(L, T=T, **ok)
+        assert st != binding.EINVAL, msg
 
 
 def test_noalloc_forward_limits(L):
@@ -188,6 +196,42 @@ def test_backward_checks_arguments_first(L):
     assert bwd(dwu=(1 << 34) + 4096) == binding.EINVAL         # two outputs overlap
     assert bwd(dwd=(8 << 36) + 256) == binding.EINVAL          # output in the workspace
     assert bwd(dwr=(1 << 32) + 64) == binding.EINVAL           # dW_router over W_gate
+
+
+def test_backward_ex_flags_and_gradient_sizes(L):
+    """olmoe_moe_backward_ex: unknown flag bits, the token range of each layer, the saved-state size
+    and the bf16 gradients' own sizes in the overlap checks (fake pointers; every call but the last
+    fails validation, and the last one only without a device)."""
+    vp = ctypes.c_void_p
+    T = 16
+    wsb = binding.backward_workspace_bytes(T)
+    g16 = 64 * 1024 * 2048 * 2   # bytes of one bf16 expert weight gradient
+
+    def ex(flags, t=T, dwg=1 << 34, dwu=2 << 34, dwd=3 << 34, wsb=wsb):
+        st = L.olmoe_moe_backward_ex(vp(1 << 20), vp(2 << 20), vp(1 << 32), vp(2 << 32), vp(3 << 32), t,
+                                     vp(4 << 20), ctypes.c_float(1.0), ctypes.c_float(0.5), vp(5 << 20), vp(6 << 20),
+                                     vp(dwg), vp(dwu), vp(dwd), vp(8 << 36), wsb, flags, None)
+        return st, L.olmoe_last_error().decode()
+
+    st, msg = ex(1 << 3)
+    assert st == binding.EINVAL and "flags" in msg
+    st, msg = ex(binding.BWD_GRAD_BF16 | (1 << 31))
+    assert st == binding.EINVAL and "flags" in msg
+    # expert choice has its own token limit; token choice takes more tokens (then the short
+    # workspace is what fails)
+    assert ex(binding.BWD_EXPERT_CHOICE, t=binding.EC_MAX_TOKENS + 1)[0] == binding.EINVAL
+    assert ex(0, t=binding.EC_MAX_TOKENS + 1)[0] == binding.EWORKSPACE
+    # each layer sizes its own workspace, saved or not
+    assert ex(binding.BWD_EXPERT_CHOICE | binding.BWD_SAVED, wsb=binding.ec_backward_workspace_bytes(T) - 256)[0] \
+        == binding.EWORKSPACE
+    assert ex(binding.BWD_SAVED, wsb=wsb - 256)[0] == binding.EWORKSPACE
+    # dW_up one bf16 gradient after dW_gate: overlaps as fp32, not as bf16
+    assert ex(0, dwu=(1 << 34) + g16)[0] == binding.EINVAL
+    assert ex(binding.BWD_GRAD_BF16, dwu=(1 << 34) + g16 - 16)[0] == binding.EINVAL
+    assert ex(binding.BWD_GRAD_BF16, dwd=(8 << 36) - g16 + 16)[0] == binding.EINVAL   # into the workspace
+    if _no_device():
+        st, msg = ex(binding.BWD_GRAD_BF16, dwu=(1 << 34) + g16)
+        assert st == binding.ENODEVICE, msg
 
 
 def test_expert_choice_checks_arguments_first(L):

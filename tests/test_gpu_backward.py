@@ -230,6 +230,83 @@ def test_expert_choice_training_pair_equals_stateless_calls(weights, T):
         assert torch.equal(b[k], b_ref[k]), k
 
 
+# ------------------------------------------------------------------ bf16 weight gradients
+
+
+BF16_HALF_ULP = 2.0 ** -8   # rounding to bf16 (nearest even) moves a value by at most this times |value|
+
+
+def _bf16_pair(w, T, variant, seed):
+    """The fp32 gradients of one backward variant and the same call with OLMOE_BWD_GRAD_BF16."""
+    x = inputs.device_x(T, seed=seed, workload="parity")
+    dout = inputs.device_x(T, seed=seed + 1, workload="parity")
+    args = (x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"])
+    kw = dict(g_aux=2.0, g_z=0.5)
+    ec = variant.startswith("expert")
+    flags = binding.BWD_GRAD_BF16 | (binding.BWD_EXPERT_CHOICE if ec else 0)
+    if variant.endswith("saved"):   # the saved state is consumed by each backward: one forward per call
+        train = binding.moe_forward_expert_choice_train if ec else binding.moe_forward_train
+        back = binding.moe_backward_expert_choice_saved if ec else binding.moe_backward_saved
+        ref = back(*args, dout, train(*args)["saved"], **kw)
+        got = binding.moe_backward_ex(*args, dout, flags=flags | binding.BWD_SAVED, workspace=train(*args)["saved"],
+                                      **kw)
+    else:
+        back = binding.moe_backward_expert_choice if ec else binding.moe_backward
+        ref = back(*args, dout, **kw)
+        got = binding.moe_backward_ex(*args, dout, flags=flags, **kw)
+    torch.cuda.synchronize()
+    return x, dout, ref, got
+
+
+@pytest.mark.parametrize("variant,T", [("token", 0), ("token", 1), ("token", 200), ("token", 769),
+                                       ("token", 4096), ("token-saved", 300), ("expert", 9), ("expert", 700),
+                                       ("expert-saved", 300)])
+def test_bf16_weight_gradients_round_the_fp32_ones(weights, variant, T):
+    """OLMOE_BWD_GRAD_BF16 returns the fp32 call's expert weight gradients rounded to nearest
+    even (torch's float -> bfloat16 conversion), bit for bit; dx and dW_router are unchanged."""
+    w, _ = weights
+    _log(f"bf16 weight gradients {variant} T={T}")
+    _, _, ref, got = _bf16_pair(w, T, variant, seed=90 + T)
+    for k in ("dx", "dw_router"):
+        assert got[k].dtype == torch.float32 and torch.equal(got[k], ref[k]), k
+    for k in ("dw_gate", "dw_up", "dw_down"):
+        assert got[k].dtype == torch.bfloat16, k
+        want = ref[k].to(torch.bfloat16)
+        bad = (got[k].view(torch.int16) != want.view(torch.int16)).sum().item()
+        assert bad == 0, f"{variant} T={T} {k}: {bad} values differ from the rounded fp32 gradient"
+
+
+@pytest.mark.parametrize("T", [200, 4096])
+def test_bf16_weight_gradients_match_oracle(weights, T):
+    """The bf16 expert weight gradients against the oracle's chain rule: the fp32 bound of the
+    gradient GEMMs plus one bf16 rounding of the result."""
+    w, hw = weights
+    _log(f"bf16 weight gradients vs oracle T={T}")
+    x, dout, _, got = _bf16_pair(w, T, "token", seed=110 + T)
+    xb = parity.bf16_tensor_to_bits(x)
+    fwd = binding.moe_forward(x, w["w_router"], w["w_gate"], w["w_up"], w["w_down"])
+    torch.cuda.synchronize()
+    ids = fwd["route_ids"].cpu().numpy()
+    ref_fwd = oracle.moe_layer_ref(xb, hw["w_router"], hw["w_gate"], hw["w_up"], hw["w_down"], 8)
+    ntie = parity.check_routing(ids, fwd["route_probs"].cpu().numpy(), ref_fwd, f"bf16 grads T={T}")
+    forced = ids if ntie or not np.array_equal(ids, ref_fwd["ids"]) else None
+    ref = oracle.moe_layer_backward_ref(xb, hw["w_router"], hw["w_gate"], hw["w_up"], hw["w_down"],
+                                        parity.bf16_tensor_to_bits(dout), 2.0, 0.5, 8, forced_ids=forced,
+                                        magnitudes=True)
+    for name, mag in (("dw_gate", "mag_gate"), ("dw_up", "mag_up"), ("dw_down", "mag_down")):
+        g = got[name].float().cpu().numpy().astype(np.float64)
+        r = ref[name]
+        nrm = np.linalg.norm(r)
+        rel = np.linalg.norm(g - r) / nrm
+        assert rel <= GRAD_REL_L2, f"{name}: rel L2 {rel:.3e}"
+        rms = nrm / np.sqrt(r.size)
+        bound = GRAD_TERM_BOUND * ref[mag] + BF16_HALF_ULP * np.abs(r) + 2.0 ** -20 * rms
+        worst = (np.abs(g - r) / bound).max()
+        assert worst <= 1.0, f"{name}: error {worst:.2f} x the bound"
+        assert not np.any(g[ref[mag] == 0]), f"{name}: nonzero gradient where no row contributes"
+        _log(f"T={T} {name} rel={rel:.2e} worst={worst:.2f}")
+
+
 def test_backward_captured_in_a_graph_replays_exactly(weights):
     """The backward, with its fork of the weight gradients onto the side streams and the join
     back, captured in a HIP graph: every replay gives the eager call's bits, with eager work and
