@@ -317,8 +317,10 @@ OLMOE_API olmoe_status_t olmoe_residual_add(float* h, const void* y, int64_t T, 
  * olmoe_moe_forward ("OLMoE Guide", items 1-3; "Mixture-of-experts LLMs from
  * scratch with OLMoE", section 2).  The routing choice and the routed shares
  * f_e are piecewise constant and carry no gradient.  The forward is recomputed
- * inside (no state is kept between calls): routing, G = x W_gate^T and
- * U = x W_up^T of every routed row, and the expert outputs.
+ * inside (no state is kept between calls): routing, and G = x W_gate^T and
+ * U = x W_up^T of every routed row.  The routing weights' gradient
+ * <dout[t], Y[t,j]> is taken as <dout[t] W_down[e_j], H[t,j]> from the
+ * gradient GEMM through W_down, so the expert outputs are not recomputed.
  *
  *   dout       bf16 [T,2048]          upstream gradient of out
  *   g_aux, g_z                        upstream gradients of the two losses (finite)

@@ -82,7 +82,7 @@ Layout make_layout(int64_t T) {
 // backward workspace: the forward's layout followed by the backward's own buffers
 struct BwdLayout {
   Layout f;
-  size_t p_all, lse, row_w, gu, dgu, hw, dxr, dlogits, dwr_part, zero, tp_bwd, tiles_bwd, total;
+  size_t p_all, lse, row_w, gu, dgu, hw, dxr, dlogits, dwr_part, zero, tp_bwd, tiles_bwd, rowdot, total;
 };
 BwdLayout make_bwd_layout(int64_t T) {
   BwdLayout B{};
@@ -106,6 +106,7 @@ BwdLayout make_bwd_layout(int64_t T) {
   B.zero = take(4096);
   B.tp_bwd = take(65 * 4);
   B.tiles_bwd = take((static_cast<size_t>(max_row_tiles(static_cast<int>(T), MIN_TILE_ROWS)) + 8) * 8);
+  B.rowdot = take(rows * BWD_MAX_DOT_PARTS * 4);
   B.total = off;
   return B;
 }
@@ -564,10 +565,12 @@ olmoe_status_t backward_checks(const void* x, const float* W_router, const void*
 }
 
 // the backward's forward part (token choice, default router): routing, the gate/up GEMM keeping
-// the fp32 pre-activations G | U, and the down GEMM, all into the backward layout B
+// the fp32 pre-activations G | U, and (with_y: for the layer's output) the down GEMM, all into the
+// backward layout B.  The gradients need no expert outputs: the routing weights' gradient comes
+// from the dH~ dgrad.
 olmoe_status_t bwd_forward_state(const void* x, const float* W_router, const void* W_gate, const void* W_up,
                                  const void* W_down, int Ti, char* ws, const BwdLayout& B, int32_t* expert_counts,
-                                 float* aux_loss, float* z_loss, hipStream_t s) {
+                                 float* aux_loss, float* z_loss, bool with_y, hipStream_t s) {
   const Layout& L = B.f;
   const GemmPlan plan = plan_gemm(Ti);
   int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
@@ -619,7 +622,7 @@ olmoe_status_t bwd_forward_state(const void* x, const float* W_router, const voi
                 reinterpret_cast<float*>(ws + B.gu),
                 reinterpret_cast<int32_t*>(ws + L.clip)};
     he = launch_gateup(ga, plan, s);
-    if (he == hipSuccess) he = launch_down(ga, plan, s);
+    if (he == hipSuccess && with_y) he = launch_down(ga, plan, s);
     if (he != hipSuccess) return fail(OLMOE_EHIP, "forward GEMM launch: %s", hipGetErrorString(he));
   }
   return OLMOE_OK;
@@ -638,13 +641,13 @@ olmoe_status_t bwd_gradients(const void* x, const float* W_router, const void* W
   BwdSmallArgs ba{Ti, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dout), W_router, ids,
                   reinterpret_cast<const float*>(ws + B.p_all), reinterpret_cast<const float*>(ws + B.lse),
                   offsets, perm, reinterpret_cast<const int32_t*>(ws + L.inv),
-                  reinterpret_cast<const uint16_t*>(ws + L.y), g_aux, g_z,
+                  reinterpret_cast<const float*>(ws + B.rowdot), g_aux, g_z,
                   reinterpret_cast<float*>(ws + B.dlogits), reinterpret_cast<const float*>(ws + B.dxr), dx,
                   reinterpret_cast<float*>(ws + B.dwr_part), dW_router, reinterpret_cast<uint16_t*>(ws + B.zero),
                   reinterpret_cast<int32_t*>(ws + B.tp_bwd), reinterpret_cast<int2*>(ws + B.tiles_bwd)};
+  ba.dot_parts = bwd_dot_parts(Ti);
   he = launch_bwd_prepare(ba, s);
-  if (he == hipSuccess) he = launch_bwd_router(ba, s);
-  if (he != hipSuccess) return fail(OLMOE_EHIP, "backward routing launch: %s", hipGetErrorString(he));
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "backward preparation launch: %s", hipGetErrorString(he));
   const uint16_t* dgu = reinterpret_cast<const uint16_t*>(ws + B.dgu);
   // dout and x rows are read through perm (expert order -> token) by the kernels that use them
   BwdWgradArgs wd{static_cast<const uint16_t*>(dout), OLMOE_D, reinterpret_cast<const uint16_t*>(ws + B.hw),
@@ -662,7 +665,8 @@ olmoe_status_t bwd_gradients(const void* x, const float* W_router, const void* W
                     reinterpret_cast<const int32_t*>(ws + B.tp_bwd) + OLMOE_E,
                     reinterpret_cast<const int2*>(ws + B.tiles_bwd),
                     reinterpret_cast<const float*>(ws + B.row_w), reinterpret_cast<const float*>(ws + B.gu),
-                    reinterpret_cast<uint16_t*>(ws + B.dgu), reinterpret_cast<uint16_t*>(ws + B.hw), nullptr};
+                    reinterpret_cast<uint16_t*>(ws + B.dgu), reinterpret_cast<uint16_t*>(ws + B.hw), nullptr,
+                    reinterpret_cast<float*>(ws + B.rowdot), K * Ti};
     BwdDgradArgs dxa{dgu, nullptr, static_cast<const uint16_t*>(W_gate), static_cast<const uint16_t*>(W_up),
                      OLMOE_D, (long)OLMOE_F * OLMOE_D, OLMOE_F,
                      reinterpret_cast<const int32_t*>(ws + B.tp_bwd) + OLMOE_E,
@@ -670,6 +674,7 @@ olmoe_status_t bwd_gradients(const void* x, const float* W_router, const void* W
                      reinterpret_cast<float*>(ws + B.dxr)};
     he = launch_dgrad(dh, Ti, true, s);
     if (he == hipSuccess) he = fork_wgrads(wd, wgu, s, *ss);   // they need dH's outputs only
+    if (he == hipSuccess) he = launch_bwd_router(ba, s);        // dlogits from dH's row sums
     if (he == hipSuccess) he = launch_dgrad(dxa, Ti, false, s);
     if (he != hipSuccess) return fail(OLMOE_EHIP, "gradient launch: %s", hipGetErrorString(he));
   } else {
@@ -686,7 +691,7 @@ olmoe_status_t bwd_gradients(const void* x, const float* W_router, const void* W
 // for its 64C rows
 struct EcBwdLayout {
   EcLayout c;
-  size_t p_all, gu, dgu, hw, dxr, dlogits, dwr_part, zero, tp_bwd, tiles_bwd, total;
+  size_t p_all, gu, dgu, hw, dxr, dlogits, dwr_part, zero, tp_bwd, tiles_bwd, rowdot, total;
 };
 EcBwdLayout make_ec_bwd_layout(int64_t T) {
   EcBwdLayout B{};
@@ -709,16 +714,17 @@ EcBwdLayout make_ec_bwd_layout(int64_t T) {
   B.zero = take(4096);
   B.tp_bwd = take(65 * 4);
   B.tiles_bwd = take((static_cast<size_t>(max_row_tiles(8 * C, MIN_TILE_ROWS)) + 8) * 8);
+  B.rowdot = take(rows * BWD_MAX_DOT_PARTS * 4);
   B.total = off;
   return B;
 }
 
-// the expert-choice backward's forward part: routing, the gate/up GEMM keeping G | U, the down
-// GEMM, into the layout B; the selection and loss outputs are optional
+// the expert-choice backward's forward part: routing, the gate/up GEMM keeping G | U, and (with_y)
+// the down GEMM, into the layout B; the selection and loss outputs are optional
 olmoe_status_t ec_bwd_forward_state(const void* x, const float* W_router, const void* W_gate, const void* W_up,
                                     const void* W_down, int Ti, char* ws, const EcBwdLayout& B,
                                     int32_t* choice_tokens, float* choice_probs, float* aux_loss, float* z_loss,
-                                    hipStream_t s) {
+                                    bool with_y, hipStream_t s) {
   const EcLayout& L = B.c;
   const int C = ec_capacity(Ti);
   const int Teff = 8 * C;
@@ -774,7 +780,7 @@ olmoe_status_t ec_bwd_forward_state(const void* x, const float* W_router, const 
                 reinterpret_cast<float*>(ws + B.gu),
                 reinterpret_cast<int32_t*>(ws + L.f.clip)};
     he = launch_gateup(ga, plan, s);
-    if (he == hipSuccess) he = launch_down(ga, plan, s);
+    if (he == hipSuccess && with_y) he = launch_down(ga, plan, s);
     if (he != hipSuccess) return fail(OLMOE_EHIP, "forward GEMM launch: %s", hipGetErrorString(he));
   }
   return OLMOE_OK;
@@ -794,14 +800,14 @@ olmoe_status_t ec_bwd_gradients(const void* x, const float* W_router, const void
   BwdSmallArgs ba{Ti, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dout), W_router, nullptr,
                   reinterpret_cast<const float*>(ws + B.p_all), reinterpret_cast<const float*>(ws + L.lse),
                   offsets, perm, nullptr,
-                  reinterpret_cast<const uint16_t*>(ws + L.f.y), g_aux, g_z,
+                  reinterpret_cast<const float*>(ws + B.rowdot), g_aux, g_z,
                   reinterpret_cast<float*>(ws + B.dlogits), reinterpret_cast<const float*>(ws + B.dxr), dx,
                   reinterpret_cast<float*>(ws + B.dwr_part), dW_router, reinterpret_cast<uint16_t*>(ws + B.zero),
                   reinterpret_cast<int32_t*>(ws + B.tp_bwd), reinterpret_cast<int2*>(ws + B.tiles_bwd),
                   reinterpret_cast<const int32_t*>(ws + L.inv_ec), OLMOE_E * C};
+  ba.dot_parts = bwd_dot_parts(Teff);
   he = launch_bwd_prepare(ba, s);
-  if (he == hipSuccess) he = launch_bwd_router(ba, s);
-  if (he != hipSuccess) return fail(OLMOE_EHIP, "backward routing launch: %s", hipGetErrorString(he));
+  if (he != hipSuccess) return fail(OLMOE_EHIP, "backward preparation launch: %s", hipGetErrorString(he));
   const uint16_t* dgu = reinterpret_cast<const uint16_t*>(ws + B.dgu);
   // dout and x rows are read through perm (expert order -> token) by the kernels that use them
   BwdWgradArgs wd{static_cast<const uint16_t*>(dout), OLMOE_D, reinterpret_cast<const uint16_t*>(ws + B.hw),
@@ -819,7 +825,8 @@ olmoe_status_t ec_bwd_gradients(const void* x, const float* W_router, const void
                     reinterpret_cast<const int32_t*>(ws + B.tp_bwd) + OLMOE_E,
                     reinterpret_cast<const int2*>(ws + B.tiles_bwd),
                     reinterpret_cast<const float*>(ws + L.row_w), reinterpret_cast<const float*>(ws + B.gu),
-                    reinterpret_cast<uint16_t*>(ws + B.dgu), reinterpret_cast<uint16_t*>(ws + B.hw), nullptr};
+                    reinterpret_cast<uint16_t*>(ws + B.dgu), reinterpret_cast<uint16_t*>(ws + B.hw), nullptr,
+                    reinterpret_cast<float*>(ws + B.rowdot), OLMOE_E * C};
     BwdDgradArgs dxa{dgu, nullptr, static_cast<const uint16_t*>(W_gate), static_cast<const uint16_t*>(W_up),
                      OLMOE_D, (long)OLMOE_F * OLMOE_D, OLMOE_F,
                      reinterpret_cast<const int32_t*>(ws + B.tp_bwd) + OLMOE_E,
@@ -827,6 +834,7 @@ olmoe_status_t ec_bwd_gradients(const void* x, const float* W_router, const void
                      reinterpret_cast<float*>(ws + B.dxr)};
     he = launch_dgrad(dh, Teff, true, s);
     if (he == hipSuccess) he = fork_wgrads(wd, wgu, s, *ss);   // they need dH's outputs only
+    if (he == hipSuccess) he = launch_bwd_router(ba, s);        // dlogits from dH's row sums
     if (he == hipSuccess) he = launch_dgrad(dxa, Teff, false, s);
     if (he != hipSuccess) return fail(OLMOE_EHIP, "gradient launch: %s", hipGetErrorString(he));
   } else {
@@ -902,7 +910,7 @@ olmoe_status_t olmoe_moe_forward_train(const void* x, const float* W_router, con
   char* ws = static_cast<char*>(saved);
   const Layout& L = B.f;
   st = bwd_forward_state(x, W_router, W_gate, W_up, W_down, static_cast<int>(T), ws, B, expert_counts, aux_loss,
-                         z_loss, s);
+                         z_loss, true, s);
   if (st != OLMOE_OK) return st;
   if (T == 0) return ok();
   hipError_t he = hipSuccess;
@@ -1109,7 +1117,7 @@ olmoe_status_t olmoe_moe_forward_expert_choice_train(const void* x, const float*
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(saved);
   st = ec_bwd_forward_state(x, W_router, W_gate, W_up, W_down, Ti, ws, B, choice_tokens, choice_probs, aux_loss,
-                            z_loss, s);
+                            z_loss, true, s);
   if (st != OLMOE_OK || Ti == 0) return st == OLMOE_OK ? ok() : st;
   const EcLayout& L = B.c;
   EcArgs ea{};
@@ -1158,7 +1166,8 @@ olmoe_status_t olmoe_moe_backward_ex(const void* x, const float* W_router, const
     st = backward_checks(x, W_router, W_gate, W_up, W_down, T, dout, g_aux, g_z, dx, dW_router, dW_gate, dW_up,
                          dW_down, workspace, workspace_bytes, B.total, wgrad_elem);
     if (st == OLMOE_OK && !from_saved)
-      st = ec_bwd_forward_state(x, W_router, W_gate, W_up, W_down, Ti, ws, B, nullptr, nullptr, nullptr, nullptr, s);
+      st = ec_bwd_forward_state(x, W_router, W_gate, W_up, W_down, Ti, ws, B, nullptr, nullptr, nullptr, nullptr,
+                                false, s);
     if (st != OLMOE_OK) return st;
     return ec_bwd_gradients(x, W_router, W_gate, W_up, W_down, Ti, dout, g_aux, g_z, dx, dW_router, dW_gate, dW_up,
                             dW_down, ws, B, s, grad_bf16);
@@ -1167,7 +1176,7 @@ olmoe_status_t olmoe_moe_backward_ex(const void* x, const float* W_router, const
   st = backward_checks(x, W_router, W_gate, W_up, W_down, T, dout, g_aux, g_z, dx, dW_router, dW_gate, dW_up, dW_down,
                        workspace, workspace_bytes, B.total, wgrad_elem);
   if (st == OLMOE_OK && !from_saved)
-    st = bwd_forward_state(x, W_router, W_gate, W_up, W_down, Ti, ws, B, nullptr, nullptr, nullptr, s);
+    st = bwd_forward_state(x, W_router, W_gate, W_up, W_down, Ti, ws, B, nullptr, nullptr, nullptr, false, s);
   if (st != OLMOE_OK) return st;
   return bwd_gradients(x, W_router, W_gate, W_up, W_down, Ti, dout, g_aux, g_z, dx, dW_router, dW_gate, dW_up,
                        dW_down, ws, B, s, grad_bf16);

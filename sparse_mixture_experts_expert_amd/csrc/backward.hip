@@ -4,7 +4,7 @@
 // With out[t] = sum_j w[t,j] Y[t,j] and w[t,j] = p[t, e_j] (the 64-way softmax
 // probabilities, not renormalised: "Mixture-of-experts LLMs from scratch with
 // OLMoE", section 2), the loss L = <dout, out> + g_aux * aux + g_z * z has
-//   dL/dw[t,j]   = <dout[t], Y[t,j]>
+//   dL/dw[t,j]   = <dout[t], Y[t,j]> = <dout[t] W_down[e_j], H[t,j]>
 //   dL/dp[t,e]   = dL/dw for the chosen e, plus g_aux * 0.01 * 64 * f_e / T from the
 //                  load-balancing term (f_e, the routed share, is piecewise constant)
 //   dL/dl[t,e]   = p (dL/dp - <p, dL/dp>)  +  g_z * 0.001 * 2 lse_t / T * p
@@ -43,45 +43,30 @@ __global__ __launch_bounds__(256) void bwd_prepare_kernel(BwdSmallArgs a, int bm
 }
 
 // one wavefront per token: dL/dw for its 8 rows (expert choice: for the rows of the experts that
-// took it, in ascending expert order), then dL/dlogits with lane = expert
+// took it, in ascending expert order), then dL/dlogits with lane = expert.  dL/dw of a row is
+// <dout[t], Y row> = <dout[t] W_down, H row>, which the dH~ dgrad epilogue leaves as dot_parts
+// partial sums per row: the expert outputs themselves are not needed.
 template <bool EC>
 __global__ __launch_bounds__(256) void bwd_router_kernel(BwdSmallArgs a) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
   const int lane = threadIdx.x & 63;
-  constexpr int NC = D / (64 * 8);
-  float g[NC][8];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(a.dout + (size_t)t * D + (c * 64 + lane) * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      g[c][2 * i] = __uint_as_float(v[i] << 16);
-      g[c][2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
-    }
-  }
-  // <dout[t], Y row> for up to 8 rows (row < 0: none), the same on every lane.  Every row's
-  // loads are issued before the first product, so the rows' memory latencies overlap.
+  const size_t stride = a.rows ? a.rows : (size_t)K * a.T;
+  // the sums for up to 8 rows (row < 0: none), the same on every lane: lane 8j+q adds parts
+  // q, q+8 of row j, then the 8 lanes of a row add up in a fixed order
   auto dot_rows = [&](const int* rows, float* out) __attribute__((always_inline)) {
-    u32x4 v[K][NC];
+    const int jl = lane >> 3, q = lane & 7;
+    int row = -1;
 #pragma unroll
-    for (int j = 0; j < K; ++j)
+    for (int j = 0; j < K; ++j) row = j == jl ? rows[j] : row;
+    float s = 0.f;
+    if (row >= 0)
+      for (int p = q; p < a.dot_parts; p += 8) s += a.rowdot[(size_t)p * stride + row];
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    s += __shfl_xor(s, 4, 64);
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        v[j][c] = rows[j] >= 0 ? *reinterpret_cast<const u32x4*>(a.y + (size_t)rows[j] * D + (c * 64 + lane) * 8)
-                               : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      float s = 0.f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          s = fmaf(g[c][2 * i], f16_to_f32(static_cast<uint16_t>(v[j][c][i] & 0xFFFFu)), s);
-          s = fmaf(g[c][2 * i + 1], f16_to_f32(static_cast<uint16_t>(v[j][c][i] >> 16)), s);
-        }
-      out[j] = wave_sum(s);
-    }
+    for (int j = 0; j < K; ++j) out[j] = __shfl(s, j * 8, 64);
   };
   const float p = a.p_all[(size_t)t * E + lane];
   const float cnt = static_cast<float>(a.offsets[lane + 1] - a.offsets[lane]);

@@ -141,6 +141,30 @@ struct DCfg {
   static_assert(STAGES >= 2 && IPS * (STAGES - 2) <= 63 && ND % BN == 0, "pipeline");
 };
 
+// lanes l and l^M of one half-wave (M < 32) trade x through the LDS crossbar's swizzle
+template <int M>
+__device__ __forceinline__ float swz_xor(float x) {
+  static_assert(M > 0 && M < 32, "xor within 32 lanes");
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (M << 10) | 0x1F));
+}
+
+// x[v] summed over the 32 lanes of each half-wave, in 16 exchanges: every step halves the values a
+// lane holds (it keeps the half its lane bit selects and adds the partner's copy of it), so after
+// four steps lane l holds value v = (l >> 1) & 15 summed over the 16 lanes that share bit 0 of l,
+// and the last exchange adds the other 16 (lanes l and l ^ 1 end with the same sum)
+__device__ __forceinline__ float half_wave_transpose_sum(const float (&x)[16], int lane) {
+  float y[8], z[4], w[2];
+  const bool b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) y[k] = (b4 ? x[k + 8] : x[k]) + swz_xor<16>(b4 ? x[k] : x[k + 8]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) z[k] = (b3 ? y[k + 4] : y[k]) + swz_xor<8>(b3 ? y[k] : y[k + 4]);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) w[k] = (b2 ? z[k + 2] : z[k]) + swz_xor<4>(b2 ? z[k] : z[k + 2]);
+  float t = (b1 ? w[1] : w[0]) + swz_xor<2>(b1 ? w[0] : w[1]);
+  return t + swz_xor<1>(t);
+}
+
 template <class C>
 __global__ __launch_bounds__(C::NT) void dgrad_kernel(BwdDgradArgs a) {
   __shared__ __align__(16) bf16_t smem[C::STAGES][C::A_ELEMS + C::B_ELEMS];
@@ -249,8 +273,12 @@ __global__ __launch_bounds__(C::NT) void dgrad_kernel(BwdDgradArgs a) {
   else if (C::FM > 3 && nf == 3) kloop(std::integral_constant<int, (C::FM > 3 ? 3 : 0)>{});
   else kloop(std::integral_constant<int, 0>{});
 
+  // dH~ epilogue: the row sums of dH~ * H over this wave's columns (dH~ = dout W_down, so summed
+  // over all columns they are <dout, Y>, the routing weight's gradient, without the expert outputs)
+  const int part = nt * C::WN + wn;
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i)
+  for (int i = 0; i < C::FM; ++i) {
+    float rsum = 0.f;   // after the j loop: row (lane/2)%16 of the fragment row block, whole wave's columns
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
       const int c = nt * C::BN + wn * (C::BN / C::WN) + j * 32 + (lane & 31);
@@ -267,18 +295,22 @@ __global__ __launch_bounds__(C::NT) void dgrad_kernel(BwdDgradArgs a) {
           u[v] = a.gu[row * (2 * F) + F + c];
           w[v] = a.row_w[row];
         }
+        float prod[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = rb + (v >> 2) * 8 + (v & 3);
-          if (r >= valid) continue;
-          const size_t row = (size_t)(row0 + r);
           const float sg = sigmoidf(g[v]);
           const float sl = g[v] * sg;
+          const float h = sl * u[v];
+          prod[v] = acc[i][j][v] * h;
+          if (r >= valid) continue;
+          const size_t row = (size_t)(row0 + r);
           const float dh = w[v] * acc[i][j][v];
           a.dgu[row * (2 * F) + c] = f32_to_bf16(dh * u[v] * (sg * (1.0f + g[v] * (1.0f - sg))));
           a.dgu[row * (2 * F) + F + c] = f32_to_bf16(dh * sl);
-          a.hw[row * F + c] = f32_to_bf16(w[v] * sl * u[v]);
+          a.hw[row * F + c] = f32_to_bf16(w[v] * h);
         }
+        rsum += half_wave_transpose_sum(prod, lane);
       } else {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -287,6 +319,12 @@ __global__ __launch_bounds__(C::NT) void dgrad_kernel(BwdDgradArgs a) {
         }
       }
     }
+    if constexpr (C::EPI == EPI_DH) {
+      const int v = (lane >> 1) & 15;
+      const int r = (i * C::WM + wm) * 32 + (lane >> 5) * 4 + (v >> 2) * 8 + (v & 3);
+      if ((lane & 1) == 0 && r < valid) a.rowdot[(size_t)part * a.rowdot_stride + row0 + r] = rsum;
+    }
+  }
 }
 
 // ----------------------------------------------------------------------------- wgrad
@@ -493,6 +531,16 @@ using WgCfg = WCfg<256, 256, 4, 2, 2>;
 
 int bwd_tile_rows(int T) {
   return T > DGRAD_LARGE_TOKENS ? DgDHL::BM : T > DGRAD_SMALL_TOKENS ? DgDH::BM : DgDHS::BM;
+}
+
+template <class C>
+constexpr int dot_parts_of() { return C::ND / C::BN * C::WN; }
+static_assert(dot_parts_of<DgDH>() <= BWD_MAX_DOT_PARTS && dot_parts_of<DgDHS>() <= BWD_MAX_DOT_PARTS &&
+              dot_parts_of<DgDHL>() <= BWD_MAX_DOT_PARTS, "row-sum parts");
+
+int bwd_dot_parts(int T) {
+  return T > DGRAD_LARGE_TOKENS ? dot_parts_of<DgDHL>() : T > DGRAD_SMALL_TOKENS ? dot_parts_of<DgDH>()
+                                                                                : dot_parts_of<DgDHS>();
 }
 
 template <class C>

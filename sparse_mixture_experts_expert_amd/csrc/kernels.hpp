@@ -170,8 +170,14 @@ struct BwdDgradArgs {
   uint16_t* dgu;
   uint16_t* hw;
   float* out_f32;             // fp32 [rows, 2048]
+  // dH~ epilogue: per row, partial sums of <dH~, H> = <dout, Y> over the columns of one wave
+  // ([bwd_dot_parts(T), rowdot_stride], row index in expert order)
+  float* rowdot = nullptr;
+  int rowdot_stride = 0;
 };
 int bwd_tile_rows(int T);   // row tile height of the dgrad kernels for T tokens (rows 8T)
+int bwd_dot_parts(int T);   // partial sums per row of the dH~ epilogue's <dout, Y>
+constexpr int BWD_MAX_DOT_PARTS = 16;
 hipError_t launch_dgrad(const BwdDgradArgs& a, int T, bool dh, hipStream_t stream);
 
 // wgrad: per expert, out[m][n] = sum over the expert's rows r of a[r][m] * b[r][n]
@@ -206,7 +212,7 @@ struct BwdSmallArgs {
   const int32_t* offsets;     // [65]
   const int32_t* perm;        // [8T]
   const int32_t* inv;         // [T,8]
-  const uint16_t* y;          // fp16 [8T,2048] expert outputs
+  const float* rowdot;        // [dot_parts, rows] partial sums of <dout[t], Y row> (dH~ dgrad epilogue)
   float g_aux, g_z;
   float* dlogits;             // fp32 [T,64]
   const float* dxr;           // fp32 [8T,2048] per-row input gradients
@@ -218,6 +224,7 @@ struct BwdSmallArgs {
   int2* tiles_bwd;
   const int32_t* inv_ec = nullptr;   // expert choice: [T,64] row of (t, e) or -1 (replaces ids / inv)
   int rows = 0;                      // rows in expert order (0: 8T)
+  int dot_parts = 0;                 // partial sums per row in rowdot (1 .. BWD_MAX_DOT_PARTS)
 };
 int bwd_router_splits(int T);
 hipError_t launch_bwd_prepare(const BwdSmallArgs& a, hipStream_t stream);   // zero row, dgrad tile list
