@@ -141,30 +141,6 @@ struct DCfg {
   static_assert(STAGES >= 2 && IPS * (STAGES - 2) <= 63 && ND % BN == 0, "pipeline");
 };
 
-// lanes l and l^M of one half-wave (M < 32) trade x through the LDS crossbar's swizzle
-template <int M>
-__device__ __forceinline__ float swz_xor(float x) {
-  static_assert(M > 0 && M < 32, "xor within 32 lanes");
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (M << 10) | 0x1F));
-}
-
-// x[v] summed over the 32 lanes of each half-wave, in 16 exchanges: every step halves the values a
-// lane holds (it keeps the half its lane bit selects and adds the partner's copy of it), so after
-// four steps lane l holds value v = (l >> 1) & 15 summed over the 16 lanes that share bit 0 of l,
-// and the last exchange adds the other 16 (lanes l and l ^ 1 end with the same sum)
-__device__ __forceinline__ float half_wave_transpose_sum(const float (&x)[16], int lane) {
-  float y[8], z[4], w[2];
-  const bool b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) y[k] = (b4 ? x[k + 8] : x[k]) + swz_xor<16>(b4 ? x[k] : x[k + 8]);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) z[k] = (b3 ? y[k + 4] : y[k]) + swz_xor<8>(b3 ? y[k] : y[k + 4]);
-#pragma unroll
-  for (int k = 0; k < 2; ++k) w[k] = (b2 ? z[k + 2] : z[k]) + swz_xor<4>(b2 ? z[k] : z[k + 2]);
-  float t = (b1 ? w[1] : w[0]) + swz_xor<2>(b1 ? w[0] : w[1]);
-  return t + swz_xor<1>(t);
-}
-
 template <class C>
 __global__ __launch_bounds__(C::NT) void dgrad_kernel(BwdDgradArgs a) {
   __shared__ __align__(16) bf16_t smem[C::STAGES][C::A_ELEMS + C::B_ELEMS];
@@ -273,56 +249,83 @@ __global__ __launch_bounds__(C::NT) void dgrad_kernel(BwdDgradArgs a) {
   else if (C::FM > 3 && nf == 3) kloop(std::integral_constant<int, (C::FM > 3 ? 3 : 0)>{});
   else kloop(std::integral_constant<int, 0>{});
 
-  // dH~ epilogue: the row sums of dH~ * H over this wave's columns (dH~ = dout W_down, so summed
-  // over all columns they are <dout, Y>, the routing weight's gradient, without the expert outputs)
-  const int part = nt * C::WN + wn;
+  // The accumulators go through LDS one slice of fragment rows (WM*32 rows x BN columns, fp32) at
+  // a time, so that each thread then takes 8 consecutive columns of a row: 16-byte loads and stores
+  // instead of 4-byte ones spread over 16 rows per lane.
+  //   dH~ epilogue: dH = w dH~; H = SiLU(G) U, so dG = dH U SiLU'(G), dU = dH SiLU(G); and the row
+  //   sums of dH~ * H, whose total over all columns is <dout, Y> (dH~ = dout W_down), the routing
+  //   weight's gradient without the expert outputs.
+  //   fp32 epilogue: the rows as they are.
+  constexpr int SR = C::WM * 32;           // rows per slice
+  constexpr int CG = C::BN / 8;            // 8-column groups per row
+  constexpr int RPP = C::NT / CG;          // rows per pass
+  constexpr int PASSES = SR / RPP;
+  static_assert(SR * C::BN * 4 <= C::STAGES * (C::A_ELEMS + C::B_ELEMS) * 2, "a slice fits the LDS ring");
+  static_assert(C::NT % CG == 0 && SR % RPP == 0 && (CG & (CG - 1)) == 0 && CG <= 64, "slice mapping");
+  float* S = reinterpret_cast<float*>(&smem[0][0]);
+  const int cg = tid % CG, rsub = tid / CG;
+  const int c0 = nt * C::BN + cg * 8;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
-    float rsum = 0.f;   // after the j loop: row (lane/2)%16 of the fragment row block, whole wave's columns
+    __syncthreads();   // the ring (or the previous slice) is no longer read
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int c = nt * C::BN + wn * (C::BN / C::WN) + j * 32 + (lane & 31);
-      const int rb = (i * C::WM + wm) * 32 + (lane >> 5) * 4;   // + (v/4)*8 + v%4
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        S[(wm * 32 + (lane >> 5) * 4 + (v >> 2) * 8 + (v & 3)) * C::BN + wn * (C::BN / C::WN) + j * 32 +
+          (lane & 31)] = acc[i][j][v];
+    __syncthreads();
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int rl = ps * RPP + rsub;
+      const int r = i * SR + rl;
+      const bool ok = r < valid;
+      const size_t row = (size_t)row0 + (ok ? r : 0);   // padding rows read row0 and store nothing
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(&S[rl * C::BN + cg * 8]);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(&S[rl * C::BN + cg * 8 + 4]);
       if constexpr (C::EPI == EPI_DH) {
-        // dH = w dH~; H = SiLU(G) U, so dG = dH U SiLU'(G), dU = dH SiLU(G).  The fragment's
-        // G, U and w are loaded together before any store (the stores could alias them).
-        float g[16], u[16], w[16];
+        const f32x4* gp = reinterpret_cast<const f32x4*>(a.gu + row * (2 * F) + c0);
+        const f32x4* up = reinterpret_cast<const f32x4*>(a.gu + row * (2 * F) + F + c0);
+        const f32x4 g0 = gp[0], g1 = gp[1], u0 = up[0], u1 = up[1];
+        const float w = a.row_w[row];
+        const float g[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+        const float u[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+        const float d[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+        float dg[8], du[8], hw[8];
+        float sum = 0.f;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = rb + (v >> 2) * 8 + (v & 3);
-          const size_t row = (size_t)(row0 + (r < valid ? r : 0));
-          g[v] = a.gu[row * (2 * F) + c];
-          u[v] = a.gu[row * (2 * F) + F + c];
-          w[v] = a.row_w[row];
+        for (int k = 0; k < 8; ++k) {
+          const float sg = sigmoidf(g[k]);
+          const float sl = g[k] * sg;
+          const float h = sl * u[k];
+          const float dh = w * d[k];
+          dg[k] = dh * u[k] * (sg * (1.0f + g[k] * (1.0f - sg)));
+          du[k] = dh * sl;
+          hw[k] = w * h;
+          sum = fmaf(d[k], h, sum);
         }
-        float prod[16];
+        if (ok) {
+          const u32x4 pg = {cvt_bf16x2(dg[0], dg[1]), cvt_bf16x2(dg[2], dg[3]), cvt_bf16x2(dg[4], dg[5]),
+                            cvt_bf16x2(dg[6], dg[7])};
+          const u32x4 pu = {cvt_bf16x2(du[0], du[1]), cvt_bf16x2(du[2], du[3]), cvt_bf16x2(du[4], du[5]),
+                            cvt_bf16x2(du[6], du[7])};
+          const u32x4 ph = {cvt_bf16x2(hw[0], hw[1]), cvt_bf16x2(hw[2], hw[3]), cvt_bf16x2(hw[4], hw[5]),
+                            cvt_bf16x2(hw[6], hw[7])};
+          *reinterpret_cast<u32x4*>(a.dgu + row * (2 * F) + c0) = pg;
+          *reinterpret_cast<u32x4*>(a.dgu + row * (2 * F) + F + c0) = pu;
+          *reinterpret_cast<u32x4*>(a.hw + row * F + c0) = ph;
+        }
+        // the row's CG lanes are consecutive: add their sums in a fixed order
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = rb + (v >> 2) * 8 + (v & 3);
-          const float sg = sigmoidf(g[v]);
-          const float sl = g[v] * sg;
-          const float h = sl * u[v];
-          prod[v] = acc[i][j][v] * h;
-          if (r >= valid) continue;
-          const size_t row = (size_t)(row0 + r);
-          const float dh = w[v] * acc[i][j][v];
-          a.dgu[row * (2 * F) + c] = f32_to_bf16(dh * u[v] * (sg * (1.0f + g[v] * (1.0f - sg))));
-          a.dgu[row * (2 * F) + F + c] = f32_to_bf16(dh * sl);
-          a.hw[row * F + c] = f32_to_bf16(w[v] * h);
-        }
-        rsum += half_wave_transpose_sum(prod, lane);
+        for (int o = 1; o < CG; o <<= 1) sum += __shfl_xor(sum, o, 64);
+        if (cg == 0 && ok) a.rowdot[(size_t)nt * a.rowdot_stride + row] = sum;
       } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = rb + (v >> 2) * 8 + (v & 3);
-          if (r < valid) a.out_f32[(size_t)(row0 + r) * D + c] = acc[i][j][v];
+        if (ok) {
+          f32x4* o = reinterpret_cast<f32x4*>(a.out_f32 + row * D + c0);
+          o[0] = d0;
+          o[1] = d1;
         }
       }
-    }
-    if constexpr (C::EPI == EPI_DH) {
-      const int v = (lane >> 1) & 15;
-      const int r = (i * C::WM + wm) * 32 + (lane >> 5) * 4 + (v >> 2) * 8 + (v & 3);
-      if ((lane & 1) == 0 && r < valid) a.rowdot[(size_t)part * a.rowdot_stride + row0 + r] = rsum;
     }
   }
 }
@@ -534,7 +537,7 @@ int bwd_tile_rows(int T) {
 }
 
 template <class C>
-constexpr int dot_parts_of() { return C::ND / C::BN * C::WN; }
+constexpr int dot_parts_of() { return C::ND / C::BN; }
 static_assert(dot_parts_of<DgDH>() <= BWD_MAX_DOT_PARTS && dot_parts_of<DgDHS>() <= BWD_MAX_DOT_PARTS &&
               dot_parts_of<DgDHL>() <= BWD_MAX_DOT_PARTS, "row-sum parts");
 

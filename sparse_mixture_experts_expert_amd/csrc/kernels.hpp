@@ -170,7 +170,7 @@ struct BwdDgradArgs {
   uint16_t* dgu;
   uint16_t* hw;
   float* out_f32;             // fp32 [rows, 2048]
-  // dH~ epilogue: per row, partial sums of <dH~, H> = <dout, Y> over the columns of one wave
+  // dH~ epilogue: per row, partial sums of <dH~, H> = <dout, Y> over the columns of one workgroup
   // ([bwd_dot_parts(T), rowdot_stride], row index in expert order)
   float* rowdot = nullptr;
   int rowdot_stride = 0;
