@@ -370,7 +370,7 @@ __global__ __launch_bounds__(C::NT) void wgrad_kernel(BwdWgradArgs a) {
   // both operands K-outer: load j of A fills k-rows (wv*IPA + j)*RPA + lane/CPA, slot lane%CPA (B
   // alike), so a wave's loads of one stage cover KW consecutive k-rows of either operand
   constexpr int KW = C::IPA * C::RPA;
-  static_assert(KW == C::IPB * C::RPB && C::RPA == 2 && C::RPB == 2, "a wave's k-rows of a stage");
+  static_assert(KW == C::IPB * C::RPB, "a wave's k-rows of a stage");
   int ka[C::IPA], oa[C::IPA], kb[C::IPB], ob[C::IPB];
 #pragma unroll
   for (int j = 0; j < C::IPA; ++j) {
@@ -394,19 +394,27 @@ __global__ __launch_bounds__(C::NT) void wgrad_kernel(BwdWgradArgs a) {
 #pragma unroll
     for (int i = 0; i < KW; ++i) ids[i] = gtab[base + i];
   };
+  // the id of the k-row that load j of a lane reads (RP rows per load, lane / CP the row)
+  auto pick = [&](const int (&ids)[KW], int j, auto rp_tag, int cp) __attribute__((always_inline)) {
+    constexpr int RP = decltype(rp_tag)::value;
+    int v = ids[j * RP];
+#pragma unroll
+    for (int q = 1; q < RP; ++q) v = lane / cp == q ? ids[j * RP + q] : v;
+    return v;
+  };
   auto issue = [&](int kt, int sl, int j0, int j1, const int (&ids)[KW]) {
 #pragma unroll
     for (int j = 0; j < C::IPS; ++j) {
       if (j < j0 || j >= j1) continue;
       if (j < C::IPA) {
         const int k = kt * BK + ka[j];   // rows past the expert's count read zeros
-        const int srow = a.a_rows ? ((lane >> 5) ? ids[2 * j + 1] : ids[2 * j]) : r0 + k;
+        const int srow = a.a_rows ? pick(ids, j, std::integral_constant<int, C::RPA>{}, C::CPA) : r0 + k;
         const bf16_t* src = k < rows ? a.a + (size_t)srow * a.lda + oa[j] : a.zero + (oa[j] - mt * C::BM);
         __builtin_amdgcn_global_load_lds(GPTR(src), LPTR(&smem[sl][(wv * C::IPA + j) * C::RPA * C::BM]), 16, 0, 0);
       } else {
         const int jb = j - C::IPA;
         const int k = kt * BK + kb[jb];
-        const int srow = a.b_rows ? ((lane >> 5) ? ids[2 * jb + 1] : ids[2 * jb]) : r0 + k;
+        const int srow = a.b_rows ? pick(ids, jb, std::integral_constant<int, C::RPB>{}, C::CPB) : r0 + k;
         const bf16_t* src = k < rows ? a.b + (size_t)srow * a.ldb + ob[jb] : a.zero + (ob[jb] - nt * C::BN);
         __builtin_amdgcn_global_load_lds(GPTR(src),
                                          LPTR(&smem[sl][C::A_ELEMS + (wv * C::IPB + jb) * C::RPB * C::BN]), 16, 0, 0);
