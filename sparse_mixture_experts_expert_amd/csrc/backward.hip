@@ -104,54 +104,72 @@ __global__ __launch_bounds__(256) void bwd_router_kernel(BwdSmallArgs a) {
 }
 
 // dW_router partial sums, one per gridDim.y token range (whole batches of WR_SPLIT_TOKENS tokens,
-// summed in token order): thread (column, 16 experts).  The 16 experts are the same for the whole
-// wavefront, so their dlogits go through scalar loads (one per wave) rather than a vector load
-// that every lane repeats.
+// summed in token order): thread (2 columns, 16 experts).  A batch's dlogits go to LDS with one
+// coalesced load per workgroup; the 16 experts are the same for the whole wavefront, so their
+// values are broadcast reads.
+constexpr int WR_COLS = 128;   // columns per workgroup (2 per thread)
 __global__ __launch_bounds__(256) void bwd_wrouter_partial_kernel(BwdSmallArgs a) {
-  const int col = blockIdx.x * 64 + (threadIdx.x & 63);
-  const int e0 = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) * 16);
+  __shared__ float sdl[WR_SPLIT_TOKENS][E];
+  const int tid = threadIdx.x;
+  const int col = blockIdx.x * WR_COLS + 2 * (tid & 63);
+  const int e0 = __builtin_amdgcn_readfirstlane((tid >> 6) * 16);
   const int batches = (a.T + WR_SPLIT_TOKENS - 1) / WR_SPLIT_TOKENS;
   const int per = (batches + gridDim.y - 1) / gridDim.y * WR_SPLIT_TOKENS;   // tokens per range
   const int r0 = blockIdx.y * per;
   const int r1 = min(a.T, r0 + per);
-  float acc[16];
+  float acc0[16], acc1[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.f;
   for (int t0 = r0; t0 < r1; t0 += WR_SPLIT_TOKENS) {
-    const int t1 = min(r1, t0 + WR_SPLIT_TOKENS);
-    if (t1 - t0 == WR_SPLIT_TOKENS) {   // full batch: every load issued before the FMAs
-      float xv[WR_SPLIT_TOKENS];
+    const int nt = min(r1, t0 + WR_SPLIT_TOKENS) - t0;
+    __syncthreads();   // the previous batch's dlogits are no longer read
+    static_assert(WR_SPLIT_TOKENS * E == 256 * 8, "two float4 per thread");
 #pragma unroll
-      for (int q = 0; q < WR_SPLIT_TOKENS; ++q) xv[q] = bf16_to_f32(a.x[(size_t)(t0 + q) * D + col]);
-#pragma unroll 4
-      for (int q = 0; q < WR_SPLIT_TOKENS; ++q) {
-        const float4* dl = reinterpret_cast<const float4*>(a.dlogits + (size_t)(t0 + q) * E + e0);
+    for (int h = 0; h < 2; ++h) {
+      const int i = (h * 256 + tid) * 4;   // float index in the batch: token i / 64, expert i % 64
+      const int tk = i / E;
+      *reinterpret_cast<f32x4*>(&sdl[tk][i % E]) =
+          tk < nt ? *reinterpret_cast<const f32x4*>(a.dlogits + (size_t)(t0 + tk) * E + i % E) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    uint32_t xv[WR_SPLIT_TOKENS];
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const float4 d4 = dl[i4];
-          acc[4 * i4] = fmaf(d4.x, xv[q], acc[4 * i4]);
-          acc[4 * i4 + 1] = fmaf(d4.y, xv[q], acc[4 * i4 + 1]);
-          acc[4 * i4 + 2] = fmaf(d4.z, xv[q], acc[4 * i4 + 2]);
-          acc[4 * i4 + 3] = fmaf(d4.w, xv[q], acc[4 * i4 + 3]);
+    for (int q = 0; q < WR_SPLIT_TOKENS; ++q)
+      xv[q] = q < nt ? *reinterpret_cast<const uint32_t*>(a.x + (size_t)(t0 + q) * D + col) : 0u;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < WR_SPLIT_TOKENS; ++q) {
+      if (q >= nt) break;   // tokens past the range are not added (sums in token order)
+      const float x0 = __uint_as_float(xv[q] << 16), x1 = __uint_as_float(xv[q] & 0xFFFF0000u);
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sdl[q][e0 + 4 * i4]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc0[4 * i4 + c] = fmaf(d4[c], x0, acc0[4 * i4 + c]);
+          acc1[4 * i4 + c] = fmaf(d4[c], x1, acc1[4 * i4 + c]);
         }
-      }
-    } else {
-      for (int t = t0; t < t1; ++t) {
-        const float xv = bf16_to_f32(a.x[(size_t)t * D + col]);
-        const float* dl = a.dlogits + (size_t)t * E + e0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = fmaf(dl[i], xv, acc[i]);
       }
     }
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) a.dwr_part[((size_t)blockIdx.y * E + e0 + i) * D + col] = acc[i];
+  for (int i = 0; i < 16; ++i) {
+    float* o = a.dwr_part + ((size_t)blockIdx.y * E + e0 + i) * D + col;
+    *reinterpret_cast<float2*>(o) = make_float2(acc0[i], acc1[i]);
+  }
 }
 
+// dW_router: the partial sums added in range order (loads of eight ranges issued together)
 __global__ __launch_bounds__(256) void bwd_wrouter_reduce_kernel(BwdSmallArgs a, int nsplit) {
   const int i = blockIdx.x * 256 + threadIdx.x;   // over 64 x 2048
   float s = 0.f;
-  for (int sp = 0; sp < nsplit; ++sp) s += a.dwr_part[(size_t)sp * E * D + i];
+  for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = sp0 + k < nsplit ? a.dwr_part[(size_t)(sp0 + k) * E * D + i] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (sp0 + k < nsplit) s += v[k];
+  }
   a.dw_router[i] = s;
 }
 
@@ -240,7 +258,7 @@ hipError_t launch_bwd_router(const BwdSmallArgs& a, hipStream_t stream) {
 
 hipError_t launch_bwd_finish(const BwdSmallArgs& a, hipStream_t stream) {
   const int ns = bwd_router_splits(a.T);
-  if (ns > 0) hipLaunchKernelGGL(bwd_wrouter_partial_kernel, dim3(D / 64, ns), dim3(256), 0, stream, a);
+  if (ns > 0) hipLaunchKernelGGL(bwd_wrouter_partial_kernel, dim3(D / WR_COLS, ns), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_wrouter_reduce_kernel, dim3(E * D / 256), dim3(256), 0, stream, a, ns);
