@@ -472,3 +472,53 @@ def test_concurrent_calls_on_two_streams(weights):
         got = host_of(b)
         for k in ("out", "route_ids", "route_probs", "expert_counts", "aux_loss", "z_loss"):
             np.testing.assert_array_equal(got[k], ref[k], err_msg=f"call {i}: {k}")
+
+
+def test_forward_captured_in_a_graph_replays_exactly(weights):
+    """Three layer calls (small, streaming and large tile plans) captured in one HIP graph: every
+    replay gives the eager calls' bits, with the outputs poisoned and eager work of other sizes on
+    the same workspaces between the replays.  Nothing the forward enqueues is a memset: the clip
+    count and the other per-call zeroing are done by its kernels."""
+    w, _ = weights
+    ws = (w["w_router"], w["w_gate"], w["w_up"], w["w_down"])
+    sizes = (256, 1024, 4096)
+    xs = [inputs.device_x(T, seed=60 + i, workload="parity") for i, T in enumerate(sizes)]
+    names = ("out", "route_ids", "route_probs", "expert_counts", "aux_loss", "z_loss")
+
+    def buffers(T):
+        return dict(out=torch.empty((T, 2048), dtype=torch.bfloat16, device="cuda"),
+                    route_ids=torch.empty((T, 8), dtype=torch.int32, device="cuda"),
+                    route_probs=torch.empty((T, 8), dtype=torch.float32, device="cuda"),
+                    expert_counts=torch.empty(64, dtype=torch.int32, device="cuda"),
+                    aux_loss=torch.empty(1, dtype=torch.float32, device="cuda"),
+                    z_loss=torch.empty(1, dtype=torch.float32, device="cuda"),
+                    workspace=binding.make_workspace(T))
+    bufs = [buffers(x.shape[0]) for x in xs]
+    for x, b in zip(xs, bufs):   # eager calls first (also outside any capture)
+        binding.moe_forward(x, *ws, **b)
+    torch.cuda.synchronize()
+    refs = [{k: b[k].clone() for k in names} for b in bufs]
+    clip0 = [binding.clip_count(b["workspace"]) for b in bufs]
+    assert clip0 == [0, 0, 0]
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for x, b in zip(xs, bufs):
+            binding.moe_forward(x, *ws, stream=s, **b)
+    for rep in range(3):
+        for b in bufs:
+            b["out"].fill_(float("nan"))
+            b["route_probs"].fill_(float("nan"))
+            b["route_ids"].fill_(-7)
+            b["expert_counts"].fill_(-7)
+        # eager work of another size on the same workspaces between the replays
+        other = inputs.device_x(100 + rep, seed=70 + rep, workload="parity")
+        for b in bufs:
+            binding.moe_forward(other, *ws, workspace=b["workspace"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (b, ref) in enumerate(zip(bufs, refs)):
+            for k in names:
+                assert torch.equal(b[k], ref[k]), (rep, sizes[i], k)
+            assert binding.clip_count(b["workspace"]) == 0, (rep, sizes[i])
