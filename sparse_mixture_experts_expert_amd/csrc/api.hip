@@ -638,7 +638,7 @@ olmoe_status_t bwd_gradients(const void* x, const float* W_router, const void* W
   const int32_t* perm = reinterpret_cast<const int32_t*>(ws + L.perm);
   const int32_t* offsets = reinterpret_cast<const int32_t*>(ws + L.offsets);
   hipError_t he = hipSuccess;
-  BwdSmallArgs ba{Ti, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dout), W_router, ids,
+  BwdSmallArgs ba{Ti, static_cast<const uint16_t*>(x), W_router, ids,
                   reinterpret_cast<const float*>(ws + B.p_all), reinterpret_cast<const float*>(ws + B.lse),
                   offsets, perm, reinterpret_cast<const int32_t*>(ws + L.inv),
                   reinterpret_cast<const float*>(ws + B.rowdot), g_aux, g_z,
@@ -797,7 +797,7 @@ olmoe_status_t ec_bwd_gradients(const void* x, const float* W_router, const void
   const int32_t* perm = reinterpret_cast<const int32_t*>(ws + L.f.perm);
   const int32_t* offsets = reinterpret_cast<const int32_t*>(ws + L.f.offsets);
   hipError_t he = hipSuccess;
-  BwdSmallArgs ba{Ti, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dout), W_router, nullptr,
+  BwdSmallArgs ba{Ti, static_cast<const uint16_t*>(x), W_router, nullptr,
                   reinterpret_cast<const float*>(ws + B.p_all), reinterpret_cast<const float*>(ws + L.lse),
                   offsets, perm, nullptr,
                   reinterpret_cast<const float*>(ws + B.rowdot), g_aux, g_z,

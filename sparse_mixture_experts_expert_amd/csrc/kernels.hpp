@@ -204,7 +204,6 @@ hipError_t launch_wgrad(const BwdWgradArgs& a, hipStream_t stream);
 struct BwdSmallArgs {
   int T;
   const uint16_t* x;          // bf16 [T,2048]
-  const uint16_t* dout;       // bf16 [T,2048]
   const float* w_router;      // fp32 [64,2048]
   const int32_t* ids;         // [T,8]
   const float* p_all;         // [T,64]
