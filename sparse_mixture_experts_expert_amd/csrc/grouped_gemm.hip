@@ -306,26 +306,77 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(
 
   // C layout of a 32x32 fragment: lane holds column lane%32, rows (v/4)*8 + (lane/32)*4 + v%4
   int nclip = 0;
+  if constexpr (!C::SAVE_GU && C::WM * 32 * C::BN * 4 <= C::STAGES * C::ROWS * BK * 2) {
+    // the fp32 results go through the drained LDS ring one slice of fragment rows (WM*32 rows x BN
+    // columns) at a time, so that each thread then stores 8 consecutive fp16 values of a row with one
+    // 16-byte store instead of 2-byte stores spread over 16 rows (1% off the layer at 4096 and 16384
+    // tokens, the same bits)
+    constexpr int SR = C::WM * 32;           // rows per slice
+    constexpr int CG = C::BN / 8;            // 8-column groups per row
+    constexpr int RPP = C::NT / CG;          // rows per pass
+    constexpr int PASSES = SR / RPP;
+    static_assert(C::NT % CG == 0 && SR % RPP == 0, "slice mapping");
+    float* S = reinterpret_cast<float*>(&smem[0][0]);
+    const int cg = tid % CG, rsub = tid / CG;
+    const int c0 = nt * C::BN + cg * 8;
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i)
+    for (int i = 0; i < C::FM; ++i) {
+      __syncthreads();   // the ring (or the previous slice) is no longer read
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
+      for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = (i * C::WM + wm) * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-        const int c = nt * C::BN + wn * (C::BN / C::WN) + j * 32 + (lane & 31);
-        if (r < valid) {
+        for (int v = 0; v < 16; ++v) {
           float o;
           if constexpr (C::GATEUP) o = silu(acc[0][i][j][v]) * acc[1][i][j][v];
           else o = acc[0][i][j][v] * (1.0f / W_DOWN_SCALE);
-          nclip += !(fabsf(o) <= F16_MAX);   // out of range or NaN: stored clipped, counted
-          Cout[(size_t)(row0 + r) * C::ND + c] = f32_to_f16_sat(o);
-          if constexpr (C::SAVE_GU) {   // [rows, 2F]: G in columns 0..F-1, U in F..2F-1
-            gu[(size_t)(row0 + r) * (2 * F) + c] = acc[0][i][j][v];
-            gu[(size_t)(row0 + r) * (2 * F) + F + c] = acc[1][i][j][v];
+          S[(wm * 32 + (lane >> 5) * 4 + (v >> 2) * 8 + (v & 3)) * C::BN + wn * (C::BN / C::WN) + j * 32 +
+            (lane & 31)] = o;
+        }
+      __syncthreads();
+#pragma unroll
+      for (int ps = 0; ps < PASSES; ++ps) {
+        const int rl = ps * RPP + rsub;
+        const int r = i * SR + rl;
+        if (r < valid) {
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(&S[rl * C::BN + cg * 8]);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(&S[rl * C::BN + cg * 8 + 4]);
+          const float d[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+          u32x4 pk;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            nclip += !(fabsf(d[2 * q]) <= F16_MAX);   // out of range or NaN: stored clipped, counted
+            nclip += !(fabsf(d[2 * q + 1]) <= F16_MAX);
+            pk[q] = static_cast<uint32_t>(f32_to_f16_sat(d[2 * q])) |
+                    (static_cast<uint32_t>(f32_to_f16_sat(d[2 * q + 1])) << 16);
           }
+          *reinterpret_cast<u32x4*>(&Cout[(size_t)(row0 + r) * C::ND + c0]) = pk;
         }
       }
+    }
+  } else {
+    // the fragments stored as they are (the tile configs whose slice does not fit the ring, and
+    // the gate/up configs that also keep G and U)
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = (i * C::WM + wm) * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+          const int c = nt * C::BN + wn * (C::BN / C::WN) + j * 32 + (lane & 31);
+          if (r < valid) {
+            float o;
+            if constexpr (C::GATEUP) o = silu(acc[0][i][j][v]) * acc[1][i][j][v];
+            else o = acc[0][i][j][v] * (1.0f / W_DOWN_SCALE);
+            nclip += !(fabsf(o) <= F16_MAX);   // out of range or NaN: stored clipped, counted
+            Cout[(size_t)(row0 + r) * C::ND + c] = f32_to_f16_sat(o);
+            if constexpr (C::SAVE_GU) {   // [rows, 2F]: G in columns 0..F-1, U in F..2F-1
+              gu[(size_t)(row0 + r) * (2 * F) + c] = acc[0][i][j][v];
+              gu[(size_t)(row0 + r) * (2 * F) + F + c] = acc[1][i][j][v];
+            }
+          }
+        }
+  }
   nclip = wave_sum_int(nclip);
   if (nclip && lane == 0 && clip) atomicAdd(clip, nclip);   // an integer count: order does not matter
 }
