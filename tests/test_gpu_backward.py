@@ -259,8 +259,8 @@ def _bf16_pair(w, T, variant, seed):
 
 
 @pytest.mark.parametrize("variant,T", [("token", 0), ("token", 1), ("token", 200), ("token", 769),
-                                       ("token", 4096), ("token-saved", 300), ("expert", 9), ("expert", 700),
-                                       ("expert-saved", 300)])
+                                       ("token", 4096), ("token-saved", 300), ("expert", 0), ("expert", 9),
+                                       ("expert", 700), ("expert-saved", 300)])
 def test_bf16_weight_gradients_round_the_fp32_ones(weights, variant, T):
     """OLMOE_BWD_GRAD_BF16 returns the fp32 call's expert weight gradients rounded to nearest
     even (torch's float -> bfloat16 conversion), bit for bit; dx and dW_router are unchanged."""
@@ -307,26 +307,27 @@ def test_bf16_weight_gradients_match_oracle(weights, T):
         _log(f"T={T} {name} rel={rel:.2e} worst={worst:.2f}")
 
 
-def test_backward_captured_in_a_graph_replays_exactly(weights):
+@pytest.mark.parametrize("flags", [0, binding.BWD_GRAD_BF16])
+def test_backward_captured_in_a_graph_replays_exactly(weights, flags):
     """The backward, with its fork of the weight gradients onto the side streams and the join
-    back, captured in a HIP graph: every replay gives the eager call's bits, with eager work and
-    synchronisations between the replays."""
+    back, captured in a HIP graph (fp32 and bf16 weight gradients): every replay gives the eager
+    call's bits, with eager work and synchronisations between the replays."""
     w, _ = weights
     T = 300
     x = inputs.device_x(T, seed=51, workload="parity")
     dout = inputs.device_x(T, seed=52, workload="parity")
     wts = (w["w_router"], w["w_gate"], w["w_up"], w["w_down"])
     names = ("dx", "dw_router", "dw_gate", "dw_up", "dw_down")
-    first = binding.moe_backward(x, *wts, dout)
+    first = binding.moe_backward_ex(x, *wts, dout, flags=flags)
     torch.cuda.synchronize()
     ref = {k: first[k].clone() for k in names}
     bufs = {k: torch.empty_like(ref[k]) for k in names}
     ws = torch.empty(max(binding.backward_workspace_bytes(T), 256), dtype=torch.uint8, device="cuda")
-    binding.moe_backward(x, *wts, dout, workspace=ws, **bufs)   # outside the capture first
+    binding.moe_backward_ex(x, *wts, dout, flags=flags, workspace=ws, **bufs)   # outside the capture first
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        binding.moe_backward(x, *wts, dout, workspace=ws, **bufs)
+        binding.moe_backward_ex(x, *wts, dout, flags=flags, workspace=ws, **bufs)
     for rep in range(3):
         for v in bufs.values():
             v.fill_(float("nan"))

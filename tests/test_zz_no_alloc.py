@@ -42,3 +42,42 @@ def test_forward_noalloc_matches_forward_on_two_calls():
     with pytest.raises(binding.OlmoeError) as ei:
         binding.moe_forward_noalloc(x, *ws)
     assert ei.value.status == binding.EINVAL
+
+
+@pytest.mark.gpu
+def test_forward_noalloc_replays_in_a_graph():
+    """The allocation-free forward captured in a HIP graph (the use it exists for): every replay
+    equals the plain forward bit for bit, with eager allocation-free calls of other sizes in
+    between that overwrite the shared scratch."""
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    binding.lib()
+    w = inputs.device_weights(seed=0, workload="parity")
+    ws = (w["w_router"], w["w_gate"], w["w_up"], w["w_down"])
+    dev = "cuda"
+    T = 256
+    x = inputs.device_x(T, seed=77, workload="parity")
+    ref = binding.moe_forward(x, *ws)
+    torch.cuda.synchronize()
+    outs = dict(out=torch.empty((T, 2048), dtype=torch.bfloat16, device=dev),
+                route_ids=torch.empty((T, 8), dtype=torch.int32, device=dev),
+                route_probs=torch.empty((T, 8), dtype=torch.float32, device=dev),
+                expert_counts=torch.empty(64, dtype=torch.int32, device=dev),
+                aux_loss=torch.empty(1, dtype=torch.float32, device=dev),
+                z_loss=torch.empty(1, dtype=torch.float32, device=dev))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        binding.moe_forward_noalloc(x, *ws, stream=s, **outs)   # first call on the device outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        binding.moe_forward_noalloc(x, *ws, stream=s, **outs)
+    for rep, other_T in enumerate((600, 31, 1024)):
+        _log(f"replay {rep} after an eager call of {other_T} tokens")
+        for t in outs.values():
+            t.fill_(-3)
+        binding.moe_forward_noalloc(inputs.device_x(other_T, seed=80 + rep, workload="parity"), *ws)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(outs[k], ref[k]), (rep, k)
